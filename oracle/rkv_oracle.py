@@ -1,0 +1,216 @@
+"""Plain float64 CPU oracle for the R-KV decode-time compression step.
+
+TEST INFRASTRUCTURE ONLY. The tests, the smoke check in ``__graft_entry__`` and
+the ``cpu_baseline`` leg of ``bench.py`` are the only code that may import
+this module. The library (``decode_kv_cache_03_amd``) never calls it, and the
+two share no code: this file is written from the pages, not from the kernels.
+
+Pages cited (by title; sections in quotes):
+  [P1] "R-KV: decoding-time KV cache compression for reasoning models"
+       (hysenlabs project page)
+  [P2] sourcepulse project summary of R-KV (its "How It Works" section)
+  [P3] "R-KV: Redundancy-aware KV Cache Compression for Reasoning Models"
+       (atlas.scime.ai AI-extracted paper summary)
+
+What the method computes, per (layer, KV head) over the N buffered candidates:
+  * importance I from attention weights [P2 "How It Works"; P3 "Approach"],
+    pooled over the query heads of a GQA group by max, mean pooling being the
+    worse ablation [P3 "Measured effects reported in the paper", last row];
+  * redundancy R from the cosine similarity of key vectors, to find and prune
+    near-duplicates [P2 "How It Works"; P3 "Approach"; P1 "How this differs
+    from attention-sink and heavy-hitter eviction"];
+  * the joint score Z = lam*I - (1-lam)*R [P3 "Approach"];
+  * a recent window exempt from eviction [P1 "What the redundancy scoring
+    actually does at decode time"], and the top tokens by Z kept within the
+    budget [P2 "How It Works"];
+  * physical eviction: the kept rows are compacted and freed cache blocks go
+    back to the allocator [P1 "What the redundancy scoring actually does at
+    decode time"; "How this differs ..."].
+
+Readings taken where the pages leave a step open (each is also listed with its
+reasoning in the design notes of the repository):
+  R1  R_i = max over EARLIER candidates j < i of cos(k_i, k_j); R_0 = 0. P1
+      describes the score as similarity to what is already retained and the
+      eviction as removing the duplicate, i.e. the later copy.
+  R2  A zero-norm key has cosine 0 with every key.
+  R3  Importance uses the last w decode queries of each of the G query heads
+      of the group; query r of the window (r = 0..w-1) sees keys j <= N-w+r.
+  R4  Logits are q.k / sqrt(d); softmax over the visible keys; mean over the w
+      queries of a head, then max over the G heads.
+  R5  No rescaling of I or R: Z is taken literally.
+  R6  The window (last w candidates) is always kept; the other B-w slots go to
+      the candidates with the largest Z, ties to the smaller index; kept
+      indices are returned ascending; -0.0 and +0.0 are equal.
+  R7  N <= B keeps everything; B <= w is invalid.
+  R8  Paged mode: each (sequence, head) compacts its kept rows into logical
+      slots 0..B_s-1 of its own sequence; pages p >= B_s/page_size of the
+      sequence are freed in (sequence, page) ascending order and their page
+      table entries become -1.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def key_norms(K) -> np.ndarray:
+    """Euclidean norm of every key row, K [N, d] -> [N]."""
+    K = _f64(K)
+    return np.sqrt(np.sum(K * K, axis=1))
+
+
+def attention_probs(K, Q, window: int) -> np.ndarray:
+    """Softmax attention of the window queries over the N candidates (reading R3, R4).
+
+    K [N, d]; Q [G, w, d] -> P [G, w, N], each row summing to 1 over the keys
+    it can see and 0 on the keys it cannot.
+    """
+    K = _f64(K)
+    Q = _f64(Q)
+    n, d = K.shape
+    g, w, _ = Q.shape
+    assert w == window
+    logits = (Q.reshape(g * w, d) @ K.T) / math.sqrt(d)          # [G*w, N]
+    logits = logits.reshape(g, w, n)
+    # Window query r attends to keys 0 .. N-w+r (causal inside the window).
+    visible = np.arange(n)[None, :] <= (n - w + np.arange(w))[:, None]   # [w, N]
+    logits = np.where(visible[None], logits, -np.inf)
+    m = logits.max(axis=2, keepdims=True)
+    e = np.exp(logits - m)
+    return e / e.sum(axis=2, keepdims=True)
+
+
+def importance(K, Q, window: int) -> np.ndarray:
+    """I_j = max over query heads g of the mean over window queries r of P[g, r, j]."""
+    P = attention_probs(K, Q, window)
+    return P.mean(axis=1).max(axis=0)
+
+
+def redundancy(K) -> np.ndarray:
+    """R_i = max_{j<i} cos(k_i, k_j), R_0 = 0 (readings R1, R2)."""
+    K = _f64(K)
+    n = K.shape[0]
+    norms = key_norms(K)
+    R = np.zeros(n)
+    for i in range(1, n):
+        dots = K[:i] @ K[i]
+        denom = norms[:i] * norms[i]
+        cos = np.divide(dots, denom, out=np.zeros(i), where=denom > 0)
+        R[i] = cos.max()
+    return R
+
+
+def redundancy_rows(K, rows) -> np.ndarray:
+    """R_i for the listed rows only (same definition as :func:`redundancy`)."""
+    K = _f64(K)
+    norms = key_norms(K)
+    out = np.zeros(len(rows))
+    for k, i in enumerate(rows):
+        i = int(i)
+        if i == 0:
+            continue
+        dots = K[:i] @ K[i]
+        denom = norms[:i] * norms[i]
+        cos = np.divide(dots, denom, out=np.zeros(i), where=denom > 0)
+        out[k] = cos.max()
+    return out
+
+
+def joint_score(I, R, lam: float) -> np.ndarray:
+    """Z = lam*I - (1-lam)*R."""
+    return lam * _f64(I) - (1.0 - lam) * _f64(R)
+
+
+def select(Z, n: int, budget: int, window: int) -> np.ndarray:
+    """Kept candidate indices, ascending (readings R6, R7)."""
+    if budget <= window:
+        raise ValueError("budget must exceed window")
+    if n <= budget:
+        return np.arange(n, dtype=np.int64)
+    Z = _f64(Z)
+    cand = n - window
+    idx = np.arange(cand)
+    # Primary key: Z descending; secondary key: index ascending.
+    order = np.lexsort((idx, -Z[:cand]))
+    chosen = order[:budget - window]
+    return np.sort(np.concatenate([chosen, np.arange(cand, n)])).astype(np.int64)
+
+
+def compress_head(K, V, Q, budget: int, window: int, lam: float) -> dict:
+    """The whole step for one head: scores, selection and the compacted rows.
+
+    K, V [N, d]; Q [G, w, d]. Returns dict(kept, K_out, V_out, I, R, Z), the
+    scores being None when N <= budget (nothing is scored).
+    """
+    K = np.asarray(K)
+    V = np.asarray(V)
+    n = K.shape[0]
+    if budget <= window:
+        raise ValueError("budget must exceed window")
+    if n <= budget:
+        kept = np.arange(n, dtype=np.int64)
+        return dict(kept=kept, K_out=K[kept].copy(), V_out=V[kept].copy(),
+                    I=None, R=None, Z=None)
+    I = importance(K, Q, window)
+    R = redundancy(K)
+    Z = joint_score(I, R, lam)
+    kept = select(Z, n, budget, window)
+    return dict(kept=kept, K_out=K[kept].copy(), V_out=V[kept].copy(), I=I, R=R, Z=Z)
+
+
+def compress_dense(K, V, Q, budget: int, window: int, lam: float, heads=None) -> list:
+    """:func:`compress_head` over heads (all, or the listed ones). K [Bh, N, d]."""
+    heads = range(K.shape[0]) if heads is None else heads
+    return [compress_head(K[h], V[h], Q[h], budget, window, lam) for h in heads]
+
+
+def logical_rows(pages, page_table_row, n: int, head: int, page_size: int) -> np.ndarray:
+    """Rows 0..n-1 of one (sequence, head) read through its page table row."""
+    t = np.arange(n)
+    return np.asarray(pages)[page_table_row[t // page_size], head, t % page_size]
+
+
+def compress_paged(K_pages, V_pages, page_table, seq_len, budget, Q, free_list,
+                   window: int, lam: float, page_size: int) -> dict:
+    """Paged compression with page return (reading R8).
+
+    K_pages, V_pages [P, H, page_size, d]; page_table [S, maxp]; seq_len,
+    budget [S]; Q [S, H, G, w, d]; free_list: the free page ids before the
+    call. Returns dict(K_pages, V_pages, page_table, free_list, kept) where
+    kept[s][h] are the kept logical indices and the pages are new arrays.
+    """
+    Kp = np.array(K_pages, copy=True)
+    Vp = np.array(V_pages, copy=True)
+    table = np.array(page_table, copy=True)
+    freed = [int(x) for x in free_list]
+    kept_all = []
+    n_seq, heads = table.shape[0], Kp.shape[1]
+    for s in range(n_seq):
+        n = int(seq_len[s])
+        b = int(budget[s])
+        if b % page_size != 0:
+            raise ValueError("paged budget must be a multiple of the page size")
+        kept_s = []
+        for h in range(heads):
+            Kl = logical_rows(K_pages, page_table[s], n, h, page_size)
+            Vl = logical_rows(V_pages, page_table[s], n, h, page_size)
+            res = compress_head(Kl, Vl, np.asarray(Q)[s, h], b, window, lam)
+            kept = res["kept"]
+            kept_s.append(kept)
+            if n <= b:
+                continue
+            r = np.arange(len(kept))
+            Kp[page_table[s][r // page_size], h, r % page_size] = Kl[kept]
+            Vp[page_table[s][r // page_size], h, r % page_size] = Vl[kept]
+        kept_all.append(kept_s)
+        if n > b:
+            for p in range(b // page_size, (n + page_size - 1) // page_size):
+                freed.append(int(table[s, p]))
+                table[s, p] = -1
+    return dict(K_pages=Kp, V_pages=Vp, page_table=table,
+                free_list=np.asarray(freed, dtype=np.int64), kept=kept_all)

@@ -1,0 +1,300 @@
+"""Pins for the CPU oracle: checks against facts fixed by the pages and by mathematics.
+
+Each ``check_*`` raises AssertionError on failure. ``test_oracle_pins.py`` runs
+them on the oracle as written; ``test_oracle_mutants.py`` plants plausible
+mistakes in the oracle and confirms at least one check fails for each.
+
+Pinned facts and where they come from:
+  * pure-Python brute force (independent loops, exhaustive subset search) on
+    tiny heads agrees with the oracle;
+  * lam = 1 reduces Z to the importance alone and the selection to an
+    attention top-k (the pages' attention-only ablation, SnapKV-like);
+    lam = 0 reduces Z to -R (the redundancy-only ablation);
+  * an exact copy (up to a positive scale) of an earlier key has cosine 1,
+    the largest redundancy possible; orthogonal keys have redundancy 0;
+    cosine is invariant to scaling keys;
+  * zero (or key-orthogonal) queries give a uniform causal softmax, whose
+    pooled importance has a closed form;
+  * softmax rows sum to one; pooled importance is at most G in total;
+    identical query heads pool to the single-head importance;
+  * a hand-worked 2-D example with keys at known angles;
+  * structure: output size, window kept, ascending order, K'/V' = gather;
+  * paged: page table and free list follow in closed form from lengths and
+    budgets; live slots hold the kept rows; nothing else changes.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from oracle import bruteforce as bf
+from oracle import rkv_oracle as orc
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def tiny_case(seed):
+    rng = _rng(seed)
+    n = int(rng.integers(6, 12))
+    d = int(rng.integers(2, 9))
+    g = int(rng.integers(1, 4))
+    w = int(rng.integers(1, 4))
+    b = int(rng.integers(w + 1, n))
+    lam = float(rng.choice([0.1, 0.3, 0.7, 0.9]))
+    K = rng.standard_normal((n, d))
+    # a near-duplicate and an exact copy make redundancy non-trivial
+    K[n - 2] = K[1] + 0.01 * rng.standard_normal(d)
+    K[n // 2] = 2.0 * K[0]
+    V = rng.standard_normal((n, d))
+    Q = rng.standard_normal((g, w, d))
+    return K, V, Q, b, w, lam
+
+
+def _close(a, b, tol=1e-12):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    err = np.abs(a - b) / np.maximum(1.0, np.abs(b))
+    assert np.all(err <= tol), f"max rel err {err.max()}"
+
+
+def check_bruteforce(seed):
+    K, V, Q, b, w, lam = tiny_case(seed)
+    o = orc.compress_head(K, V, Q, b, w, lam)
+    r = bf.compress_head_bf(K.tolist(), V.tolist(), Q.tolist(), b, w, lam)
+    _close(o["I"], r["I"])
+    _close(o["R"], r["R"])
+    _close(o["Z"], r["Z"])
+    assert list(o["kept"]) == list(r["kept"]), (list(o["kept"]), r["kept"])
+
+
+def check_select_ties(seed):
+    """Integer-valued Z with many exact ties, window scored lowest."""
+    rng = _rng(seed)
+    n = int(rng.integers(7, 13))
+    w = int(rng.integers(1, 4))
+    b = int(rng.integers(w + 1, n))
+    Z = rng.integers(-2, 3, size=n).astype(np.float64)
+    Z[n - w:] = -100.0
+    if seed % 2:
+        Z[rng.integers(0, n - w)] = -0.0
+    kept = orc.select(Z, n, b, w)
+    assert list(kept) == bf.select_bf(Z.tolist(), n, b, w)
+
+
+def check_lambda_one(seed):
+    K, V, Q, b, w, _ = tiny_case(seed)
+    n = K.shape[0]
+    o = orc.compress_head(K, V, Q, b, w, 1.0)
+    assert np.array_equal(o["Z"], o["I"])
+    I = orc.importance(K, Q, w)
+    top = np.argsort(-I[:n - w], kind="stable")[:b - w]
+    assert list(o["kept"]) == sorted(list(top) + list(range(n - w, n)))
+
+
+def check_lambda_zero(seed):
+    K, V, Q, b, w, _ = tiny_case(seed)
+    n = K.shape[0]
+    o = orc.compress_head(K, V, Q, b, w, 0.0)
+    assert np.array_equal(o["Z"], -o["R"])
+    R = orc.redundancy(K)
+    least = np.argsort(R[:n - w], kind="stable")[:b - w]
+    assert list(o["kept"]) == sorted(list(least) + list(range(n - w, n)))
+
+
+def check_duplicates(seed):
+    rng = _rng(seed)
+    n, d, w = 40, 16, 4
+    b = 30
+    K = rng.standard_normal((n, d))
+    copies = []
+    for t in range(5, n - w, 3):          # 11 later copies outside the window
+        src = int(rng.integers(0, t))
+        K[t] = float(rng.choice([0.5, 1.0, 3.0])) * K[src]
+        copies.append(t)
+    assert len(copies) >= n - b
+    R = orc.redundancy(K)
+    for t in copies:
+        assert abs(R[t] - 1.0) <= 1e-12, R[t]
+        assert R[t] >= R.max() - 1e-12
+    Q = rng.standard_normal((2, w, d))
+    kept = orc.compress_head(K, K, Q, b, w, 0.0)["kept"]
+    evicted = sorted(set(range(n)) - set(kept.tolist()))
+    assert set(evicted) <= set(copies), (evicted, copies)
+
+
+def check_orthogonal(seed):
+    rng = _rng(seed)
+    d = 16
+    n = int(rng.integers(4, d + 1))
+    basis = np.eye(d)[rng.permutation(d)[:n]] * rng.uniform(0.5, 3.0, size=(n, 1))
+    R = orc.redundancy(basis)
+    assert np.array_equal(R, np.zeros(n))
+    Q = rng.standard_normal((2, 2, d))
+    o = orc.compress_head(basis, basis, Q, max(3, n - 2), 2, 0.3) if n > 3 else None
+    if o is not None and o["Z"] is not None:
+        _close(o["Z"], 0.3 * o["I"], 1e-15)
+
+
+def check_scale_invariance(seed):
+    rng = _rng(seed)
+    K = rng.standard_normal((30, 12))
+    K[20] = K[3]
+    R = orc.redundancy(K)
+    for s in (0.25, 4.0, 1024.0):
+        _close(orc.redundancy(K * s), R, 1e-12)
+
+
+def uniform_importance(n, w):
+    """Closed form of the pooled importance when every logit is equal."""
+    out = np.zeros(n)
+    for j in range(n):
+        # window query r sees keys 0 .. n-w+r, i.e. n-w+r+1 keys
+        out[j] = sum(1.0 / (n - w + r + 1) for r in range(w) if j <= n - w + r) / w
+    return out
+
+
+def check_zero_queries(seed):
+    rng = _rng(seed)
+    n = int(rng.integers(5, 60))
+    w = int(rng.integers(1, min(8, n)))
+    g = int(rng.integers(1, 5))
+    d = 8
+    K = rng.standard_normal((n, d))
+    I = orc.importance(K, np.zeros((g, w, d)), w)
+    _close(I, uniform_importance(n, w), 1e-13)
+    # queries orthogonal to every key give the same uniform softmax
+    K2 = np.concatenate([rng.standard_normal((n, d - 1)), np.zeros((n, 1))], axis=1)
+    Qo = np.zeros((g, w, d))
+    Qo[..., -1] = rng.standard_normal((g, w))
+    _close(orc.importance(K2, Qo, w), uniform_importance(n, w), 1e-13)
+    # one zero head beside a random head: max pooling never drops below the
+    # uniform head, and equals the larger of the two heads' window means
+    Qm = np.concatenate([np.zeros((1, w, d)), 3.0 * rng.standard_normal((1, w, d))])
+    Im = orc.importance(K, Qm, w)
+    P1 = orc.attention_probs(K, Qm[1:], w)[0].mean(axis=0)
+    _close(Im, np.maximum(uniform_importance(n, w), P1), 1e-13)
+
+
+def check_logit_scale(seed):
+    """One window query, one key aligned with it: softmax of a single logit
+    a = q.k/sqrt(d) among N-1 zero logits is e^a / (e^a + N - 1)."""
+    rng = _rng(seed)
+    d = int(rng.choice([4, 16, 64]))
+    n = int(rng.integers(3, 20))
+    K = np.zeros((n, d))
+    K[:, 1:] = rng.standard_normal((n, d - 1))
+    K[0, 0] = 2.0
+    q = np.zeros((1, 1, d))
+    q[0, 0, 0] = 3.0                       # q.k_0 = 6, q.k_j = 0 for j > 0
+    a = 6.0 / math.sqrt(d)
+    I = orc.importance(K, q, 1)
+    _close(I[0], math.exp(a) / (math.exp(a) + n - 1), 1e-14)
+
+
+def check_softmax_rows(seed):
+    rng = _rng(seed)
+    n, d, g, w = 50, 16, 3, 5
+    K = rng.standard_normal((n, d))
+    Q = 2.0 * rng.standard_normal((g, w, d))
+    P = orc.attention_probs(K, Q, w)
+    _close(P.sum(axis=2), np.ones((g, w)), 1e-13)
+    for r in range(w):
+        assert np.all(P[:, r, n - w + r + 1:] == 0.0)
+        assert np.all(P[:, r, :n - w + r + 1] > 0.0)
+    I = orc.importance(K, Q, w)
+    assert I.sum() <= g + 1e-12
+    assert np.all(I >= P.mean(axis=1).min(axis=0) - 1e-15)
+
+
+def check_identical_heads(seed):
+    rng = _rng(seed)
+    n, d, w = 30, 8, 4
+    K = rng.standard_normal((n, d))
+    q = rng.standard_normal((1, w, d))
+    _close(orc.importance(K, np.repeat(q, 4, axis=0), w), orc.importance(K, q, w), 1e-15)
+
+
+def check_hand_example(seed=0):
+    """2-D keys at known angles; zero queries; lam = 0 and lam = 1."""
+    K = np.array([[1.0, 0.0], [0.0, 2.0], [3.0, 3.0], [-1.0, 0.0], [2.0, 0.0], [0.0, -1.0]])
+    R = orc.redundancy(K)
+    # k1 is orthogonal to k0; k2 is at 45 degrees to both; k3 is opposite k0,
+    # orthogonal to k1, 135 degrees from k2; k4 is parallel to k0; k5 is
+    # orthogonal to k0, k3, k4 and opposite k1.
+    expect = [0.0, 0.0, math.sqrt(0.5), 0.0, 1.0, 0.0]
+    _close(R, expect, 1e-15)
+    Q = np.zeros((1, 1, 2))
+    I = orc.importance(K, Q, 1)
+    _close(I, np.full(6, 1.0 / 6.0), 1e-15)
+    # lam = 0: Z = -R = [0, 0, -.707, 0, -1, 0]; window {5}; three of 0..4 by Z
+    assert list(orc.compress_head(K, K, Q, 4, 1, 0.0)["kept"]) == [0, 1, 3, 5]
+    # lam = 1 with uniform I: all ties, the earliest indices win
+    assert list(orc.compress_head(K, K, Q, 4, 1, 1.0)["kept"]) == [0, 1, 2, 5]
+    # lam = 0.5: Z = (1/6 - R)/2 -> 4 lowest, then 2; keep 0, 1, 3
+    assert list(orc.compress_head(K, K, Q, 4, 1, 0.5)["kept"]) == [0, 1, 3, 5]
+
+
+def check_structure(seed):
+    rng = _rng(seed)
+    n = int(rng.integers(10, 80))
+    w = int(rng.integers(1, 6))
+    b = int(rng.integers(w + 1, n + 10))
+    d = 8
+    K = rng.standard_normal((n, d))
+    V = rng.standard_normal((n, d))
+    Q = rng.standard_normal((2, w, d))
+    o = orc.compress_head(K, V, Q, b, w, 0.1)
+    kept = o["kept"]
+    assert len(kept) == min(n, b)
+    assert np.all(np.diff(kept) > 0)
+    if n > b:
+        assert set(range(n - w, n)) <= set(kept.tolist())
+    assert np.array_equal(o["K_out"], K[kept])
+    assert np.array_equal(o["V_out"], V[kept])
+
+
+def check_paged(seed):
+    from synth import paged_case_host
+    ps = 16
+    lens = [40, 100, 16, 130]
+    fracs = [0.5, 0.3, 0.9, 0.4]
+    case = paged_case_host(seed, lens, fracs, kv_heads=2, gqa=2, window=4, lam=0.1,
+                           dtype="f32", page_size=ps, spare_pages=5, d=8)
+    out = orc.compress_paged(case.K_pages, case.V_pages, case.page_table, case.seq_len,
+                             case.budget, case.Q, case.free_list, case.window, case.lam, ps)
+    table = case.page_table.copy()
+    free = list(case.free_list)
+    for s, n in enumerate(case.seq_len):
+        b = int(case.budget[s])
+        if n > b:
+            for p in range(b // ps, -(-int(n) // ps)):
+                free.append(int(table[s, p]))
+                table[s, p] = -1
+    assert np.array_equal(out["page_table"], table)
+    assert list(out["free_list"]) == free
+    live = np.zeros(case.K_pages.shape[:1] + case.K_pages.shape[1:3], dtype=bool)
+    for s, n in enumerate(case.seq_len):
+        n = int(n)
+        for h in range(case.kv_heads):
+            kept = out["kept"][s][h]
+            assert len(kept) == min(n, int(case.budget[s]))
+            for r, src in enumerate(kept):
+                pg_src = case.page_table[s, src // ps]
+                pg_dst = case.page_table[s, r // ps]
+                assert np.array_equal(out["K_pages"][pg_dst, h, r % ps],
+                                      case.K_pages[pg_src, h, src % ps])
+                assert np.array_equal(out["V_pages"][pg_dst, h, r % ps],
+                                      case.V_pages[pg_src, h, src % ps])
+                live[pg_dst, h, r % ps] = True
+    assert np.array_equal(out["K_pages"][~live], case.K_pages[~live])
+    assert np.array_equal(out["V_pages"][~live], case.V_pages[~live])
+
+
+ALL_CHECKS = [check_bruteforce, check_select_ties, check_lambda_one, check_lambda_zero,
+              check_duplicates, check_orthogonal, check_scale_invariance, check_zero_queries,
+              check_softmax_rows, check_identical_heads, check_logit_scale, check_hand_example, check_structure,
+              check_paged]

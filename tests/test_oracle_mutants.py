@@ -1,0 +1,114 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check the pins catch each one.
+
+Every mutant below is the oracle with one step changed: a dropped or swapped
+pooling, a wrong mask or scale, a wrong sign or weight, a wrong index range, a
+wrong tie-break. If some mutant passed every pin, the pins would not be strong
+enough to trust the oracle; this test fails in that case.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle_pins as pins
+from oracle import rkv_oracle as orc
+
+_orig_probs = orc.attention_probs
+_orig_red = orc.redundancy
+
+
+def _probs_variant(K, Q, window, mask_shift=0, scale_pow=0.5, causal=True, swap_r=False):
+    K = np.asarray(K, dtype=np.float64)
+    Q = np.asarray(Q, dtype=np.float64)
+    n, d = K.shape
+    g, w, _ = Q.shape
+    logits = (Q.reshape(g * w, d) @ K.T / d ** scale_pow).reshape(g, w, n)
+    rr = np.arange(w)[::-1] if swap_r else np.arange(w)
+    if causal:
+        vis = np.arange(n)[None, :] <= (n - w + rr + mask_shift)[:, None]
+        logits = np.where(vis[None], logits, -np.inf)
+    m = logits.max(axis=2, keepdims=True)
+    e = np.exp(logits - m)
+    return e / e.sum(axis=2, keepdims=True)
+
+
+def _red_variant(K, mode):
+    K = np.asarray(K, dtype=np.float64)
+    n = K.shape[0]
+    nrm = np.sqrt((K * K).sum(1))
+    C = (K @ K.T) / np.outer(nrm, nrm)
+    R = np.zeros(n)
+    for i in range(n):
+        if mode == "self":
+            R[i] = C[i, :i + 1].max()
+        elif mode == "later":
+            R[i] = C[i, i + 1:].max() if i + 1 < n else 0.0
+        elif mode == "mean":
+            R[i] = C[i, :i].mean() if i else 0.0
+        elif mode == "unnormalised":
+            R[i] = (K[:i] @ K[i]).max() if i else 0.0
+        elif mode == "symmetric":
+            R[i] = np.delete(C[i], i).max()
+    return R
+
+
+def _select_variant(Z, n, budget, window, mode):
+    if budget <= window:
+        raise ValueError
+    if n <= budget:
+        return np.arange(n)
+    Z = np.asarray(Z, dtype=np.float64)
+    idx = np.arange(n)
+    if mode == "no_window":
+        order = np.lexsort((idx, -Z))
+        return np.sort(order[:budget])
+    cand = n - window
+    if mode == "tie_high":
+        order = np.lexsort((-idx[:cand], -Z[:cand]))
+    elif mode == "lowest":
+        order = np.lexsort((idx[:cand], Z[:cand]))
+    return np.sort(np.concatenate([order[:budget - window], np.arange(cand, n)]))
+
+
+MUTANTS = {
+    "mean_pool_over_heads": ("importance", lambda K, Q, w: orc.attention_probs(K, Q, w).mean(1).mean(0)),
+    "sum_over_queries": ("importance", lambda K, Q, w: orc.attention_probs(K, Q, w).sum(1).max(0)),
+    "pool_order_swapped": ("importance", lambda K, Q, w: orc.attention_probs(K, Q, w).max(1).mean(0)),
+    "no_causal_mask": ("attention_probs", lambda K, Q, w: _probs_variant(K, Q, w, causal=False)),
+    "mask_off_by_one": ("attention_probs", lambda K, Q, w: _probs_variant(K, Q, w, mask_shift=1)),
+    "mask_reversed": ("attention_probs", lambda K, Q, w: _probs_variant(K, Q, w, swap_r=True)),
+    "scale_1_over_d": ("attention_probs", lambda K, Q, w: _probs_variant(K, Q, w, scale_pow=1.0)),
+    "no_scale": ("attention_probs", lambda K, Q, w: _probs_variant(K, Q, w, scale_pow=0.0)),
+    "red_includes_self": ("redundancy", lambda K: _red_variant(K, "self")),
+    "red_later_tokens": ("redundancy", lambda K: _red_variant(K, "later")),
+    "red_mean": ("redundancy", lambda K: _red_variant(K, "mean")),
+    "red_unnormalised": ("redundancy", lambda K: _red_variant(K, "unnormalised")),
+    "red_symmetric": ("redundancy", lambda K: _red_variant(K, "symmetric")),
+    "z_sign_flipped": ("joint_score", lambda I, R, lam: lam * np.asarray(I) + (1 - lam) * np.asarray(R)),
+    "z_weights_swapped": ("joint_score", lambda I, R, lam: (1 - lam) * np.asarray(I) - lam * np.asarray(R)),
+    "window_not_protected": ("select", lambda Z, n, b, w: _select_variant(Z, n, b, w, "no_window")),
+    "ties_to_larger_index": ("select", lambda Z, n, b, w: _select_variant(Z, n, b, w, "tie_high")),
+    "keeps_lowest": ("select", lambda Z, n, b, w: _select_variant(Z, n, b, w, "lowest")),
+}
+
+
+def _some_pin_fails():
+    for check in pins.ALL_CHECKS:
+        for seed in range(3):
+            try:
+                check(seed)
+            except (AssertionError, ValueError, IndexError):
+                return check.__name__
+    return None
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(orc, attr, fn)
+    caught = _some_pin_fails()
+    assert caught is not None, f"mutant {name} passed every pin"
+
+
+def test_unmutated_oracle_passes_all_pins():
+    assert _some_pin_fails() is None

@@ -1,0 +1,55 @@
+"""Input generators: bf16 rounding and the workload structure (no GPU)."""
+import numpy as np
+import pytest
+
+from synth import (CONFIGS, bf16_round, dense_case_host, paged_case_host, segment_layout,
+                   tiny_head_case)
+
+
+def test_bf16_round_matches_torch():
+    import torch
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32),
+                        np.array([1.00390625, 1.01171875, -1.00390625, 0.0, -0.0,
+                                  3.0e38, 1e-40], dtype=np.float32)])
+    ours = bf16_round(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(ours.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_segment_layout(seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n = 1152
+    src = segment_layout(rng, n, 0.40)
+    cov = (src >= 0).mean()
+    assert 0.40 <= cov <= 0.41 + 1e-9
+    t = np.nonzero(src >= 0)[0]
+    assert np.all(src[t] < t)
+    # copied positions are fresh in the source stream is not required; only earlier
+
+
+def test_tiny_case_shape():
+    c = tiny_head_case(0)
+    assert c.K.shape == (1, 96, 128) and c.Q.shape == (1, 4, 8, 128)
+    assert len(c.meta["dup_positions"]) == 29
+    assert np.all(c.meta["dup_sources"] < c.meta["dup_positions"])
+
+
+def test_dense_host_exact_bf16():
+    c = dense_case_host(1, batch=1, layers=1, kv_heads=2, gqa=4, n=300, budget=256, window=8,
+                        lam=0.1)
+    assert np.array_equal(bf16_round(c.K), c.K)
+    assert 0.39 <= c.meta["coverage"] <= 0.42
+
+
+def test_paged_host_layout():
+    c = paged_case_host(0, [40, 100, 130], [0.5, 0.3, 0.4], kv_heads=2, gqa=2, window=4)
+    used = c.page_table[c.page_table >= 0]
+    allp = np.concatenate([used, c.free_list])
+    assert sorted(allp.tolist()) == list(range(c.meta["pool"]))
+    assert np.all(c.budget % 16 == 0)
+
+
+def test_configs_present():
+    assert sorted(CONFIGS) == [0, 1, 2, 3, 4]
