@@ -1,0 +1,94 @@
+"""ctypes view of librkv.so (the C ABI in include/rkv.h). No computation here."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librkv.so")
+
+RKV_OK = 0
+RKV_EINVAL = -1
+RKV_EWORKSPACE = -2
+RKV_EFREELIST = -3
+RKV_EUNSUPPORTED = -4
+RKV_EHIP = -5
+RKV_F32 = 0
+RKV_BF16 = 1
+
+STATUS_NAMES = {RKV_OK: "RKV_OK", RKV_EINVAL: "RKV_EINVAL", RKV_EWORKSPACE: "RKV_EWORKSPACE",
+                RKV_EFREELIST: "RKV_EFREELIST", RKV_EUNSUPPORTED: "RKV_EUNSUPPORTED",
+                RKV_EHIP: "RKV_EHIP"}
+
+EXPORTS = ["rkv_workspace_size", "rkv_compress", "rkv_paged_workspace_size", "rkv_compress_paged",
+           "rkv_last_error", "rkv_timing_enable", "rkv_timing_read"]
+
+
+class DenseDesc(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("n_cand", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("gqa_group", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("budget", ctypes.c_int32),
+                ("mix_lambda", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("kv_head_stride", ctypes.c_int64), ("out_head_stride", ctypes.c_int64)]
+
+
+class PagedDesc(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("gqa_group", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("mix_lambda", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("page_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
+                ("slot_stride", ctypes.c_int64)]
+
+
+class RkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load():
+    """Load librkv.so, raising if it has not been built. Never falls back."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m decode_kv_cache_03_amd.build` (no CPU fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_float
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    lib.rkv_workspace_size.argtypes = [ctypes.POINTER(DenseDesc)]
+    lib.rkv_workspace_size.restype = sz
+    lib.rkv_compress.argtypes = [ctypes.POINTER(DenseDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                 sz, vp]
+    lib.rkv_compress.restype = ctypes.c_int
+    lib.rkv_paged_workspace_size.argtypes = [ctypes.POINTER(PagedDesc), pi32, pi32]
+    lib.rkv_paged_workspace_size.restype = sz
+    lib.rkv_compress_paged.argtypes = [ctypes.POINTER(PagedDesc), vp, vp, vp, pi32, pi32, vp, vp, vp,
+                                       i32, pi32, vp, vp, sz, vp]
+    lib.rkv_compress_paged.restype = ctypes.c_int
+    lib.rkv_last_error.argtypes = []
+    lib.rkv_last_error.restype = ctypes.c_char_p
+    lib.rkv_timing_enable.argtypes = [ctypes.c_int]
+    lib.rkv_timing_enable.restype = ctypes.c_int
+    lib.rkv_timing_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), pi32,
+                                    ctypes.POINTER(ctypes.c_double), i32]
+    lib.rkv_timing_read.restype = ctypes.c_int
+    _ = f32
+    _lib = lib
+    return lib
+
+
+def check(status: int) -> None:
+    if status != RKV_OK:
+        msg = load().rkv_last_error().decode(errors="replace")
+        raise RkvError(status, msg)
+
+
+def last_error() -> str:
+    return load().rkv_last_error().decode(errors="replace")

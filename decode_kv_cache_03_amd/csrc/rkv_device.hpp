@@ -1,0 +1,127 @@
+// Device-side building blocks shared by the R-KV kernels (gfx950, wave64).
+//
+// Fragments. Every dense contraction here has head_dim = 128 as its inner
+// dimension and runs on the 32x32 MFMA tiles of CDNA4:
+//   bf16: v_mfma_f32_32x32x16_bf16, 8 bf16 of k per lane per instruction;
+//   fp32: v_mfma_f32_32x32x2_f32,   1 fp32 of k per lane per instruction.
+// Lane l of a 32-row operand holds row (l & 31); the two 32-lane halves hold
+// two disjoint parts of k. Since a dot product may visit k in any order as
+// long as both operands agree, half h (= l >> 5) of every operand takes the
+// contiguous elements [64h, 64h+64) of its 128-element row, streamed as 16-byte
+// chunks: chunk c of half h feeds the instruction(s) of k-step c. So a lane
+// loads 128 contiguous bytes (bf16) or 256 (fp32) of one row, and A and B
+// fragments are loaded by the same code.
+//
+// Accumulator layout of a 32x32 fp32 tile: lane l, register v holds
+//   row 8*(v/4) + 4*(l/32) + (v%4),  column l % 32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rkv {
+
+constexpr int kD = 128;        // head_dim
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+typedef uint16_t bf16_bits;    // storage type of a bfloat16 element
+
+// log2(e) / sqrt(128): logits are kept in base-2 units so softmax uses exp2.
+constexpr float kLogitScaleLog2 = (float)(1.4426950408889634 / 11.313708498984761);
+
+template <typename T> struct Elem;
+template <> struct Elem<bf16_bits> {
+  static constexpr int kRowChunks = 16;    // 16-byte chunks per 128-element row
+  static constexpr int kHalfChunks = 8;
+  static constexpr int kRowBytes = 256;
+};
+template <> struct Elem<float> {
+  static constexpr int kRowChunks = 32;
+  static constexpr int kHalfChunks = 16;
+  static constexpr int kRowBytes = 512;
+};
+
+__device__ __forceinline__ u32x4_t ld16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4_t v) {
+  *reinterpret_cast<u32x4_t*>(p) = v;
+}
+__device__ __forceinline__ u32x4_t zero16() {
+  u32x4_t z = {0u, 0u, 0u, 0u};
+  return z;
+}
+
+// acc += A_chunk * B_chunk over the k-values of one 16-byte chunk per lane.
+template <typename T>
+__device__ __forceinline__ void mma_chunk(f32x16_t& acc, u32x4_t a, u32x4_t b) {
+  if constexpr (sizeof(T) == 2) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+  }
+}
+
+// Sum of squares of the elements in a 16-byte chunk, in fp32.
+template <typename T>
+__device__ __forceinline__ float sumsq_chunk(u32x4_t c) {
+  float s = 0.f;
+  if constexpr (sizeof(T) == 2) {
+    uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float lo = __uint_as_float(w[i] << 16);
+      float hi = __uint_as_float(w[i] & 0xffff0000u);
+      s = fmaf(lo, lo, s);
+      s = fmaf(hi, hi, s);
+    }
+  } else {
+    float f[4] = {__uint_as_float(c.x), __uint_as_float(c.y), __uint_as_float(c.z), __uint_as_float(c.w)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s = fmaf(f[i], f[i], s);
+  }
+  return s;
+}
+
+// Row of accumulator register v for lane `lane` in a 32x32 tile.
+__device__ __forceinline__ int acc_row(int v, int lane) {
+  return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Order-preserving map of a float to uint32 (larger float -> larger key);
+// -0 is folded onto +0 first so the two compare equal.
+__device__ __forceinline__ uint32_t order_key(float z) {
+  uint32_t b = __float_as_uint(z + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Inclusive scan of one uint32 per thread over a 256-thread block.
+// `scratch` must hold 4 uint32 and be shared. Also returns the block total.
+__device__ __forceinline__ uint32_t block_inclusive_scan256(uint32_t v, uint32_t* scratch,
+                                                            uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint32_t o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63) scratch[wave] = v;
+  __syncthreads();
+  uint32_t w0 = scratch[0], w1 = scratch[1], w2 = scratch[2], w3 = scratch[3];
+  uint32_t before = (wave > 0 ? w0 : 0u) + (wave > 1 ? w1 : 0u) + (wave > 2 ? w2 : 0u);
+  *total = w0 + w1 + w2 + w3;
+  __syncthreads();
+  return v + before;
+}
+
+}  // namespace rkv

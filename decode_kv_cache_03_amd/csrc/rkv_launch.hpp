@@ -1,0 +1,56 @@
+// Kernel launch helper with optional per-launch event timing, and the
+// host-side entry points of each kernel family.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "rkv_problem.hpp"
+
+namespace rkv {
+
+struct TimingSlot;
+// Returns a slot whose start event has been recorded on `st`, or nullptr when
+// timing is off (or its record buffer is full).
+TimingSlot* timing_begin(const char* name, hipStream_t st);
+void timing_end(TimingSlot* slot, hipStream_t st);
+
+template <typename... KArgs, typename... Args>
+hipError_t launch(const char* name, void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                  hipStream_t st, Args... args) {
+  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
+  TimingSlot* ts = timing_begin(name, st);
+  kern<<<grid, block, shmem, st>>>(args...);
+  hipError_t e = hipGetLastError();
+  timing_end(ts, st);
+  return e;
+}
+
+// Importance: rinv [units][N], I [units][N]; part/fin are statistics scratch.
+template <typename T, class P>
+hipError_t run_k1(const P& p, int nqb, int k1_items, int num_units, float* part, float* fin,
+                  float* rinv, float* imp, int rpg_shift, hipStream_t st);
+
+// Redundancy and joint score: Z [units][N] (and R when dbg_R != nullptr).
+template <typename T, class P>
+hipError_t run_k2(const P& p, int k2_items, const float* rinv, const float* imp, float* Z,
+                  float* dbg_R, float lam, hipStream_t st);
+
+// Selection: kept indices per unit (ascending), from Z.
+template <class P>
+hipError_t run_k4(const P& p, int units, const float* Z, int32_t* kept, int fill_tail,
+                  hipStream_t st);
+
+// Dense gather of the kept rows into K_out / V_out.
+template <typename T>
+hipError_t run_k5_dense(const DenseProblem<T>& p, const int32_t* kept, T* K_out, T* V_out,
+                        int64_t out_stride, int nkeep, hipStream_t st);
+
+// Paged in-place compaction and page return.
+template <typename T>
+hipError_t run_k5_paged(const PagedProblem<T>& p, T* Kp, T* Vp, const int32_t* kept,
+                        hipStream_t st);
+hipError_t run_free_pages(int32_t* page_table, int maxp, const int32_t* seq_len,
+                          const int32_t* bud, const int32_t* free_off, int ps_shift, int num_seqs,
+                          int32_t* free_list, int32_t free_start, hipStream_t st);
+
+}  // namespace rkv

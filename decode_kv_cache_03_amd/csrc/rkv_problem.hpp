@@ -1,0 +1,139 @@
+// Where a unit's rows, queries, scores and kept indices live.
+//
+// A unit is one (sequence, layer, KV head) whose N candidates are scored
+// together. Two layouts are served by the same kernels through these
+// policies:
+//   Dense: unit u has rows K + u*kv_stride + t*128; all units share N and B.
+//   Paged: unit u = (s, hk) with s = u / H; row t of the unit lives in page
+//          page_table[s][t >> ps_shift] at slot t & (page_size-1); N and B
+//          are per sequence. Work items are listed by the host.
+#pragma once
+
+#include "rkv_device.hpp"
+
+namespace rkv {
+
+constexpr int kK1Keys = 256;   // keys per importance work item (4 waves x 64)
+constexpr int kK2Rows = 256;   // rows per redundancy work item (4 waves x 64)
+constexpr int kK2Cols = 64;    // columns per LDS tile of the redundancy kernel
+
+template <typename T>
+struct DenseProblem {
+  const T* K;
+  const T* V;
+  const T* Q;              // [units][G][w][128]
+  int64_t kv_stride;       // elements between units of K and V
+  int num_units, N, B, G, W;
+  int k1_chunks;           // ceil(N / kK1Keys)
+  int k2_blocks;           // ceil(N / kK2Rows)
+
+  __device__ int n(int) const { return N; }
+  __device__ int budget(int) const { return B; }
+  __device__ const T* krow(int u, int t) const { return K + (int64_t)u * kv_stride + (int64_t)t * kD; }
+  __device__ const T* vrow(int u, int t) const { return V + (int64_t)u * kv_stride + (int64_t)t * kD; }
+  __device__ const T* q(int u) const { return Q + (int64_t)u * G * W * kD; }
+  __device__ int64_t score_off(int u) const { return (int64_t)u * N; }
+  __device__ int64_t kept_off(int u) const { return (int64_t)u * B; }
+
+  // importance work item -> (unit, chunk); partial-statistics slot
+  __device__ bool k1_item(int b, int& u, int& c) const {
+    u = b / k1_chunks;
+    c = b - u * k1_chunks;
+    return u < num_units;
+  }
+  __device__ int64_t k1_slot(int u, int c) const { return (int64_t)u * k1_chunks + c; }
+  __device__ int k1_nchunks(int) const { return k1_chunks; }
+
+  // redundancy work item -> (unit, row block). The blocks of one unit are
+  // placed on one XCD (workgroups go to XCDs round-robin by index), so the
+  // unit's keys are re-read from that XCD's L2; the longest block goes first.
+  __device__ bool k2_item(int b, int& u, int& blk) const {
+    const int x = b & 7;
+    const int k = b >> 3;
+    const int hl = k / k2_blocks;
+    const int ib = k - hl * k2_blocks;
+    u = hl * 8 + x;
+    blk = k2_blocks - 1 - ib;
+    return u < num_units;
+  }
+  __device__ bool unit_item(int b, int& u) const {
+    u = b;
+    return u < num_units;
+  }
+  __device__ bool select_item(int b, int& u) const { return unit_item(b, u); }
+};
+
+template <typename T>
+struct PagedProblem {
+  const T* Kp;
+  const T* Vp;
+  const T* Q;                // [S][H][G][w][128]
+  const int32_t* page_table; // [S][maxp]
+  int64_t page_stride, head_stride, slot_stride;
+  int maxp, num_pages, ps_shift, H, G, W;
+  const int32_t* seq_len;    // device [S]
+  const int32_t* bud;        // device [S]
+  const int64_t* score_base; // device [S]: H * sum_{s'<s} N_s'
+  const int64_t* kept_base;  // device [S]: H * sum_{s'<s} min(N_s', B_s')
+  const int64_t* k1_base;    // device [S*H]: first partial-statistics slot of each unit
+  const int2* k1_list;       // importance work items (unit, chunk)
+  int k1_count;
+  const int2* k2_list;       // redundancy work items (unit, block); unit -1 = idle
+  int k2_count;
+  const int32_t* unit_list;  // units with N > B (compaction)
+  int unit_count;
+  int all_units;             // S * H
+
+  __device__ int n(int u) const { return seq_len[u / H]; }
+  __device__ int budget(int u) const { return bud[u / H]; }
+  __device__ const T* row_in(const T* pool, int u, int t) const {
+    const int s = u / H;
+    const int hk = u - s * H;
+    int pg = page_table[(int64_t)s * maxp + (t >> ps_shift)];
+    // Out-of-range page ids are never dereferenced: the row reads as page 0's
+    // slot instead (results for such a table are undefined, memory stays safe).
+    pg = (pg >= 0 && pg < num_pages) ? pg : 0;
+    return pool + (int64_t)pg * page_stride + (int64_t)hk * head_stride +
+           (int64_t)(t & ((1 << ps_shift) - 1)) * slot_stride;
+  }
+  __device__ const T* krow(int u, int t) const { return row_in(Kp, u, t); }
+  __device__ const T* vrow(int u, int t) const { return row_in(Vp, u, t); }
+  __device__ const T* q(int u) const { return Q + (int64_t)u * G * W * kD; }
+  __device__ int64_t score_off(int u) const {
+    const int s = u / H;
+    return score_base[s] + (int64_t)(u - s * H) * seq_len[s];
+  }
+  __device__ int64_t kept_off(int u) const {
+    const int s = u / H;
+    const int nb = min(seq_len[s], bud[s]);
+    return kept_base[s] + (int64_t)(u - s * H) * nb;
+  }
+  __device__ bool k1_item(int b, int& u, int& c) const {
+    if (b >= k1_count) return false;
+    const int2 it = k1_list[b];
+    u = it.x;
+    c = it.y;
+    return true;
+  }
+  __device__ int64_t k1_slot(int u, int c) const { return k1_base[u] + c; }
+  __device__ int k1_nchunks(int u) const { return (n(u) + kK1Keys - 1) / kK1Keys; }
+  __device__ bool k2_item(int b, int& u, int& blk) const {
+    if (b >= k2_count) return false;
+    const int2 it = k2_list[b];
+    u = it.x;
+    blk = it.y;
+    return u >= 0;
+  }
+  __device__ bool unit_item(int b, int& u) const {
+    if (b >= unit_count) return false;
+    u = unit_list[b];
+    return true;
+  }
+  // selection visits every unit: those with N <= B get the identity
+  __device__ bool select_item(int b, int& u) const {
+    u = b;
+    return b < all_units;
+  }
+};
+
+}  // namespace rkv

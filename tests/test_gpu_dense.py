@@ -1,0 +1,202 @@
+"""GPU parity of the dense path: rkv_compress (through the C ABI) vs the CPU oracle."""
+import numpy as np
+import pytest
+
+import parity as par
+from oracle import rkv_oracle as orc
+from synth import CONFIGS, dense_case_device, dense_case_host, tiny_head_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rkv():
+    import torch
+    assert torch.cuda.is_available(), "gpu tests need a GPU"
+    import decode_kv_cache_03_amd as mod
+    return mod
+
+
+def _run(rkv, case, debug=True, **kw):
+    import torch
+    K = par.to_device(case.K, case.dtype)
+    V = par.to_device(case.V, case.dtype)
+    Q = par.to_device(case.Q, case.dtype)
+    res = rkv.compress(K, V, Q, case.budget, case.window, case.lam, debug=debug, **kw)
+    torch.cuda.synchronize()
+    return res
+
+
+def _check(case, res, heads=None, what=""):
+    kept = res.kept_idx.cpu().numpy()
+    Ko, Vo = par.to_host_f32(res.K_out), par.to_host_f32(res.V_out)
+    I = res.I.cpu().numpy() if res.I is not None else None
+    R = res.R.cpu().numpy() if res.R is not None else None
+    Z = res.Z.cpu().numpy() if res.Z is not None else None
+    n, b = case.n, case.budget
+    nk = min(n, b)
+    heads = range(case.num_heads) if heads is None else heads
+    for h in heads:
+        par.check_head(case.K[h], case.V[h], case.Q[h], b, case.window, case.lam,
+                       kept[h, :nk], Ko[h, :nk], Vo[h, :nk],
+                       I[h] if I is not None else None, R[h] if R is not None else None,
+                       Z[h] if Z is not None else None, what=f"{what} head {h}")
+        if n < b:
+            assert np.all(kept[h, n:] == -1)
+
+
+def test_tiny_fp32(rkv):
+    c = CONFIGS[0]
+    case = tiny_head_case(0, n=c["n"], budget=c["budget"], window=c["window"], gqa=c["gqa"],
+                          lam=c["lam"])
+    _check(case, _run(rkv, case), what="tiny")
+
+
+def test_llama_one_layer(rkv):
+    c = CONFIGS[1]
+    case = dense_case_host(1, c["batch"], c["layers"], c["kv_heads"], c["gqa"], c["n"], c["budget"],
+                           c["window"], c["lam"], c["dtype"], c["coverage"], c["sigma"])
+    _check(case, _run(rkv, case), what="llama-layer")
+
+
+SHAPES = [
+    # (N, B, w, G, lam, dtype, heads)
+    (700, 512, 8, 5, 0.1, "bf16", 3),      # several tiles, ragged tail
+    (70, 40, 8, 4, 0.1, "bf16", 2),        # one partial tile
+    (257, 200, 8, 2, 0.5, "bf16", 2),      # last importance chunk holds one key
+    (300, 120, 1, 1, 0.1, "bf16", 2),      # w = 1, G = 1
+    (130, 9, 8, 8, 0.1, "bf16", 2),        # B = w + 1, G = 8
+    (500, 300, 12, 3, 0.3, "bf16", 2),     # 16 query rows per head
+    (400, 100, 32, 4, 0.1, "bf16", 1),     # 32 query rows per head, 4 query blocks
+    (200, 150, 8, 2, 0.0, "bf16", 2),      # redundancy only
+    (200, 150, 8, 2, 1.0, "bf16", 2),      # importance only
+    (1153, 1152, 8, 4, 0.1, "bf16", 2),    # N = B + 1
+    (300, 200, 8, 2, 0.1, "f32", 2),
+    (260, 100, 8, 8, 0.1, "f32", 1),       # fp32 with two query blocks
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"N{s[0]}-B{s[1]}-w{s[2]}-G{s[3]}-l{s[4]}-{s[5]}"
+                                               for s in SHAPES])
+def test_shapes(rkv, shape):
+    n, b, w, g, lam, dt, heads = shape
+    case = dense_case_host(11 + n, 1, 1, heads, g, n, b, w, lam, dt, 0.4, 0.02)
+    _check(case, _run(rkv, case), what=str(shape))
+
+
+def test_noop_when_n_le_budget(rkv):
+    case = dense_case_host(3, 1, 1, 3, 4, 100, 128, 8, 0.1, "bf16")
+    _check(case, _run(rkv, case), what="noop")
+    case = dense_case_host(4, 1, 1, 2, 4, 128, 128, 8, 0.1, "bf16")
+    _check(case, _run(rkv, case), what="noop-equal")
+
+
+def test_exact_duplicates_get_max_redundancy(rkv):
+    case = dense_case_host(5, 1, 1, 2, 4, 600, 480, 8, 0.0, "bf16", coverage=0.0)
+    rng = np.random.default_rng(5)
+    copies = sorted(rng.choice(np.arange(50, 590), size=150, replace=False).tolist())
+    for h in range(case.num_heads):
+        for t in copies:
+            case.K[h, t] = case.K[h, int(rng.integers(0, t))] * np.float32(rng.choice([0.5, 2.0]))
+    res = _run(rkv, case)
+    _check(case, res, what="dups")
+    R = res.R.cpu().numpy()
+    kept = res.kept_idx.cpu().numpy()
+    for h in range(case.num_heads):
+        assert np.all(np.abs(R[h, copies] - 1.0) <= 1e-5)
+        evicted = sorted(set(range(600)) - set(kept[h].tolist()))
+        assert set(evicted) <= set(copies)
+
+
+def test_zero_norm_keys(rkv):
+    case = dense_case_host(6, 1, 1, 2, 4, 400, 300, 8, 0.1, "bf16")
+    case.K[:, [0, 17, 200, 333]] = 0.0
+    res = _run(rkv, case)
+    _check(case, res, what="zero-norm")
+    R = res.R.cpu().numpy()
+    assert np.all(R[:, [0, 17, 200, 333]] == 0.0)
+
+
+def test_strided_cache_buffers(rkv):
+    """Units spaced by a cache capacity larger than N, outputs by one larger than B."""
+    import torch
+    case = dense_case_host(7, 1, 1, 4, 4, 600, 500, 8, 0.1, "bf16")
+    cap, ocap = 640, 520
+    Kb = torch.zeros((4, cap, 128), dtype=torch.bfloat16, device="cuda")
+    Vb = torch.zeros_like(Kb)
+    Kb[:, :600] = par.to_device(case.K, "bf16")
+    Vb[:, :600] = par.to_device(case.V, "bf16")
+    Ko = torch.full((4, ocap, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    Vo = torch.full_like(Ko, 7.0)
+    res = rkv.compress(Kb[:, :600], Vb[:, :600], par.to_device(case.Q, "bf16"), 500, 8, 0.1,
+                       K_out=Ko[:, :500], V_out=Vo[:, :500], debug=True)
+    torch.cuda.synchronize()
+    _check(case, res, what="strided")
+    assert torch.all(Ko[:, 500:] == 7.0) and torch.all(Vo[:, 500:] == 7.0)
+
+
+def test_repeat_calls_are_bit_identical(rkv):
+    case = dense_case_host(8, 1, 1, 8, 4, 1152, 1024, 8, 0.1, "bf16")
+    a = _run(rkv, case)
+    b = _run(rkv, case)
+    import torch
+    assert torch.equal(a.kept_idx, b.kept_idx)
+    assert torch.equal(a.Z.view(torch.int32), b.Z.view(torch.int32))
+    assert par.bits_equal(a.K_out, b.K_out) and par.bits_equal(a.V_out, b.V_out)
+
+
+def test_zero_units_is_a_noop(rkv):
+    import torch
+    K = torch.zeros((0, 100, 128), dtype=torch.bfloat16, device="cuda")
+    Q = torch.zeros((0, 4, 8, 128), dtype=torch.bfloat16, device="cuda")
+    res = rkv.compress(K, K.clone(), Q, 64, 8, 0.1)
+    torch.cuda.synchronize()
+    assert res.kept_idx.shape == (0, 64)
+
+
+def _device_case_checks(rkv, case, sample, what):
+    """Full-size device-generated case: oracle on sampled units, structure on all."""
+    import torch
+    res = rkv.compress(case.K, case.V, case.Q, case.budget, case.window, case.lam, debug=True)
+    torch.cuda.synchronize()
+    n, b, w = case.n, case.budget, case.window
+    kept = res.kept_idx
+    # every unit: ascending, window kept, rows are a bit-exact gather
+    assert torch.all(kept[:, 1:] > kept[:, :-1])
+    assert torch.all(kept[:, b - w:] == torch.arange(n - w, n, device="cuda", dtype=torch.int32))
+    idx = kept.long()[..., None].expand(-1, -1, 128)
+    assert par.bits_equal(res.K_out, torch.gather(case.K, 1, idx))
+    assert par.bits_equal(res.V_out, torch.gather(case.V, 1, idx))
+    assert bool(torch.isfinite(res.Z).all())
+    for h in sample:
+        Kh = par.to_host_f32(case.K[h])
+        Vh = par.to_host_f32(case.V[h])
+        Qh = par.to_host_f32(case.Q[h])
+        par.check_head(Kh, Vh, Qh, b, w, case.lam, kept[h].cpu().numpy(),
+                       par.to_host_f32(res.K_out[h]), par.to_host_f32(res.V_out[h]),
+                       res.I[h].cpu().numpy(), res.R[h].cpu().numpy(), res.Z[h].cpu().numpy(),
+                       what=f"{what} unit {h}")
+    return res
+
+
+def test_llama_decode_event_full_size(rkv):
+    """One compression event of the Llama3-8B decode loop: 64 x 32 x 8 = 16384 units."""
+    c = CONFIGS[2]
+    case = dense_case_device(2, c["batch"], c["layers"], c["kv_heads"], c["gqa"], c["n"],
+                             c["budget"], c["window"], c["lam"], c["dtype"], c["coverage"],
+                             c["sigma"])
+    rng = np.random.default_rng(2)
+    sample = [0, 255, 16383] + rng.choice(case.num_heads, 3, replace=False).tolist()
+    _device_case_checks(rkv, case, sample, "llama-event")
+
+
+def test_qwen_full_size_lambda_sweep(rkv):
+    """Qwen-14B shape: 32 x 48 x 8 = 12288 units, N = 2176, lambda in {0, 0.1, 1}."""
+    c = CONFIGS[3]
+    case = dense_case_device(3, c["batch"], c["layers"], c["kv_heads"], c["gqa"], c["n"],
+                             c["budget"], c["window"], 0.0, c["dtype"], c["coverage"], c["sigma"])
+    rng = np.random.default_rng(3)
+    for lam in c["lams"]:
+        case.lam = lam
+        sample = [int(x) for x in rng.choice(case.num_heads, 2, replace=False)]
+        _device_case_checks(rkv, case, sample, f"qwen lam={lam}")
