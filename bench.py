@@ -132,6 +132,9 @@ def main():
     ap.add_argument("--lam", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device-to-device copy kernel three times, so "
+                         "memory counters can be scaled against a known byte count")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the compression step is per-unit independent and "
@@ -141,6 +144,16 @@ def main():
     import torch
     import decode_kv_cache_03_amd as rkv
     from synth import CONFIGS, dense_case_device
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": src.numel() * 2,
+                          "copy_calibration_bytes_written": dst.numel() * 2}), file=sys.stderr)
+        del src, dst
 
     wl = WORKLOADS[args.workload]
     c = CONFIGS[wl["cfg"]]

@@ -18,12 +18,22 @@
 // Nothing N x N is ever stored: each lane keeps running row maxima in
 // registers.
 //
-// Work item = (unit, block of 256 rows). The block's 4 waves own 64 rows
-// each, held as MFMA A fragments in registers for the whole item. Column
-// tiles of 64 keys are staged in LDS (double-buffered, XOR-swizzled 16-byte
-// chunks so fragment reads hit distinct banks) and every wave multiplies its
-// 64 rows by the tile: 2x2 tiles of 32x32x16 per k-step. Only tiles left of
-// the diagonal are visited; tiles crossing it are masked per element.
+// Work item = (unit, block of 128 rows); column tiles of 128 keys are staged
+// in LDS (double-buffered, XOR-swizzled 16-byte chunks so fragment reads hit
+// distinct banks). The 4 waves form a 2x2 grid over each 128x128 step: wave
+// (r, c) holds rows 64r..64r+63 of the block as MFMA A fragments in registers
+// for the whole item and multiplies them by columns 64c..64c+63 of the tile,
+// as 2x2 tiles of 32x32x16 per k-step.
+//
+// The block's own tile (the diagonal one) is loaded first: it supplies the A
+// fragments (read from LDS, so the rows are fetched once) and is the only
+// step that needs the j < i mask; the wave above the diagonal idles on it.
+// The remaining tiles 0..blk-1 lie wholly left of the diagonal and run
+// unmasked. ~95% of wave-steps do useful work at N = 1152.
+//
+// The MFMA issue rate is the budget, so per-lane addresses are computed once:
+// tiles arrive by direct global->LDS loads from a uniform base plus a fixed
+// per-lane offset, and fragment reads use fixed per-lane LDS offsets.
 #include "rkv_problem.hpp"
 #include "rkv_launch.hpp"
 
@@ -35,42 +45,89 @@ struct K2Cfg {
   static constexpr int RC = Elem<T>::kRowChunks;
   static constexpr int RB = Elem<T>::kRowBytes;
   static constexpr int TILE_BYTES = kK2Cols * RB;
-  static constexpr int LOADS = kK2Cols * RC / 256;
-  static constexpr int RED_STRIDE = kK2Rows + 1;   // floats; odd stride avoids bank conflicts
-  static constexpr int RED_BYTES = 32 * RED_STRIDE * 4;
+  static constexpr int LOADS = kK2Cols * RB / 1024 / 4;   // KiB of tile per wave
+  static constexpr int ROWS_PER_KB = 1024 / RB;
+  static constexpr int RED_STRIDE = 68;                   // floats per row of partial maxima
+  static constexpr int RED_BYTES = kK2Rows * RED_STRIDE * 4;
   static constexpr int LDS_BYTES = (2 * TILE_BYTES > RED_BYTES) ? 2 * TILE_BYTES : RED_BYTES;
 };
 
+// Byte offset, inside a tile, of LDS chunk slot `pos` of tile row n: the slot
+// holds global chunk pos ^ (n & 15) of that row.
+template <typename T>
+__device__ __forceinline__ int frag_offset(int n, int chunk) {
+  return n * Elem<T>::kRowBytes + ((chunk ^ (n & 15)) << 4);
+}
+
 template <typename T, class P>
-__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_redundancy_kernel(P p, const float* __restrict__ rinv,
-                                                               const float* __restrict__ imp,
-                                                               float* __restrict__ Z,
-                                                               float* __restrict__ Rdbg, float lam) {
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_redundancy_kernel(
+    P p, const float* __restrict__ rinv, const float* __restrict__ imp, float* __restrict__ Z,
+    float* __restrict__ Rdbg, float lam) {
   using C = K2Cfg<T>;
   constexpr int NCH = C::NCH;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
 
   int u, blk;
   if (!p.k2_item(blockIdx.x, u, blk)) return;
+  u = __builtin_amdgcn_readfirstlane(u);
+  blk = __builtin_amdgcn_readfirstlane(blk);
   const int N = p.n(u);
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, half = lane >> 5;
-  const int row0 = blk * kK2Rows + wave * 64;
-  const int blk_last = min(N, (blk + 1) * kK2Rows) - 1;
-  const int ntile = (blk_last + kK2Cols - 1) / kK2Cols;
+  const int lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1;      // row group, column group of this wave
+  const int base = blk * kK2Rows;               // first row (and first column of the diagonal tile)
+  const int row0 = base + wr * 64;
   const bool wave_live = row0 < N;
-  const int wave_last = min(row0 + 63, N - 1);
   const int64_t so = p.score_off(u);
 
+  // Per-lane tile-load offsets (bytes from the tile's first row) and LDS
+  // destinations: wave w fills KiB w*LOADS .. w*LOADS+LOADS-1 of the tile.
+  int trow[C::LOADS], tcol[C::LOADS];
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int kb = wave * C::LOADS + i;
+    trow[i] = kb * C::ROWS_PER_KB + lane / C::RC;
+    tcol[i] = ((lane % C::RC) ^ (trow[i] & 15)) << 4;
+  }
+  auto tile_load = [&](int first_row, int buf, bool clamp) {
+    char* dst = lds + buf * C::TILE_BYTES + wave * C::LOADS * 1024;
+    if constexpr (P::kRowsContiguous) {
+      if (!clamp) {
+        const char* src = reinterpret_cast<const char*>(p.krow(u, first_row));
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i)
+          load16_to_lds(src + trow[i] * C::RB + tcol[i], dst + i * 1024);
+        return;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int r = min(first_row + trow[i], N - 1);
+      load16_to_lds(reinterpret_cast<const char*>(p.krow(u, r)) + tcol[i], dst + i * 1024);
+    }
+  };
+
+  // Fragment read offsets: rows (A) wr*64 + rb*32 + l32, columns (B)
+  // wc*64 + cb*32 + l32, chunk half*NCH + c. Adding 32 to a row leaves
+  // (row & 15) unchanged, so the second 32 rows/columns sit 32*RB further.
+  int aoff[NCH], boff[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    aoff[c] = frag_offset<T>(wr * 64 + l32, half * NCH + c);
+    boff[c] = frag_offset<T>(wc * 64 + l32, half * NCH + c);
+  }
+
+  // 1. the block's own tile -> LDS buffer 0, A fragments from it
+  tile_load(base, 0, true);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   u32x4_t af[2][NCH];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int row = row0 + rb * 32 + (lane & 31);
-    const bool ok = row < N;
-    const char* src = reinterpret_cast<const char*>(p.krow(u, ok ? row : 0)) + half * (NCH * 16);
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) af[rb][c] = ok ? ld16(src + 16 * c) : zero16();
-  }
+    for (int c = 0; c < NCH; ++c) af[rb][c] = ld16(lds + aoff[c] + rb * 32 * C::RB);
+  if (blk > 0) tile_load(0, 1, false);          // prefetch tile 0
 
   float mx[2][16];
 #pragma unroll
@@ -78,100 +135,89 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_redundancy_ker
 #pragma unroll
     for (int v = 0; v < 16; ++v) mx[rb][v] = -INFINITY;
 
-  u32x4_t stage[C::LOADS];
-  auto gload = [&](int J) {
+  auto tile_mma = [&](const char* tb, f32x16_t (&acc)[2][2]) {
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int q = i * 256 + tid;
-      const int n = q / C::RC, c = q % C::RC;
-      const int col = J * kK2Cols + n;
-      stage[i] = col < N ? ld16(reinterpret_cast<const char*>(p.krow(u, col)) + 16 * c) : zero16();
-    }
-  };
-  auto sstore = [&](int buf) {
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int q = i * 256 + tid;
-      const int n = q / C::RC, c = q % C::RC;
-      st16(lds + buf * C::TILE_BYTES + n * C::RB + ((c ^ (n & 15)) << 4), stage[i]);
+      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x16_t{};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const u32x4_t b0 = ld16(tb + boff[c]);
+      const u32x4_t b1 = ld16(tb + boff[c] + 32 * C::RB);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        mma_chunk<T>(acc[rb][0], af[rb][c], b0);
+        mma_chunk<T>(acc[rb][1], af[rb][c], b1);
+      }
     }
   };
 
-  if (ntile > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
-  for (int J = 0; J < ntile; ++J) {
-    if (J + 1 < ntile) gload(J + 1);
-    const int col0 = J * kK2Cols;
-    if (wave_live && wave_last > col0) {
-      const char* tb = lds + (J & 1) * C::TILE_BYTES;
-      float rc[2];
+  // 2. diagonal step (masked): columns base + wc*64 + cb*32 + l32
+  if (wave_live && wc <= wr) {
+    f32x16_t acc[2][2];
+    tile_mma(lds, acc);
+    float rc[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int col = base + wc * 64 + cb * 32 + l32;
+      rc[cb] = col < N ? rinv[so + col] : 0.f;
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        const int col = col0 + cb * 32 + (lane & 31);
-        rc[cb] = col < N ? rinv[so + col] : 0.f;
+        const int j = base + wc * 64 + cb * 32 + l32;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int i = row0 + rb * 32 + acc_row(v, lane);
+          if (j < i) mx[rb][v] = fmaxf(mx[rb][v], acc[rb][cb][v] * rc[cb]);
+        }
       }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // 3. tiles 0..blk-1, wholly left of the diagonal; tile J sits in buffer (J+1)&1
+  const float* rcol = rinv + so + wc * 64 + l32;
+  for (int J = 0; J < blk; ++J) {
+    if (J + 1 < blk) tile_load((J + 1) * kK2Cols, J & 1, false);
+    if (wave_live) {
       f32x16_t acc[2][2];
+      tile_mma(lds + ((J + 1) & 1) * C::TILE_BYTES, acc);
+      const float r0 = rcol[J * kK2Cols], r1 = rcol[J * kK2Cols + 32];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x16_t{};
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        u32x4_t bfr[2];
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          const int n = cb * 32 + (lane & 31);
-          const int cc = half * NCH + c;
-          bfr[cb] = ld16(tb + n * C::RB + ((cc ^ (n & 15)) << 4));
-        }
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb) mma_chunk<T>(acc[rb][cb], af[rb][c], bfr[cb]);
-      }
-      if (col0 + kK2Cols - 1 < row0) {
-        // every column precedes every row of this wave
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            mx[rb][v] = fmaxf(mx[rb][v], fmaxf(acc[rb][0][v] * rc[0], acc[rb][1][v] * rc[1]));
-      } else {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb) {
-            const int j = col0 + cb * 32 + (lane & 31);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int i = row0 + rb * 32 + acc_row(v, lane);
-              if (j < i) mx[rb][v] = fmaxf(mx[rb][v], acc[rb][cb][v] * rc[cb]);
-            }
-          }
-      }
+        for (int v = 0; v < 16; ++v)
+          mx[rb][v] = fmaxf(mx[rb][v], fmaxf(acc[rb][0][v] * r0, acc[rb][1][v] * r1));
     }
-    if (J + 1 < ntile) sstore((J + 1) & 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
-  // Row maxima: lanes of a half hold the same rows for different columns.
+  // 4. row maxima: the 32 lanes of a half and the two column-group waves hold
+  // 64 partial maxima per row; they meet in LDS (row-major, padded rows).
   float* red = reinterpret_cast<float*>(lds);
   if (wave_live) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        red[(lane & 31) * C::RED_STRIDE + wave * 64 + rb * 32 + acc_row(v, lane)] = mx[rb][v];
+        red[(wr * 64 + rb * 32 + acc_row(v, lane)) * C::RED_STRIDE + wc * 32 + l32] = mx[rb][v];
   }
   __syncthreads();
-  const int row = blk * kK2Rows + tid;
-  if (row < N) {
-    float m = -INFINITY;
+  // two threads per row, 32 partials each
+  const int rl = tid >> 1;
+  const float4* pr = reinterpret_cast<const float4*>(red + rl * C::RED_STRIDE + (tid & 1) * 32);
+  float m = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < 32; ++c) m = fmaxf(m, red[c * C::RED_STRIDE + tid]);
+  for (int k = 0; k < 8; ++k) {
+    const float4 q = pr[k];
+    m = fmaxf(m, fmaxf(fmaxf(q.x, q.y), fmaxf(q.z, q.w)));
+  }
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  const int row = base + rl;
+  if ((tid & 1) == 0 && row < N && wave_live) {
     const float R = (row == 0) ? 0.f : m * rinv[so + row];
     const float z = lam * imp[so + row] - (1.0f - lam) * R;
     Z[so + row] = z + 0.0f;   // folds -0 onto +0

@@ -56,6 +56,13 @@ __device__ __forceinline__ u32x4_t zero16() {
   return z;
 }
 
+// 16 bytes per lane from global memory straight into LDS. The 64 lanes of the
+// wave fill 1 KiB of LDS at `lds_dst` in lane order (lane l -> bytes 16l..16l+15);
+// each lane's source address is free. Completion is tracked by vmcnt.
+__device__ __forceinline__ void load16_to_lds(const void* src, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_dst), 16, 0, 0);
+}
+
 // acc += A_chunk * B_chunk over the k-values of one 16-byte chunk per lane.
 template <typename T>
 __device__ __forceinline__ void mma_chunk(f32x16_t& acc, u32x4_t a, u32x4_t b) {

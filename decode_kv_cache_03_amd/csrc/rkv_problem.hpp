@@ -14,11 +14,12 @@
 namespace rkv {
 
 constexpr int kK1Keys = 256;   // keys per importance work item (4 waves x 64)
-constexpr int kK2Rows = 256;   // rows per redundancy work item (4 waves x 64)
-constexpr int kK2Cols = 64;    // columns per LDS tile of the redundancy kernel
+constexpr int kK2Rows = 128;   // rows per redundancy work item (2 row groups of 64)
+constexpr int kK2Cols = 128;   // columns per LDS tile of the redundancy kernel (2 groups of 64)
 
 template <typename T>
 struct DenseProblem {
+  static constexpr bool kRowsContiguous = true;   // rows of a unit are 128 elements apart
   const T* K;
   const T* V;
   const T* Q;              // [units][G][w][128]
@@ -65,6 +66,7 @@ struct DenseProblem {
 
 template <typename T>
 struct PagedProblem {
+  static constexpr bool kRowsContiguous = false;
   const T* Kp;
   const T* Vp;
   const T* Q;                // [S][H][G][w][128]
