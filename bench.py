@@ -51,7 +51,7 @@ def kernel_work(name, units, n, b, g, w, esize=2):
     if name == "rkv_k5_gather":
         nk = min(n, b)
         return "hbm", units * (4 * nk * row + 4 * nk), "byte"
-    if name in ("rkv_k1_stats", "rkv_k1_weights"):
+    if name == "rkv_k1_stats":
         return "hbm", units * (n * row + g * w * row), "byte"
     if name == "rkv_k4_select":
         return "hbm", units * (4 * n + 4 * b), "byte"
@@ -73,8 +73,7 @@ def source_hash(kernel_file):
 
 
 KERNEL_SOURCES = {"rkv_k2_redundancy": "k2_redundancy.hip", "rkv_k5_gather": "k5_compact.hip",
-                  "rkv_k1_stats": "k1_importance.hip", "rkv_k1_weights": "k1_importance.hip",
-                  "rkv_k4_select": "k4_select.hip"}
+                  "rkv_k1_stats": "k1_importance.hip", "rkv_k4_select": "k4_select.hip"}
 
 
 def measured_traffic(kernel, workload):

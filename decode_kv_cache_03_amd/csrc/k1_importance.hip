@@ -9,18 +9,17 @@
 // "Measured effects reported in the paper", last row). Window query r sees
 // candidates j <= N-w+r; logits are q.k/sqrt(128).
 //
-// Three launches per call, each over independent units:
+// This file holds the first two launches; the weights themselves are formed
+// in the redundancy kernel (k2_redundancy.hip), which already holds every key
+// row in registers as MFMA fragments:
 //   k1_stats     per (unit, 256-key chunk): logits on MFMA with the keys as
 //                the A operand, so each lane owns one query column and its
 //                running max / sum of exp stay in registers; also writes
 //                1/||k|| for every key.
-//   k1_combine   per unit: merges the chunks' (max, sum) per query row.
-//   k1_weights   per (unit, chunk): recomputes the logits with the queries
-//                as the A operand, so each lane owns one key and the mean
-//                over queries / max over heads reduce inside the lane (plus
-//                one exchange between the two 32-lane halves).
-// The keys are read twice from memory (statistics, then weights); a query
-// row's normaliser needs every key before any weight can be formed.
+//   k1_combine   per unit: merges the chunks' (max, sum) per query row into
+//                (max, 1/sum).
+// A query row's normaliser needs every key before any weight can be formed,
+// hence the separate statistics pass over the keys.
 //
 // Query rows are laid out in groups of `rpg` rows (8, 16 or 32 >= w) per
 // query head: MFMA row m is query head m / rpg, window query m % rpg; rows
@@ -169,107 +168,37 @@ __global__ __launch_bounds__(128) void k1_combine_kernel(P p, const float* __res
   reinterpret_cast<float2*>(fin)[(int64_t)u * NQB * 32 + t] = out;
 }
 
-template <typename T, int NQB, class P>
-__global__ __launch_bounds__(256) void k1_weights_kernel(P p, const float* __restrict__ fin,
-                                                         float* __restrict__ imp, int rpg_shift) {
-  constexpr int NCH = Elem<T>::kHalfChunks;
-  int u, chunk;
-  if (!p.k1_item(blockIdx.x, u, chunk)) return;
-  const int N = p.n(u);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
-  const int rpg_mask = (1 << rpg_shift) - 1;
-  const int octets_per_group = (1 << rpg_shift) >> 3;
-  const float inv_w = 1.0f / (float)p.W;
-
-  u32x4_t qf[NQB][NCH];
-  load_queries<T, NQB>(qf, p, u, lane, rpg_shift);
-  // normalisers of the lane's 16 query rows per block
-  float Mx[NQB][16], iS[NQB][16];
-  const float2* fp = reinterpret_cast<const float2*>(fin) + (int64_t)u * NQB * 32;
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = qb * 32 + acc_row(v, lane);
-      const float2 e = fp[m];
-      const bool qvalid = (m >> rpg_shift) < p.G && (m & rpg_mask) < p.W;
-      Mx[qb][v] = e.x;
-      iS[qb][v] = qvalid ? e.y : 0.f;
-    }
-
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int kbase = chunk * kK1Keys + wave * 64 + kb * 32;
-    const int key = kbase + (lane & 31);
-    const bool kvalid = key < N;
-    u32x4_t kf[NCH];
-    load_half_row<T>(kf, kvalid ? p.krow(u, key) : p.krow(u, 0), half, kvalid);
-    float best = 0.f;
-    float run = 0.f;
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      f32x16_t acc = {};
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) mma_chunk<T>(acc, qf[qb][c], kf[c]);   // C[query][key]
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        float os = 0.f;   // this lane's 4 rows of octet (qb, t)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int v = 4 * t + j;
-          const int m = qb * 32 + acc_row(v, lane);
-          const int last = N - p.W + (m & rpg_mask);
-          const float pr = fast_exp2(acc[v] * kLogitScaleLog2 - Mx[qb][v]) * iS[qb][v];
-          os += (key <= last) ? pr : 0.f;
-        }
-        os += __shfl_xor(os, 32, 64);   // the octet's other 4 rows
-        run += os;
-        const int o = qb * 4 + t;       // octet index; a group spans octets_per_group
-        if (((o + 1) & (octets_per_group - 1)) == 0) {
-          const int g = o / octets_per_group;
-          if (g < p.G) best = fmaxf(best, run * inv_w);
-          run = 0.f;
-        }
-      }
-    }
-    if (half == 0 && kvalid) imp[p.score_off(u) + key] = best;
-  }
-}
-
 // ---------------------------------------------------------------------------
 template <typename T, int NQB, class P>
 static hipError_t run_k1_t(const P& p, int k1_items, int num_units, float* part, float* fin,
-                           float* rinv, float* imp, int rpg_shift, hipStream_t st) {
+                           float* rinv, int rpg_shift, hipStream_t st) {
   hipError_t e = launch("rkv_k1_stats", k1_stats_kernel<T, NQB, P>, dim3(k1_items), dim3(256), 0, st,
                         p, part, rinv, rpg_shift);
   if (e != hipSuccess) return e;
-  e = launch("rkv_k1_combine", k1_combine_kernel<NQB, P>, dim3(num_units), dim3(128), 0, st, p,
-             (const float*)part, fin, num_units);
-  if (e != hipSuccess) return e;
-  return launch("rkv_k1_weights", k1_weights_kernel<T, NQB, P>, dim3(k1_items), dim3(256), 0, st,
-                p, (const float*)fin, imp, rpg_shift);
+  return launch("rkv_k1_combine", k1_combine_kernel<NQB, P>, dim3(num_units), dim3(128), 0, st, p,
+                (const float*)part, fin, num_units);
 }
 
 template <typename T, class P>
 hipError_t run_k1(const P& p, int nqb, int k1_items, int num_units, float* part, float* fin,
-                  float* rinv, float* imp, int rpg_shift, hipStream_t st) {
+                  float* rinv, int rpg_shift, hipStream_t st) {
   // fp32 inputs are limited to two query blocks on the host (register budget)
   if constexpr (sizeof(T) == 4) {
-    if (nqb == 1) return run_k1_t<T, 1>(p, k1_items, num_units, part, fin, rinv, imp, rpg_shift, st);
-    return run_k1_t<T, 2>(p, k1_items, num_units, part, fin, rinv, imp, rpg_shift, st);
+    if (nqb == 1) return run_k1_t<T, 1>(p, k1_items, num_units, part, fin, rinv, rpg_shift, st);
+    return run_k1_t<T, 2>(p, k1_items, num_units, part, fin, rinv, rpg_shift, st);
   } else {
     switch (nqb) {
-      case 1: return run_k1_t<T, 1>(p, k1_items, num_units, part, fin, rinv, imp, rpg_shift, st);
-      case 2: return run_k1_t<T, 2>(p, k1_items, num_units, part, fin, rinv, imp, rpg_shift, st);
-      case 3: return run_k1_t<T, 3>(p, k1_items, num_units, part, fin, rinv, imp, rpg_shift, st);
-      default: return run_k1_t<T, 4>(p, k1_items, num_units, part, fin, rinv, imp, rpg_shift, st);
+      case 1: return run_k1_t<T, 1>(p, k1_items, num_units, part, fin, rinv, rpg_shift, st);
+      case 2: return run_k1_t<T, 2>(p, k1_items, num_units, part, fin, rinv, rpg_shift, st);
+      case 3: return run_k1_t<T, 3>(p, k1_items, num_units, part, fin, rinv, rpg_shift, st);
+      default: return run_k1_t<T, 4>(p, k1_items, num_units, part, fin, rinv, rpg_shift, st);
     }
   }
 }
 
-template hipError_t run_k1<bf16_bits, DenseProblem<bf16_bits>>(const DenseProblem<bf16_bits>&, int, int, int, float*, float*, float*, float*, int, hipStream_t);
-template hipError_t run_k1<float, DenseProblem<float>>(const DenseProblem<float>&, int, int, int, float*, float*, float*, float*, int, hipStream_t);
-template hipError_t run_k1<bf16_bits, PagedProblem<bf16_bits>>(const PagedProblem<bf16_bits>&, int, int, int, float*, float*, float*, float*, int, hipStream_t);
-template hipError_t run_k1<float, PagedProblem<float>>(const PagedProblem<float>&, int, int, int, float*, float*, float*, float*, int, hipStream_t);
+template hipError_t run_k1<bf16_bits, DenseProblem<bf16_bits>>(const DenseProblem<bf16_bits>&, int, int, int, float*, float*, float*, int, hipStream_t);
+template hipError_t run_k1<float, DenseProblem<float>>(const DenseProblem<float>&, int, int, int, float*, float*, float*, int, hipStream_t);
+template hipError_t run_k1<bf16_bits, PagedProblem<bf16_bits>>(const PagedProblem<bf16_bits>&, int, int, int, float*, float*, float*, int, hipStream_t);
+template hipError_t run_k1<float, PagedProblem<float>>(const PagedProblem<float>&, int, int, int, float*, float*, float*, int, hipStream_t);
 
 }  // namespace rkv

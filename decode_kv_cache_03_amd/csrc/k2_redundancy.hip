@@ -1,4 +1,4 @@
-// Redundancy R and joint score Z.
+// Redundancy R, importance I and joint score Z, one pass over the keys.
 //
 // Pages: redundancy is measured by the cosine similarity of key vectors and
 // serves to find and prune near-duplicates (sourcepulse summary of R-KV,
@@ -31,6 +31,11 @@
 // The remaining tiles 0..blk-1 lie wholly left of the diagonal and run
 // unmasked. ~95% of wave-steps do useful work at N = 1152.
 //
+// After the tile loop the block's key rows, still in registers, are reused
+// for the importance weights (Q x K^T against the softmax normalisers the
+// statistics pass produced), so Z leaves the kernel without a second read of
+// the keys.
+//
 // The MFMA issue rate is the budget, so per-lane addresses are computed once:
 // tiles arrive by direct global->LDS loads from a uniform base plus a fixed
 // per-lane offset, and fragment reads use fixed per-lane LDS offsets.
@@ -48,7 +53,7 @@ struct K2Cfg {
   static constexpr int LOADS = kK2Cols * RB / 1024 / 4;   // KiB of tile per wave
   static constexpr int ROWS_PER_KB = 1024 / RB;
   static constexpr int RED_STRIDE = 68;                   // floats per row of partial maxima
-  static constexpr int RED_BYTES = kK2Rows * RED_STRIDE * 4;
+  static constexpr int RED_BYTES = kK2Rows * RED_STRIDE * 4 + kK2Rows * 4;   // + importance
   static constexpr int LDS_BYTES = (2 * TILE_BYTES > RED_BYTES) ? 2 * TILE_BYTES : RED_BYTES;
 };
 
@@ -59,10 +64,10 @@ __device__ __forceinline__ int frag_offset(int n, int chunk) {
   return n * Elem<T>::kRowBytes + ((chunk ^ (n & 15)) << 4);
 }
 
-template <typename T, class P>
+template <typename T, int NQB, class P>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_redundancy_kernel(
-    P p, const float* __restrict__ rinv, const float* __restrict__ imp, float* __restrict__ Z,
-    float* __restrict__ Rdbg, float lam) {
+    P p, const float* __restrict__ rinv, const float* __restrict__ fin, float* __restrict__ Z,
+    float* __restrict__ Rdbg, float* __restrict__ Idbg, float lam, int rpg_shift) {
   using C = K2Cfg<T>;
   constexpr int NCH = C::NCH;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
@@ -198,6 +203,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_redundancy_ker
   // 4. row maxima: the 32 lanes of a half and the two column-group waves hold
   // 64 partial maxima per row; they meet in LDS (row-major, padded rows).
   float* red = reinterpret_cast<float*>(lds);
+  float* imp_l = red + kK2Rows * C::RED_STRIDE;   // importance of the block's keys
   if (wave_live) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
@@ -205,8 +211,71 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_redundancy_ker
       for (int v = 0; v < 16; ++v)
         red[(wr * 64 + rb * 32 + acc_row(v, lane)) * C::RED_STRIDE + wc * 32 + l32] = mx[rb][v];
   }
+
+  // 5. importance of the block's keys. The key rows are already in registers
+  // as A fragments; used as the B operand of Q x K^T they give one key per
+  // lane and 16 query rows per register set, so the mean over each head's
+  // window queries and the max over the G heads reduce inside the lane plus
+  // one exchange between the 32-lane halves. Query rows come in groups of
+  // 2^rpg_shift (>= w) per head; the normalisers (max, 1/sum) were merged
+  // over all keys beforehand. The two waves of a row group split its two
+  // 32-key halves.
+  if (wave_live) {
+    const int rpg_mask = (1 << rpg_shift) - 1;
+    const int octets_per_group = (1 << rpg_shift) >> 3;
+    const float inv_w = 1.0f / (float)p.W;
+    const int key = row0 + wc * 32 + l32;
+    const T* qrow0 = p.q(u);
+    const float2* fp = reinterpret_cast<const float2*>(fin) + (int64_t)u * NQB * 32;
+    // the key fragments are taken by compile-time index (a runtime index
+    // would move the register array to scratch memory)
+    auto importance_of = [&](const u32x4_t (&kf)[NCH]) -> float {
+      float best = 0.f, run = 0.f;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        u32x4_t qf[NCH];
+        {
+          const int m = qb * 32 + l32;
+          const bool qok = (m >> rpg_shift) < p.G && (m & rpg_mask) < p.W;
+          const char* q = reinterpret_cast<const char*>(
+                              qrow0 + (qok ? (int64_t)((m >> rpg_shift) * p.W + (m & rpg_mask)) * kD : 0)) +
+                          half * (NCH * 16);
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) qf[c] = qok ? ld16(q + 16 * c) : zero16();
+        }
+        f32x16_t acc = {};
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) mma_chunk<T>(acc, qf[c], kf[c]);   // C[query][key]
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          float os = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int v = 4 * t + j;
+            const int m = qb * 32 + acc_row(v, lane);
+            const float2 st = fp[m];
+            const bool vis = (m >> rpg_shift) < p.G && (m & rpg_mask) < p.W &&
+                             key <= N - p.W + (m & rpg_mask);
+            const float pr = fast_exp2(acc[v] * kLogitScaleLog2 - st.x) * st.y;
+            os += vis ? pr : 0.f;
+          }
+          os += __shfl_xor(os, 32, 64);
+          run += os;
+          const int o = qb * 4 + t;
+          if (((o + 1) & (octets_per_group - 1)) == 0) {
+            if (o / octets_per_group < p.G) best = fmaxf(best, run * inv_w);
+            run = 0.f;
+          }
+        }
+      }
+      return best;
+    };
+    const float best = (wc == 0) ? importance_of(af[0]) : importance_of(af[1]);
+    if (half == 0) imp_l[wr * 64 + wc * 32 + l32] = best;
+  }
   __syncthreads();
-  // two threads per row, 32 partials each
+
+  // 6. R, I and Z per row: two threads per row, 32 partial maxima each
   const int rl = tid >> 1;
   const float4* pr = reinterpret_cast<const float4*>(red + rl * C::RED_STRIDE + (tid & 1) * 32);
   float m = -INFINITY;
@@ -217,24 +286,42 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_redundancy_ker
   }
   m = fmaxf(m, __shfl_xor(m, 1, 64));
   const int row = base + rl;
-  if ((tid & 1) == 0 && row < N && wave_live) {
+  if ((tid & 1) == 0 && row < N) {
     const float R = (row == 0) ? 0.f : m * rinv[so + row];
-    const float z = lam * imp[so + row] - (1.0f - lam) * R;
+    const float I = imp_l[rl];
+    const float z = lam * I - (1.0f - lam) * R;
     Z[so + row] = z + 0.0f;   // folds -0 onto +0
     if (Rdbg != nullptr) Rdbg[so + row] = R;
+    if (Idbg != nullptr) Idbg[so + row] = I;
   }
 }
 
-template <typename T, class P>
-hipError_t run_k2(const P& p, int k2_items, const float* rinv, const float* imp, float* Z,
-                  float* dbg_R, float lam, hipStream_t st) {
-  return launch("rkv_k2_redundancy", k2_redundancy_kernel<T, P>, dim3(k2_items), dim3(256), 0, st,
-                p, rinv, imp, Z, dbg_R, lam);
+template <typename T, int NQB, class P>
+static hipError_t run_k2_t(const P& p, int k2_items, const float* rinv, const float* fin, float* Z,
+                           float* dbg_R, float* dbg_I, float lam, int rpg_shift, hipStream_t st) {
+  return launch("rkv_k2_redundancy", k2_redundancy_kernel<T, NQB, P>, dim3(k2_items), dim3(256), 0,
+                st, p, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift);
 }
 
-template hipError_t run_k2<bf16_bits, DenseProblem<bf16_bits>>(const DenseProblem<bf16_bits>&, int, const float*, const float*, float*, float*, float, hipStream_t);
-template hipError_t run_k2<float, DenseProblem<float>>(const DenseProblem<float>&, int, const float*, const float*, float*, float*, float, hipStream_t);
-template hipError_t run_k2<bf16_bits, PagedProblem<bf16_bits>>(const PagedProblem<bf16_bits>&, int, const float*, const float*, float*, float*, float, hipStream_t);
-template hipError_t run_k2<float, PagedProblem<float>>(const PagedProblem<float>&, int, const float*, const float*, float*, float*, float, hipStream_t);
+template <typename T, class P>
+hipError_t run_k2(const P& p, int nqb, int k2_items, const float* rinv, const float* fin, float* Z,
+                  float* dbg_R, float* dbg_I, float lam, int rpg_shift, hipStream_t st) {
+  if constexpr (sizeof(T) == 4) {
+    if (nqb == 1) return run_k2_t<T, 1>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, st);
+    return run_k2_t<T, 2>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, st);
+  } else {
+    switch (nqb) {
+      case 1: return run_k2_t<T, 1>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, st);
+      case 2: return run_k2_t<T, 2>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, st);
+      case 3: return run_k2_t<T, 3>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, st);
+      default: return run_k2_t<T, 4>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, st);
+    }
+  }
+}
+
+template hipError_t run_k2<bf16_bits, DenseProblem<bf16_bits>>(const DenseProblem<bf16_bits>&, int, int, const float*, const float*, float*, float*, float*, float, int, hipStream_t);
+template hipError_t run_k2<float, DenseProblem<float>>(const DenseProblem<float>&, int, int, const float*, const float*, float*, float*, float*, float, int, hipStream_t);
+template hipError_t run_k2<bf16_bits, PagedProblem<bf16_bits>>(const PagedProblem<bf16_bits>&, int, int, const float*, const float*, float*, float*, float*, float, int, hipStream_t);
+template hipError_t run_k2<float, PagedProblem<float>>(const PagedProblem<float>&, int, int, const float*, const float*, float*, float*, float*, float, int, hipStream_t);
 
 }  // namespace rkv

@@ -126,7 +126,6 @@ namespace {
 
 struct DenseLayout {
   float* rinv;
-  float* imp;
   float* z;
   float* part;
   float* fin;
@@ -174,7 +173,6 @@ DenseLayout dense_layout(const rkv_dense_desc* d, char* base) {
   const size_t chunks = (n + rkv::kK1Keys - 1) / rkv::kK1Keys;
   DenseLayout L;
   L.rinv = c.take<float>(units * n);
-  L.imp = c.take<float>(units * n);
   L.z = c.take<float>(units * n);
   L.part = c.take<float>(units * chunks * nqb * 32 * 2);
   L.fin = c.take<float>(units * nqb * 32 * 2);
@@ -208,14 +206,13 @@ int dense_run(const rkv_dense_desc* d, const void* K, const void* V, const void*
   const int nkeep = std::min(d->n_cand, d->budget);
   hipError_t e;
   if (d->n_cand > d->budget) {
-    float* imp = dbg_I ? dbg_I : L.imp;
     float* z = dbg_Z ? dbg_Z : L.z;
     const int rpg_shift = rows_per_group_shift(d->window);
-    e = rkv::run_k1<T>(p, nqb_of(d->gqa_group, d->window), units * p.k1_chunks, units, L.part,
-                       L.fin, L.rinv, imp, rpg_shift, st);
+    const int nqb = nqb_of(d->gqa_group, d->window);
+    e = rkv::run_k1<T>(p, nqb, units * p.k1_chunks, units, L.part, L.fin, L.rinv, rpg_shift, st);
     if (e != hipSuccess) return hip_fail(e, "importance launch");
     const int k2_items = 8 * ((units + 7) / 8) * p.k2_blocks;
-    e = rkv::run_k2<T>(p, k2_items, L.rinv, imp, z, dbg_R, d->mix_lambda, st);
+    e = rkv::run_k2<T>(p, nqb, k2_items, L.rinv, L.fin, z, dbg_R, dbg_I, d->mix_lambda, rpg_shift, st);
     if (e != hipSuccess) return hip_fail(e, "redundancy launch");
     e = rkv::run_k4(p, units, z, kept, 1, st);
     if (e != hipSuccess) return hip_fail(e, "select launch");
@@ -375,7 +372,6 @@ struct PagedLayout {
   int2* k1_list;
   int2* k2_list;
   float* rinv;
-  float* imp;
   float* z;
   float* part;
   float* fin;
@@ -398,7 +394,6 @@ PagedLayout paged_layout(const rkv_paged_desc* d, const PagedPlan& P, char* base
   L.k2_list = c.take<int2>(P.k2_list.size());
   L.meta_bytes = c.used;
   L.rinv = c.take<float>(P.total_scores);
-  L.imp = c.take<float>(P.total_scores);
   L.z = c.take<float>(P.total_scores);
   L.part = c.take<float>((size_t)P.total_chunks * P.nqb * 32 * 2);
   L.fin = c.take<float>(U * P.nqb * 32 * 2);
@@ -456,10 +451,11 @@ int paged_run(const rkv_paged_desc* d, void* Kp, void* Vp, int32_t* page_table, 
   float* z = dbg_Z ? dbg_Z : L.z;
   hipError_t e;
   if (p.unit_count > 0) {
-    e = rkv::run_k1<T>(p, P.nqb, p.k1_count, p.all_units, L.part, L.fin, L.rinv, L.imp,
-                       rows_per_group_shift(d->window), st);
+    const int rpg_shift = rows_per_group_shift(d->window);
+    e = rkv::run_k1<T>(p, P.nqb, p.k1_count, p.all_units, L.part, L.fin, L.rinv, rpg_shift, st);
     if (e != hipSuccess) return hip_fail(e, "importance launch");
-    e = rkv::run_k2<T>(p, p.k2_count, L.rinv, L.imp, z, nullptr, d->mix_lambda, st);
+    e = rkv::run_k2<T>(p, P.nqb, p.k2_count, L.rinv, L.fin, z, nullptr, nullptr, d->mix_lambda,
+                       rpg_shift, st);
     if (e != hipSuccess) return hip_fail(e, "redundancy launch");
   }
   e = rkv::run_k4(p, p.all_units, z, kept, 0, st);

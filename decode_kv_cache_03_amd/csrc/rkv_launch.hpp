@@ -25,15 +25,16 @@ hipError_t launch(const char* name, void (*kern)(KArgs...), dim3 grid, dim3 bloc
   return e;
 }
 
-// Importance: rinv [units][N], I [units][N]; part/fin are statistics scratch.
+// Softmax statistics of the window queries: rinv [units][N] and, per unit and
+// query row, (max, 1/sum) in fin; part is per-chunk scratch.
 template <typename T, class P>
 hipError_t run_k1(const P& p, int nqb, int k1_items, int num_units, float* part, float* fin,
-                  float* rinv, float* imp, int rpg_shift, hipStream_t st);
+                  float* rinv, int rpg_shift, hipStream_t st);
 
-// Redundancy and joint score: Z [units][N] (and R when dbg_R != nullptr).
+// Redundancy, importance and joint score: Z [units][N] (R, I when requested).
 template <typename T, class P>
-hipError_t run_k2(const P& p, int k2_items, const float* rinv, const float* imp, float* Z,
-                  float* dbg_R, float lam, hipStream_t st);
+hipError_t run_k2(const P& p, int nqb, int k2_items, const float* rinv, const float* fin, float* Z,
+                  float* dbg_R, float* dbg_I, float lam, int rpg_shift, hipStream_t st);
 
 // Selection: kept indices per unit (ascending), from Z.
 template <class P>
