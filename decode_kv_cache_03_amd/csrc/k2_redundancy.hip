@@ -8,8 +8,10 @@
 // compression for reasoning models", hysenlabs page, "How this differs from
 // attention-sink and heavy-hitter eviction"). Reading used here:
 // R_i = max over earlier candidates j < i of cos(k_i, k_j), R_0 = 0.
-// The joint score is Z = lambda*I - (1-lambda)*R (atlas.scime.ai summary,
-// "Approach").
+// Importance is the window queries' softmax attention, mean over a head's
+// queries, max over the GQA group (atlas.scime.ai summary, "Approach" and
+// "Measured effects reported in the paper"). The joint score is
+// Z = lambda*I - (1-lambda)*R (same summary, "Approach").
 //
 // The cosine matrix is the one dense contraction of the step (N x N x 128
 // per unit), so it runs on bf16 MFMA with fp32 accumulation on the raw keys
@@ -18,23 +20,31 @@
 // Nothing N x N is ever stored: each lane keeps running row maxima in
 // registers.
 //
-// Work item = (unit, block of 128 rows); column tiles of 128 keys are staged
+// Work item = (unit, block of 128 rows). Column tiles of 128 keys are staged
 // in LDS (double-buffered, XOR-swizzled 16-byte chunks so fragment reads hit
 // distinct banks). The 4 waves form a 2x2 grid over each 128x128 step: wave
 // (r, c) holds rows 64r..64r+63 of the block as MFMA A fragments in registers
-// for the whole item and multiplies them by columns 64c..64c+63 of the tile,
-// as 2x2 tiles of 32x32x16 per k-step.
+// and multiplies them by columns 64c..64c+63 of the tile, as 2x2 tiles of
+// 32x32x16 per k-step. The block's own (diagonal) tile comes first: it
+// supplies the A fragments and is the only step that needs the j < i mask.
+// Tiles 0..blk-1 lie wholly left of the diagonal and run unmasked.
 //
-// The block's own tile (the diagonal one) is loaded first: it supplies the A
-// fragments (read from LDS, so the rows are fetched once) and is the only
-// step that needs the j < i mask; the wave above the diagonal idles on it.
-// The remaining tiles 0..blk-1 lie wholly left of the diagonal and run
-// unmasked. ~95% of wave-steps do useful work at N = 1152.
+// The grid is persistent: about two workgroups per CU walk the work items,
+// workgroup w taking items w, w+G, w+2G, ... (G = grid size, a multiple of
+// 8, so every item a workgroup takes maps to its own XCD, where all blocks of
+// a unit are scheduled together and share the unit's keys in that XCD's L2).
+// The tile stream never stops between items: during an item's last step the
+// next item's diagonal tile and query rows are already being loaded, so the
+// per-item start-up latency is hidden.
 //
-// After the tile loop the block's key rows, still in registers, are reused
-// for the importance weights (Q x K^T against the softmax normalisers the
-// statistics pass produced), so Z leaves the kernel without a second read of
-// the keys.
+// Per item, after the A fragments are read, the block's keys are scored for
+// importance: with the key rows as the B operand of Q x K^T each lane holds
+// one key and 16 query rows, so the mean over a head's window queries and the
+// max over heads reduce inside the lane (plus one exchange between the
+// 32-lane halves), against the softmax normalisers merged beforehand.
+// At the end of the item the row maxima are reduced across lanes by a
+// butterfly that halves the values per lane at each exchange, so no large
+// LDS buffer competes with the tile buffers.
 //
 // The MFMA issue rate is the budget, so per-lane addresses are computed once:
 // tiles arrive by direct global->LDS loads from a uniform base plus a fixed
@@ -52,95 +62,122 @@ struct K2Cfg {
   static constexpr int TILE_BYTES = kK2Cols * RB;
   static constexpr int LOADS = kK2Cols * RB / 1024 / 4;   // KiB of tile per wave
   static constexpr int ROWS_PER_KB = 1024 / RB;
-  static constexpr int RED_STRIDE = 68;                   // floats per row of partial maxima
-  static constexpr int RED_BYTES = kK2Rows * RED_STRIDE * 4 + kK2Rows * 4;   // + importance
-  static constexpr int LDS_BYTES = (2 * TILE_BYTES > RED_BYTES) ? 2 * TILE_BYTES : RED_BYTES;
 };
 
-// Byte offset, inside a tile, of LDS chunk slot `pos` of tile row n: the slot
-// holds global chunk pos ^ (n & 15) of that row.
+// Byte offset, inside a tile, of the slot holding chunk `chunk` of tile row n:
+// the slot at position pos holds global chunk pos ^ (n & 15) of the row.
 template <typename T>
 __device__ __forceinline__ int frag_offset(int n, int chunk) {
   return n * Elem<T>::kRowBytes + ((chunk ^ (n & 15)) << 4);
 }
 
+// One butterfly exchange of the row-max reduction: lanes whose bit W is set
+// keep values W..2W-1 of the current range, the others keep 0..W-1; each
+// receives the half it keeps from the partner lane l ^ W.
+template <int W>
+__device__ __forceinline__ void max_butterfly_step(float (&val)[32], int lane) {
+  const bool upper = (lane & W) != 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    const float keep = upper ? val[i + W] : val[i];
+    const float send = upper ? val[i] : val[i + W];
+    val[i] = fmaxf(keep, __shfl_xor(send, W, 64));
+  }
+}
+
 template <typename T, int NQB, class P>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_redundancy_kernel(
-    P p, const float* __restrict__ rinv, const float* __restrict__ fin, float* __restrict__ Z,
-    float* __restrict__ Rdbg, float* __restrict__ Idbg, float lam, int rpg_shift) {
+    P p, int total_items, const float* __restrict__ rinv, const float* __restrict__ fin,
+    float* __restrict__ Z, float* __restrict__ Rdbg, float* __restrict__ Idbg, float lam,
+    int rpg_shift) {
   using C = K2Cfg<T>;
   constexpr int NCH = C::NCH;
-  __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int gw = p.G * p.W;
+  const K2Lds plan = k2_lds_plan(C::RB, gw, NQB);
+  char* const tiles = lds + plan.tiles;
+  char* const qlds = lds + plan.q;
+  float2* const slds = reinterpret_cast<float2*>(lds + plan.stats);
+  float* const imp_l = reinterpret_cast<float*>(lds + plan.imp);
+  float* const comb = reinterpret_cast<float*>(lds + plan.comb);
 
-  int u, blk;
-  if (!p.k2_item(blockIdx.x, u, blk)) return;
-  u = __builtin_amdgcn_readfirstlane(u);
-  blk = __builtin_amdgcn_readfirstlane(blk);
-  const int N = p.n(u);
   const int tid = threadIdx.x;
   const int lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;      // row group, column group of this wave
-  const int base = blk * kK2Rows;               // first row (and first column of the diagonal tile)
-  const int row0 = base + wr * 64;
-  const bool wave_live = row0 < N;
-  const int64_t so = p.score_off(u);
+  const int stride = gridDim.x;
+  const int rpg_mask = (1 << rpg_shift) - 1;
+  const int octets_per_group = (1 << rpg_shift) >> 3;
+  const float inv_w = 1.0f / (float)p.W;
 
-  // Per-lane tile-load offsets (bytes from the tile's first row) and LDS
-  // destinations: wave w fills KiB w*LOADS .. w*LOADS+LOADS-1 of the tile.
-  int trow[C::LOADS], tcol[C::LOADS];
+  // next valid work item at or after k (in steps of the grid size)
+  auto next_item = [&](int k, int& u, int& blk) -> int {
+    for (; k < total_items; k += stride)
+      if (p.k2_item(k, u, blk)) {
+        u = __builtin_amdgcn_readfirstlane(u);
+        blk = __builtin_amdgcn_readfirstlane(blk);
+        return k;
+      }
+    return total_items;
+  };
+
+  // Per-lane tile-load offsets. Wave w fills KiB w*LOADS + i of a tile; lane
+  // l of load i writes row ROWS_PER_KB*i + l/RC of the wave's rows at slot
+  // l % RC, fetching chunk slot ^ (row & 15). Row & 15 repeats every
+  // 16/ROWS_PER_KB loads, so a few offsets cover them all.
+  constexpr int PER = 16 / C::ROWS_PER_KB;
+  int lofs[PER];
 #pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) {
-    const int kb = wave * C::LOADS + i;
-    trow[i] = kb * C::ROWS_PER_KB + lane / C::RC;
-    tcol[i] = ((lane % C::RC) ^ (trow[i] & 15)) << 4;
+  for (int q = 0; q < PER; ++q) {
+    const int r16 = (q * C::ROWS_PER_KB + lane / C::RC) & 15;   // (tile row) & 15 for load i = q mod PER
+    lofs[q] = (lane / C::RC) * C::RB + (((lane % C::RC) ^ r16) << 4);
   }
-  auto tile_load = [&](int first_row, int buf, bool clamp) {
-    char* dst = lds + buf * C::TILE_BYTES + wave * C::LOADS * 1024;
+  // Rows first_row.. of unit u into tile buffer buf; rows past the unit
+  // (only in a diagonal tile) repeat its last row.
+  auto tile_load = [&](int u, int n_u, int first_row, int buf, bool clamp) {
+    char* dst = tiles + buf * C::TILE_BYTES + wave * C::LOADS * 1024;
+    const int wrow = first_row + wave * C::LOADS * C::ROWS_PER_KB;   // first row this wave loads
     if constexpr (P::kRowsContiguous) {
       if (!clamp) {
-        const char* src = reinterpret_cast<const char*>(p.krow(u, first_row));
+        const char* src = reinterpret_cast<const char*>(p.krow(u, wrow));
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i)
-          load16_to_lds(src + trow[i] * C::RB + tcol[i], dst + i * 1024);
+          load16_to_lds(src + i * 1024 + lofs[i % PER], dst + i * 1024);
         return;
       }
     }
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int r = min(first_row + trow[i], N - 1);
-      load16_to_lds(reinterpret_cast<const char*>(p.krow(u, r)) + tcol[i], dst + i * 1024);
+      const int r = min(wrow + i * C::ROWS_PER_KB + lane / C::RC, n_u - 1);
+      const int chunk_ofs = lofs[i % PER] - (lane / C::RC) * C::RB;
+      load16_to_lds(reinterpret_cast<const char*>(p.krow(u, r)) + chunk_ofs, dst + i * 1024);
     }
+  };
+  // The unit's window queries (G*w rows, swizzled) and softmax normalisers.
+  auto q_load = [&](int u) {
+    const char* q = reinterpret_cast<const char*>(p.q(u));
+    const int qkb = (gw * C::RB + 1023) / 1024;
+    for (int kb = wave; kb < qkb; kb += 4) {
+      const int n = kb * C::ROWS_PER_KB + lane / C::RC;
+      const int c = (lane % C::RC) ^ (n & 15);
+      const int nn = min(n, gw - 1);
+      load16_to_lds(q + nn * C::RB + c * 16, qlds + kb * 1024);
+    }
+    if (wave == 0 && lane < NQB * 16)
+      load16_to_lds(reinterpret_cast<const char*>(fin) + ((int64_t)u * NQB * 32 + 2 * lane) * 8,
+                    reinterpret_cast<char*>(slds));
   };
 
   // Fragment read offsets: rows (A) wr*64 + rb*32 + l32, columns (B)
   // wc*64 + cb*32 + l32, chunk half*NCH + c. Adding 32 to a row leaves
   // (row & 15) unchanged, so the second 32 rows/columns sit 32*RB further.
-  int aoff[NCH], boff[NCH];
+  int boff[NCH];
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    aoff[c] = frag_offset<T>(wr * 64 + l32, half * NCH + c);
-    boff[c] = frag_offset<T>(wc * 64 + l32, half * NCH + c);
-  }
+  for (int c = 0; c < NCH; ++c) boff[c] = frag_offset<T>(wc * 64 + l32, half * NCH + c);
+  // rows and columns differ by a multiple of 64 rows, which keeps row & 15
+  const int a_minus_b = (wr - wc) * 64 * C::RB;
 
-  // 1. the block's own tile -> LDS buffer 0, A fragments from it
-  tile_load(base, 0, true);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  u32x4_t af[2][NCH];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) af[rb][c] = ld16(lds + aoff[c] + rb * 32 * C::RB);
-  if (blk > 0) tile_load(0, 1, false);          // prefetch tile 0
-
-  float mx[2][16];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) mx[rb][v] = -INFINITY;
-
-  auto tile_mma = [&](const char* tb, f32x16_t (&acc)[2][2]) {
+  auto tile_mma = [&](const char* tb, const u32x4_t (&af)[2][NCH], f32x16_t (&acc)[2][2]) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -157,150 +194,223 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_redundancy_ker
     }
   };
 
-  // 2. diagonal step (masked): columns base + wc*64 + cb*32 + l32
-  if (wave_live && wc <= wr) {
-    f32x16_t acc[2][2];
-    tile_mma(lds, acc);
-    float rc[2];
+  // Importance of one 32-key half of the wave's rows (key = row of kf).
+  // Padding query rows (r >= w or g >= G) have zero queries and zero 1/sum,
+  // so they add nothing; only keys among the last w need the causal test.
+  auto importance_of = [&](const u32x4_t (&kf)[NCH], int key, int n_u, bool causal) -> float {
+    float best = 0.f, run = 0.f;
+    int lane_v = lane;   // re-materialised per item: keeps per-lane masks out of the loop preheader
+    asm volatile("" : "+v"(lane_v));
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int col = base + wc * 64 + cb * 32 + l32;
-      rc[cb] = col < N ? rinv[so + col] : 0.f;
+    for (int qb = 0; qb < NQB; ++qb) {
+      u32x4_t qf[NCH];
+      {
+        const int m = qb * 32 + (lane_v & 31);
+        const int g = m >> rpg_shift, r = m & rpg_mask;
+        const bool qok = g < p.G && r < p.W;
+        const int n = qok ? g * p.W + r : 0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+          qf[c] = qok ? ld16(qlds + frag_offset<T>(n, half * NCH + c)) : zero16();
+      }
+      f32x16_t acc = {};
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) mma_chunk<T>(acc, qf[c], kf[c]);   // C[query][key]
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float os = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int v = 4 * t + j;
+          const int m = qb * 32 + acc_row(v, lane_v);
+          const float2 st = slds[m];
+          const float pr = fast_exp2(acc[v] * kLogitScaleLog2 - st.x) * st.y;
+          const float vis = (!causal || key <= n_u - p.W + (m & rpg_mask)) ? 1.f : 0.f;
+          os = fmaf(pr, vis, os);   // arithmetic, not a branch around the exp
+        }
+        os += __shfl_xor(os, 32, 64);
+        run += os;
+        const int o = qb * 4 + t;
+        if (((o + 1) & (octets_per_group - 1)) == 0) {
+          if (o / octets_per_group < p.G) best = fmaxf(best, run * inv_w);
+          run = 0.f;
+        }
+      }
     }
+    return best;
+  };
+
+  int u, blk;
+  int k = next_item(blockIdx.x, u, blk);
+  if (k >= total_items) return;
+  int N = p.n(u);
+  tile_load(u, N, blk * kK2Rows, 0, true);
+  q_load(u);
+  int cur = 0;   // buffer holding the current tile
+
+  while (true) {
+    const int base = blk * kK2Rows;
+    const int row0 = base + wr * 64;
+    const bool wave_live = row0 < N;
+    const int64_t so = p.score_off(u);
+    int un = 0, bn = 0;
+    const int kn = next_item(k + stride, un, bn);
+    const bool has_next = kn < total_items;
+    const int Nn = has_next ? p.n(un) : 0;
+
+    // 1. the diagonal tile (and this unit's queries) have landed
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    u32x4_t af[2][NCH];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int j = base + wc * 64 + cb * 32 + l32;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int i = row0 + rb * 32 + acc_row(v, lane);
-          if (j < i) mx[rb][v] = fmaxf(mx[rb][v], acc[rb][cb][v] * rc[cb]);
-        }
-      }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+      for (int c = 0; c < NCH; ++c)
+        af[rb][c] = ld16(tiles + cur * C::TILE_BYTES + boff[c] + a_minus_b + rb * 32 * C::RB);
 
-  // 3. tiles 0..blk-1, wholly left of the diagonal; tile J sits in buffer (J+1)&1
-  const float* rcol = rinv + so + wc * 64 + l32;
-  for (int J = 0; J < blk; ++J) {
-    if (J + 1 < blk) tile_load((J + 1) * kK2Cols, J & 1, false);
+    // 2. importance of the block's keys; wave (r, c) takes keys r*64 + c*32 + l32
     if (wave_live) {
+      const int key = row0 + wc * 32 + l32;
+      const bool causal = base + kK2Rows > N - p.W;   // block reaches the window's keys
+      const float best = (wc == 0) ? importance_of(af[0], key, N, causal)
+                                   : importance_of(af[1], key, N, causal);
+      if (half == 0) imp_l[wr * 64 + wc * 32 + l32] = best;
+    }
+    __syncthreads();   // queries are no longer read: the prefetch below may replace them
+
+    // 3. prefetch: tile 0 of this block, or the next item's diagonal tile
+    if (blk > 0) {
+      tile_load(u, N, 0, cur ^ 1, false);
+    } else if (has_next) {
+      tile_load(un, Nn, bn * kK2Rows, cur ^ 1, true);
+      q_load(un);
+    }
+
+    float mx[2][16];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx[rb][v] = -INFINITY;
+
+    // 4. diagonal step: wave (0,1) lies above the diagonal, (1,0) below it;
+    // (0,0) and (1,1) straddle it and mask per element (j < i)
+    if (wave_live && wc <= wr) {
       f32x16_t acc[2][2];
-      tile_mma(lds + ((J + 1) & 1) * C::TILE_BYTES, acc);
-      const float r0 = rcol[J * kK2Cols], r1 = rcol[J * kK2Cols + 32];
+      tile_mma(tiles + cur * C::TILE_BYTES, af, acc);
+      float rc[2];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int cb = 0; cb < 2; ++cb) {
+        const int col = base + wc * 64 + cb * 32 + l32;
+        rc[cb] = col < N ? rinv[so + col] : 0.f;
+      }
+      if (wc < wr) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          mx[rb][v] = fmaxf(mx[rb][v], fmaxf(acc[rb][0][v] * r0, acc[rb][1][v] * r1));
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            mx[rb][v] = fmaxf(mx[rb][v], fmaxf(acc[rb][0][v] * rc[0], acc[rb][1][v] * rc[1]));
+      } else {
+        // rows and columns are the same 64 keys: row rb*32 + a follows column
+        // cb*32 + b iff rb > cb, or rb == cb and a > b
+        int lane_v = lane;   // re-materialised per item (see importance_of)
+        asm volatile("" : "+v"(lane_v));
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int cb = 0; cb <= rb; ++cb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const bool ok = (rb > cb) || (acc_row(v, lane_v) > (lane_v & 31));
+              if (ok) mx[rb][v] = fmaxf(mx[rb][v], acc[rb][cb][v] * rc[cb]);
+            }
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  }
+    cur ^= 1;
 
-  // 4. row maxima: the 32 lanes of a half and the two column-group waves hold
-  // 64 partial maxima per row; they meet in LDS (row-major, padded rows).
-  float* red = reinterpret_cast<float*>(lds);
-  float* imp_l = red + kK2Rows * C::RED_STRIDE;   // importance of the block's keys
-  if (wave_live) {
+    // 5. tiles 0..blk-1, wholly left of the diagonal; tile J is in buffer cur
+    const float* rcol = rinv + so + wc * 64 + l32;
+    for (int J = 0; J < blk; ++J) {
+      if (J + 1 < blk) {
+        tile_load(u, N, (J + 1) * kK2Cols, cur ^ 1, false);
+      } else if (has_next) {
+        tile_load(un, Nn, bn * kK2Rows, cur ^ 1, true);
+        q_load(un);
+      }
+      if (wave_live) {
+        f32x16_t acc[2][2];
+        tile_mma(tiles + cur * C::TILE_BYTES, af, acc);
+        const float r0 = rcol[J * kK2Cols], r1 = rcol[J * kK2Cols + 32];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            mx[rb][v] = fmaxf(mx[rb][v], fmaxf(acc[rb][0][v] * r0, acc[rb][1][v] * r1));
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      cur ^= 1;
+    }
+
+    // 6. row maxima. Value j = rb*16 + v of a lane belongs to row
+    // rb*32 + acc_row(v, lane); the 32 lanes of a half share rows. A butterfly
+    // over lane bits 4..0 keeps half of the remaining values at each exchange,
+    // so lane l ends with the max over its half for value j = l & 31.
+    float val[32];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        red[(wr * 64 + rb * 32 + acc_row(v, lane)) * C::RED_STRIDE + wc * 32 + l32] = mx[rb][v];
-  }
+      for (int v = 0; v < 16; ++v) val[rb * 16 + v] = mx[rb][v];
+    max_butterfly_step<16>(val, lane);
+    max_butterfly_step<8>(val, lane);
+    max_butterfly_step<4>(val, lane);
+    max_butterfly_step<2>(val, lane);
+    max_butterfly_step<1>(val, lane);
+    if (wave_live) {
+      const int rl = wr * 64 + (l32 >> 4) * 32 + acc_row(l32 & 15, lane);   // row within the block
+      comb[wc * kK2Rows + rl] = val[0];
+    }
+    __syncthreads();
 
-  // 5. importance of the block's keys. The key rows are already in registers
-  // as A fragments; used as the B operand of Q x K^T they give one key per
-  // lane and 16 query rows per register set, so the mean over each head's
-  // window queries and the max over the G heads reduce inside the lane plus
-  // one exchange between the 32-lane halves. Query rows come in groups of
-  // 2^rpg_shift (>= w) per head; the normalisers (max, 1/sum) were merged
-  // over all keys beforehand. The two waves of a row group split its two
-  // 32-key halves.
-  if (wave_live) {
-    const int rpg_mask = (1 << rpg_shift) - 1;
-    const int octets_per_group = (1 << rpg_shift) >> 3;
-    const float inv_w = 1.0f / (float)p.W;
-    const int key = row0 + wc * 32 + l32;
-    const T* qrow0 = p.q(u);
-    const float2* fp = reinterpret_cast<const float2*>(fin) + (int64_t)u * NQB * 32;
-    // the key fragments are taken by compile-time index (a runtime index
-    // would move the register array to scratch memory)
-    auto importance_of = [&](const u32x4_t (&kf)[NCH]) -> float {
-      float best = 0.f, run = 0.f;
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        u32x4_t qf[NCH];
-        {
-          const int m = qb * 32 + l32;
-          const bool qok = (m >> rpg_shift) < p.G && (m & rpg_mask) < p.W;
-          const char* q = reinterpret_cast<const char*>(
-                              qrow0 + (qok ? (int64_t)((m >> rpg_shift) * p.W + (m & rpg_mask)) * kD : 0)) +
-                          half * (NCH * 16);
-#pragma unroll
-          for (int c = 0; c < NCH; ++c) qf[c] = qok ? ld16(q + 16 * c) : zero16();
-        }
-        f32x16_t acc = {};
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) mma_chunk<T>(acc, qf[c], kf[c]);   // C[query][key]
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          float os = 0.f;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int v = 4 * t + j;
-            const int m = qb * 32 + acc_row(v, lane);
-            const float2 st = fp[m];
-            const bool vis = (m >> rpg_shift) < p.G && (m & rpg_mask) < p.W &&
-                             key <= N - p.W + (m & rpg_mask);
-            const float pr = fast_exp2(acc[v] * kLogitScaleLog2 - st.x) * st.y;
-            os += vis ? pr : 0.f;
-          }
-          os += __shfl_xor(os, 32, 64);
-          run += os;
-          const int o = qb * 4 + t;
-          if (((o + 1) & (octets_per_group - 1)) == 0) {
-            if (o / octets_per_group < p.G) best = fmaxf(best, run * inv_w);
-            run = 0.f;
-          }
-        }
+    // 7. R, I and Z for the block's rows
+    if (tid < kK2Rows) {
+      const int row = base + tid;
+      if (row < N) {
+        const float m = fmaxf(comb[tid], comb[kK2Rows + tid]);
+        const float R = (row == 0) ? 0.f : m * rinv[so + row];
+        const float I = imp_l[tid];
+        const float z = lam * I - (1.0f - lam) * R;
+        Z[so + row] = z + 0.0f;   // folds -0 onto +0
+        if (Rdbg != nullptr) Rdbg[so + row] = R;
+        if (Idbg != nullptr) Idbg[so + row] = I;
       }
-      return best;
-    };
-    const float best = (wc == 0) ? importance_of(af[0]) : importance_of(af[1]);
-    if (half == 0) imp_l[wr * 64 + wc * 32 + l32] = best;
-  }
-  __syncthreads();
+    }
 
-  // 6. R, I and Z per row: two threads per row, 32 partial maxima each
-  const int rl = tid >> 1;
-  const float4* pr = reinterpret_cast<const float4*>(red + rl * C::RED_STRIDE + (tid & 1) * 32);
-  float m = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float4 q = pr[k];
-    m = fmaxf(m, fmaxf(fmaxf(q.x, q.y), fmaxf(q.z, q.w)));
-  }
-  m = fmaxf(m, __shfl_xor(m, 1, 64));
-  const int row = base + rl;
-  if ((tid & 1) == 0 && row < N) {
-    const float R = (row == 0) ? 0.f : m * rinv[so + row];
-    const float I = imp_l[rl];
-    const float z = lam * I - (1.0f - lam) * R;
-    Z[so + row] = z + 0.0f;   // folds -0 onto +0
-    if (Rdbg != nullptr) Rdbg[so + row] = R;
-    if (Idbg != nullptr) Idbg[so + row] = I;
+    if (!has_next) break;
+    k = kn;
+    u = un;
+    blk = bn;
+    N = Nn;
   }
 }
 
 template <typename T, int NQB, class P>
 static hipError_t run_k2_t(const P& p, int k2_items, const float* rinv, const float* fin, float* Z,
                            float* dbg_R, float* dbg_I, float lam, int rpg_shift, hipStream_t st) {
-  return launch("rkv_k2_redundancy", k2_redundancy_kernel<T, NQB, P>, dim3(k2_items), dim3(256), 0,
-                st, p, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift);
+  const K2Lds plan = k2_lds_plan(Elem<T>::kRowBytes, p.G * p.W, NQB);
+  auto kern = k2_redundancy_kernel<T, NQB, P>;
+  const void* fn = reinterpret_cast<const void*>(kern);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, plan.total);
+  int dev = 0, cus = 0, per_cu = 0;
+  if (e == hipSuccess) e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, plan.total);
+  if (e != hipSuccess) return e;
+  int grid = 8 * ((max(1, per_cu) * cus + 7) / 8);
+  grid = min(grid, 8 * ((k2_items + 7) / 8));
+  return launch("rkv_k2_redundancy", kern, dim3(grid), dim3(256), plan.total, st, p, k2_items, rinv,
+                fin, Z, dbg_R, dbg_I, lam, rpg_shift);
 }
 
 template <typename T, class P>

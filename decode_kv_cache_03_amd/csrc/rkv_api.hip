@@ -145,6 +145,11 @@ int check_common(int head_dim, int gqa, int window, float lam, int dtype) {
     return fail(RKV_EUNSUPPORTED,
                 "gqa_group * window rounded up to 8/16/32 per head must be <= %d (got %d)",
                 max_rows, rows);
+  const rkv::K2Lds plan = rkv::k2_lds_plan(dtype == RKV_BF16 ? 256 : 512, gqa * window, (rows + 31) / 32);
+  if (plan.total > rkv::kLdsBytesPerCU)
+    return fail(RKV_EUNSUPPORTED,
+                "gqa_group * window = %d needs %d bytes of LDS for the %s kernels (limit %d)",
+                gqa * window, plan.total, dtype == RKV_BF16 ? "bf16" : "fp32", rkv::kLdsBytesPerCU);
   return RKV_OK;
 }
 

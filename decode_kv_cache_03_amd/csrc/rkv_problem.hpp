@@ -17,6 +17,31 @@ constexpr int kK1Keys = 256;   // keys per importance work item (4 waves x 64)
 constexpr int kK2Rows = 128;   // rows per redundancy work item (2 row groups of 64)
 constexpr int kK2Cols = 128;   // columns per LDS tile of the redundancy kernel (2 groups of 64)
 
+// LDS plan of the redundancy kernel (bytes from the start of its dynamic
+// shared memory); the host checks it against the 160 KiB of a CU.
+struct K2Lds {
+  int tiles;     // 2 tile buffers
+  int q;         // window queries of the current unit, G*w rows, swizzled like tiles
+  int stats;     // (max, 1/sum) per query row, NQB*32 float2
+  int imp;       // importance of the block's 128 keys
+  int comb;      // row maxima of the two column-group waves: [2][128] floats
+  int total;
+};
+
+__host__ __device__ inline K2Lds k2_lds_plan(int row_bytes, int gw, int nqb) {
+  K2Lds L;
+  L.tiles = 0;
+  L.q = 2 * kK2Cols * row_bytes;
+  const int qkb = (gw * row_bytes + 1023) / 1024;          // whole KiB per direct load
+  L.stats = L.q + qkb * 1024;
+  L.imp = L.stats + nqb * 32 * 8;
+  L.comb = L.imp + kK2Rows * 4;
+  L.total = L.comb + 2 * kK2Rows * 4;
+  return L;
+}
+
+constexpr int kLdsBytesPerCU = 160 * 1024;
+
 template <typename T>
 struct DenseProblem {
   static constexpr bool kRowsContiguous = true;   // rows of a unit are 128 elements apart

@@ -74,7 +74,11 @@ def test_dense_desc_errors(lib, field, value, code):
 def test_fp32_query_rows_limit(lib):
     d = dense(dtype=_lib.RKV_F32, gqa_group=16)
     assert call_dense(lib, d) == _lib.RKV_EUNSUPPORTED
-    d = dense(dtype=_lib.RKV_F32, gqa_group=8)
+    d = dense(dtype=_lib.RKV_F32, gqa_group=8)     # queries and fp32 tiles exceed the LDS
+    assert call_dense(lib, d) == _lib.RKV_EUNSUPPORTED
+    d = dense(dtype=_lib.RKV_F32, gqa_group=6)
+    assert lib.rkv_workspace_size(ctypes.byref(d)) > 0
+    d = dense(dtype=_lib.RKV_BF16, gqa_group=16)    # bf16 tiles leave room for 128 query rows
     assert lib.rkv_workspace_size(ctypes.byref(d)) > 0
 
 

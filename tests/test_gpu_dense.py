@@ -72,7 +72,7 @@ SHAPES = [
     (200, 150, 8, 2, 1.0, "bf16", 2),      # importance only
     (1153, 1152, 8, 4, 0.1, "bf16", 2),    # N = B + 1
     (300, 200, 8, 2, 0.1, "f32", 2),
-    (260, 100, 8, 8, 0.1, "f32", 1),       # fp32 with two query blocks
+    (260, 100, 8, 6, 0.1, "f32", 1),       # fp32 with two query blocks
 ]
 
 
