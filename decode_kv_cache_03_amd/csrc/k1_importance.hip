@@ -196,8 +196,6 @@ hipError_t run_k1(const P& p, int nqb, int k1_items, int num_units, float* part,
   }
 }
 
-template hipError_t run_k1<bf16_bits, DenseProblem<bf16_bits>>(const DenseProblem<bf16_bits>&, int, int, int, float*, float*, float*, int, hipStream_t);
-template hipError_t run_k1<float, DenseProblem<float>>(const DenseProblem<float>&, int, int, int, float*, float*, float*, int, hipStream_t);
 template hipError_t run_k1<bf16_bits, PagedProblem<bf16_bits>>(const PagedProblem<bf16_bits>&, int, int, int, float*, float*, float*, int, hipStream_t);
 template hipError_t run_k1<float, PagedProblem<float>>(const PagedProblem<float>&, int, int, int, float*, float*, float*, int, hipStream_t);
 

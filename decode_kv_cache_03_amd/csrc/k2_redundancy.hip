@@ -1,4 +1,5 @@
-// Redundancy R, importance I and joint score Z, one pass over the keys.
+// Redundancy R, importance I and joint score Z; and the fused dense kernel
+// that runs the whole step per unit.
 //
 // Pages: redundancy is measured by the cosine similarity of key vectors and
 // serves to find and prune near-duplicates (sourcepulse summary of R-KV,
@@ -20,37 +21,42 @@
 // Nothing N x N is ever stored: each lane keeps running row maxima in
 // registers.
 //
-// Work item = (unit, block of 128 rows). Column tiles of 128 keys are staged
-// in LDS (double-buffered, XOR-swizzled 16-byte chunks so fragment reads hit
+// Block = (unit, 128 rows). Column tiles of 128 keys are staged in LDS
+// (double-buffered, XOR-swizzled 16-byte chunks so fragment reads hit
 // distinct banks). The 4 waves form a 2x2 grid over each 128x128 step: wave
 // (r, c) holds rows 64r..64r+63 of the block as MFMA A fragments in registers
 // and multiplies them by columns 64c..64c+63 of the tile, as 2x2 tiles of
 // 32x32x16 per k-step. The block's own (diagonal) tile comes first: it
 // supplies the A fragments and is the only step that needs the j < i mask.
-// Tiles 0..blk-1 lie wholly left of the diagonal and run unmasked.
+// Tiles 0..blk-1 lie wholly left of the diagonal and run unmasked. After
+// the A fragments are read, the block's keys are scored for importance: with
+// the key rows as the B operand of Q x K^T each lane holds one key and 16
+// query rows, so the mean over a head's window queries and the max over heads
+// reduce inside the lane (plus one exchange between the 32-lane halves). At
+// the end the row maxima are reduced across lanes by a butterfly that halves
+// the values per lane at each exchange.
 //
-// The grid is persistent: about two workgroups per CU walk the work items,
-// workgroup w taking items w, w+G, w+2G, ... (G = grid size, a multiple of
-// 8, so every item a workgroup takes maps to its own XCD, where all blocks of
-// a unit are scheduled together and share the unit's keys in that XCD's L2).
-// The tile stream never stops between items: during an item's last step the
-// next item's diagonal tile and query rows are already being loaded, so the
-// per-item start-up latency is hidden.
+// Both kernels are persistent: about two workgroups per CU. The tile stream
+// never stops between blocks: during a block's last step the next block's
+// diagonal tile is already being loaded. Per-lane addresses are computed once
+// (tiles arrive by direct global->LDS loads from a uniform base plus a fixed
+// per-lane offset; fragment reads use fixed per-lane LDS offsets), since the
+// MFMA issue rate is the budget.
 //
-// Per item, after the A fragments are read, the block's keys are scored for
-// importance: with the key rows as the B operand of Q x K^T each lane holds
-// one key and 16 query rows, so the mean over a head's window queries and the
-// max over heads reduce inside the lane (plus one exchange between the
-// 32-lane halves), against the softmax normalisers merged beforehand.
-// At the end of the item the row maxima are reduced across lanes by a
-// butterfly that halves the values per lane at each exchange, so no large
-// LDS buffer competes with the tile buffers.
-//
-// The MFMA issue rate is the budget, so per-lane addresses are computed once:
-// tiles arrive by direct global->LDS loads from a uniform base plus a fixed
-// per-lane offset, and fragment reads use fixed per-lane LDS offsets.
+//  * k2_items_kernel walks a list of (unit, block) items; item k goes to
+//    workgroup k mod G (G a multiple of 8, so all blocks of a unit run on one
+//    XCD and share its keys in that XCD's L2). Used for paged caches, whose
+//    ragged units are balanced by the host's longest-first list. Needs the
+//    softmax statistics and norms of a separate pass (k1_importance.hip).
+//  * k2_fused_kernel (dense caches) gives each workgroup whole units and runs
+//    the entire step for each: (S) stream the unit's keys once from memory
+//    for the softmax statistics and norms, (R) all blocks as above with the
+//    tiles re-read from cache, (T) select the kept indices, (G) gather the
+//    kept K/V rows. No state crosses workgroups, and with two workgroups per
+//    CU one's memory phases overlap the other's MFMA phase.
 #include "rkv_problem.hpp"
 #include "rkv_launch.hpp"
+#include "rkv_select.hpp"
 
 namespace rkv {
 
@@ -62,6 +68,7 @@ struct K2Cfg {
   static constexpr int TILE_BYTES = kK2Cols * RB;
   static constexpr int LOADS = kK2Cols * RB / 1024 / 4;   // KiB of tile per wave
   static constexpr int ROWS_PER_KB = 1024 / RB;
+  static constexpr int PER = 16 / ROWS_PER_KB;            // tile loads per swizzle period
 };
 
 // Byte offset, inside a tile, of the slot holding chunk `chunk` of tile row n:
@@ -85,31 +92,346 @@ __device__ __forceinline__ void max_butterfly_step(float (&val)[32], int lane) {
   }
 }
 
+// Per-workgroup context: LDS regions and per-lane constants.
+template <typename T>
+struct K2Ctx {
+  using C = K2Cfg<T>;
+  char* tiles;
+  char* qlds;
+  float2* slds;
+  float* imp_l;
+  float* comb;
+  int tid, lane, half, l32, wave, wr, wc;
+  int rpg_shift;
+  float lam;
+  int lofs[C::PER];   // tile-load offsets (bytes) by load index mod PER
+  int boff[C::NCH];   // B fragment offsets; A fragments sit a_minus_b further
+  int a_minus_b;
+
+  __device__ __forceinline__ void init(char* lds, const K2Lds& plan, int rpg, float lam_) {
+    tiles = lds + plan.tiles;
+    qlds = lds + plan.q;
+    slds = reinterpret_cast<float2*>(lds + plan.stats);
+    imp_l = reinterpret_cast<float*>(lds + plan.imp);
+    comb = reinterpret_cast<float*>(lds + plan.comb);
+    tid = threadIdx.x;
+    lane = tid & 63;
+    half = lane >> 5;
+    l32 = lane & 31;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    wr = wave >> 1;
+    wc = wave & 1;
+    rpg_shift = rpg;
+    lam = lam_;
+    // Wave w fills KiB w*LOADS + i of a tile; lane l of load i writes row
+    // ROWS_PER_KB*i + l/RC of the wave's rows at slot l % RC, fetching chunk
+    // slot ^ (row & 15); row & 15 repeats every PER loads.
+#pragma unroll
+    for (int q = 0; q < C::PER; ++q) {
+      const int r16 = (q * C::ROWS_PER_KB + lane / C::RC) & 15;
+      lofs[q] = (lane / C::RC) * C::RB + (((lane % C::RC) ^ r16) << 4);
+    }
+    // Fragment reads: rows (A) wr*64 + rb*32 + l32, columns (B) wc*64 + cb*32
+    // + l32, chunk half*NCH + c; +32 rows keeps row & 15, so it is +32*RB.
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c) boff[c] = frag_offset<T>(wc * 64 + l32, half * C::NCH + c);
+    a_minus_b = (wr - wc) * 64 * C::RB;
+  }
+};
+
+// Rows first_row..first_row+127 of unit u into tile buffer buf; rows past the
+// unit repeat its last row (only the last tile of a unit has such rows).
+template <typename T, class P>
+__device__ __forceinline__ void tile_load(const P& p, const K2Ctx<T>& x, int u, int n_u,
+                                          int first_row, int buf, bool clamp) {
+  using C = K2Cfg<T>;
+  char* dst = x.tiles + buf * C::TILE_BYTES + x.wave * C::LOADS * 1024;
+  const int wrow = first_row + x.wave * C::LOADS * C::ROWS_PER_KB;   // first row this wave loads
+  if constexpr (P::kRowsContiguous) {
+    if (!clamp) {
+      const char* src = reinterpret_cast<const char*>(p.krow(u, wrow));
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i)
+        load16_to_lds(src + i * 1024 + x.lofs[i % C::PER], dst + i * 1024);
+      return;
+    }
+  }
+  int lane = x.lane;
+  asm volatile("" : "+v"(lane));   // per call: keeps the row offsets out of callers' loops
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int r = min(wrow + i * C::ROWS_PER_KB + lane / C::RC, n_u - 1);
+    const int chunk_ofs = x.lofs[i % C::PER] - (lane / C::RC) * C::RB;
+    load16_to_lds(reinterpret_cast<const char*>(p.krow(u, r)) + chunk_ofs, dst + i * 1024);
+  }
+}
+
+// The unit's window queries (G*w rows, swizzled like tile rows) into LDS.
+template <typename T, class P>
+__device__ __forceinline__ void q_load(const P& p, const K2Ctx<T>& x, int u) {
+  using C = K2Cfg<T>;
+  const int gw = p.G * p.W;
+  const char* q = reinterpret_cast<const char*>(p.q(u));
+  const int qkb = (gw * C::RB + 1023) / 1024;
+  int lane = x.lane;
+  asm volatile("" : "+v"(lane));   // per call: keeps the offsets out of callers' loops
+  for (int kb = x.wave; kb < qkb; kb += 4) {
+    const int n = kb * C::ROWS_PER_KB + lane / C::RC;
+    const int c = (lane % C::RC) ^ (n & 15);
+    load16_to_lds(q + min(n, gw - 1) * C::RB + c * 16, x.qlds + kb * 1024);
+  }
+}
+
+// Softmax normalisers (max, 1/sum) of the unit's query rows from global memory.
+template <int NQB, typename T>
+__device__ __forceinline__ void stats_load(const float* fin, const K2Ctx<T>& x, int u) {
+  if (x.wave == 0 && x.lane < NQB * 16)
+    load16_to_lds(reinterpret_cast<const char*>(fin) + ((int64_t)u * NQB * 32 + 2 * x.lane) * 8,
+                  reinterpret_cast<char*>(x.slds));
+}
+
+template <typename T>
+__device__ __forceinline__ void tile_mma(const char* tb, const K2Ctx<T>& x,
+                                         const u32x4_t (&af)[2][K2Cfg<T>::NCH],
+                                         f32x16_t (&acc)[2][2]) {
+  using C = K2Cfg<T>;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x16_t{};
+#pragma unroll
+  for (int c = 0; c < C::NCH; ++c) {
+    const u32x4_t b0 = ld16(tb + x.boff[c]);
+    const u32x4_t b1 = ld16(tb + x.boff[c] + 32 * C::RB);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      mma_chunk<T>(acc[rb][0], af[rb][c], b0);
+      mma_chunk<T>(acc[rb][1], af[rb][c], b1);
+    }
+  }
+}
+
+// Importance of one key per lane (key = row of kf; both 32-lane halves hold
+// the same key). Padding query rows (r >= w or g >= G) have zero queries and
+// zero 1/sum, so they add nothing; only keys among the last w need the
+// causal test.
 template <typename T, int NQB, class P>
-__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_redundancy_kernel(
+__device__ __forceinline__ float block_importance(const P& p, const K2Ctx<T>& x,
+                                                  const u32x4_t (&kf)[K2Cfg<T>::NCH], int key,
+                                                  int n_u, bool causal) {
+  using C = K2Cfg<T>;
+  const int rpg_mask = (1 << x.rpg_shift) - 1;
+  const int octets_per_group = (1 << x.rpg_shift) >> 3;
+  const float inv_w = 1.0f / (float)p.W;
+  float best = 0.f, run = 0.f;
+  int lane_v = x.lane;   // re-materialised per call: keeps per-lane masks out of loop preheaders
+  asm volatile("" : "+v"(lane_v));
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    u32x4_t qf[C::NCH];
+    {
+      const int m = qb * 32 + (lane_v & 31);
+      const int g = m >> x.rpg_shift, r = m & rpg_mask;
+      const bool qok = g < p.G && r < p.W;
+      const int n = qok ? g * p.W + r : 0;
+#pragma unroll
+      for (int c = 0; c < C::NCH; ++c)
+        qf[c] = qok ? ld16(x.qlds + frag_offset<T>(n, x.half * C::NCH + c)) : zero16();
+    }
+    f32x16_t acc = {};
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c) mma_chunk<T>(acc, qf[c], kf[c]);   // C[query][key]
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float os = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int v = 4 * t + j;
+        const int m = qb * 32 + acc_row(v, lane_v);
+        const float2 st = x.slds[m];
+        const float pr = fast_exp2(acc[v] * kLogitScaleLog2 - st.x) * st.y;
+        const float vis = (!causal || key <= n_u - p.W + (m & rpg_mask)) ? 1.f : 0.f;
+        os = fmaf(pr, vis, os);   // arithmetic, not a branch around the exp
+      }
+      os += __shfl_xor(os, 32, 64);
+      run += os;
+      const int o = qb * 4 + t;
+      if (((o + 1) & (octets_per_group - 1)) == 0) {
+        if (o / octets_per_group < p.G) best = fmaxf(best, run * inv_w);
+        run = 0.f;
+      }
+    }
+  }
+  return best;
+}
+
+// What a block loads during its last step: the next block's diagonal tile,
+// and for a different unit its queries and normalisers (from `fin`).
+struct Prefetch {
+  bool valid;
+  int u, n, first_row;
+  bool queries;
+};
+
+// One block (unit u, rows blk*128..): on entry its diagonal tile is in flight
+// into buffer `cur`; on exit `cur` holds the prefetched tile, if any.
+template <typename T, int NQB, class P>
+__device__ __forceinline__ void k2_block(const P& p, const K2Ctx<T>& x, int& cur, int u, int N,
+                                         int blk, const float* __restrict__ rinv,
+                                         const Prefetch& nx, const float* __restrict__ fin,
+                                         float* __restrict__ Z, float* __restrict__ Rdbg,
+                                         float* __restrict__ Idbg) {
+  using C = K2Cfg<T>;
+  constexpr int NCH = C::NCH;
+  const int base = blk * kK2Rows;
+  const int row0 = base + x.wr * 64;
+  const bool wave_live = row0 < N;
+  const int64_t so = p.score_off(u);
+  auto prefetch_next = [&]() {
+    if (!nx.valid) return;
+    tile_load<T>(p, x, nx.u, nx.n, nx.first_row, cur ^ 1, true);
+    if (nx.queries) {
+      q_load<T>(p, x, nx.u);
+      stats_load<NQB>(fin, x, nx.u);
+    }
+  };
+
+  // 1. the diagonal tile (and the unit's queries) have landed
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  u32x4_t af[2][NCH];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      af[rb][c] = ld16(x.tiles + cur * C::TILE_BYTES + x.boff[c] + x.a_minus_b + rb * 32 * C::RB);
+
+  // 2. importance of the block's keys; wave (r, c) takes keys r*64 + c*32 + l32
+  if (wave_live) {
+    const int key = row0 + x.wc * 32 + x.l32;
+    const bool causal = base + kK2Rows > N - p.W;   // block reaches the window's keys
+    const float best = (x.wc == 0) ? block_importance<T, NQB>(p, x, af[0], key, N, causal)
+                                   : block_importance<T, NQB>(p, x, af[1], key, N, causal);
+    if (x.half == 0) x.imp_l[x.wr * 64 + x.wc * 32 + x.l32] = best;
+  }
+  __syncthreads();   // queries are no longer read: a prefetch may replace them
+
+  // 3. prefetch: tile 0 of this block, or what follows the block
+  if (blk > 0)
+    tile_load<T>(p, x, u, N, 0, cur ^ 1, false);
+  else
+    prefetch_next();
+
+  float mx[2][16];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx[rb][v] = -INFINITY;
+
+  // 4. diagonal step: wave (0,1) lies above the diagonal, (1,0) below it;
+  // (0,0) and (1,1) straddle it and mask per element (j < i)
+  if (wave_live && x.wc <= x.wr) {
+    f32x16_t acc[2][2];
+    tile_mma<T>(x.tiles + cur * C::TILE_BYTES, x, af, acc);
+    float rc[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int col = base + x.wc * 64 + cb * 32 + x.l32;
+      rc[cb] = col < N ? rinv[so + col] : 0.f;
+    }
+    if (x.wc < x.wr) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          mx[rb][v] = fmaxf(mx[rb][v], fmaxf(acc[rb][0][v] * rc[0], acc[rb][1][v] * rc[1]));
+    } else {
+      // rows and columns are the same 64 keys: row rb*32 + a follows column
+      // cb*32 + b iff rb > cb, or rb == cb and a > b
+      int lane_v = x.lane;   // re-materialised (see block_importance)
+      asm volatile("" : "+v"(lane_v));
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb <= rb; ++cb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const bool ok = (rb > cb) || (acc_row(v, lane_v) > (lane_v & 31));
+            if (ok) mx[rb][v] = fmaxf(mx[rb][v], acc[rb][cb][v] * rc[cb]);
+          }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  cur ^= 1;
+
+  // 5. tiles 0..blk-1, wholly left of the diagonal; tile J is in buffer cur
+  const float* rcol = rinv + so + x.wc * 64 + x.l32;
+  for (int J = 0; J < blk; ++J) {
+    if (J + 1 < blk)
+      tile_load<T>(p, x, u, N, (J + 1) * kK2Cols, cur ^ 1, false);
+    else
+      prefetch_next();
+    if (wave_live) {
+      f32x16_t acc[2][2];
+      tile_mma<T>(x.tiles + cur * C::TILE_BYTES, x, af, acc);
+      const float r0 = rcol[J * kK2Cols], r1 = rcol[J * kK2Cols + 32];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          mx[rb][v] = fmaxf(mx[rb][v], fmaxf(acc[rb][0][v] * r0, acc[rb][1][v] * r1));
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  // 6. row maxima. Value j = rb*16 + v of a lane belongs to row
+  // rb*32 + acc_row(v, lane); the 32 lanes of a half share rows. The
+  // butterfly over lane bits 4..0 leaves lane l with value j = l & 31.
+  float val[32];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) val[rb * 16 + v] = mx[rb][v];
+  max_butterfly_step<16>(val, x.lane);
+  max_butterfly_step<8>(val, x.lane);
+  max_butterfly_step<4>(val, x.lane);
+  max_butterfly_step<2>(val, x.lane);
+  max_butterfly_step<1>(val, x.lane);
+  if (wave_live) {
+    const int rl = x.wr * 64 + (x.l32 >> 4) * 32 + acc_row(x.l32 & 15, x.lane);   // row in block
+    x.comb[x.wc * kK2Rows + rl] = val[0];
+  }
+  __syncthreads();
+
+  // 7. R, I and Z for the block's rows
+  if (x.tid < kK2Rows) {
+    const int row = base + x.tid;
+    if (row < N) {
+      const float m = fmaxf(x.comb[x.tid], x.comb[kK2Rows + x.tid]);
+      const float R = (row == 0) ? 0.f : m * rinv[so + row];
+      const float I = x.imp_l[x.tid];
+      const float z = x.lam * I - (1.0f - x.lam) * R;
+      Z[so + row] = z + 0.0f;   // folds -0 onto +0
+      if (Rdbg != nullptr) Rdbg[so + row] = R;
+      if (Idbg != nullptr) Idbg[so + row] = I;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent kernel over a list of (unit, block) items.
+template <typename T, int NQB, class P>
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_items_kernel(
     P p, int total_items, const float* __restrict__ rinv, const float* __restrict__ fin,
     float* __restrict__ Z, float* __restrict__ Rdbg, float* __restrict__ Idbg, float lam,
     int rpg_shift) {
-  using C = K2Cfg<T>;
-  constexpr int NCH = C::NCH;
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int gw = p.G * p.W;
-  const K2Lds plan = k2_lds_plan(C::RB, gw, NQB);
-  char* const tiles = lds + plan.tiles;
-  char* const qlds = lds + plan.q;
-  float2* const slds = reinterpret_cast<float2*>(lds + plan.stats);
-  float* const imp_l = reinterpret_cast<float*>(lds + plan.imp);
-  float* const comb = reinterpret_cast<float*>(lds + plan.comb);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, half = lane >> 5, l32 = lane & 31;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wave >> 1, wc = wave & 1;      // row group, column group of this wave
+  K2Ctx<T> x;
+  x.init(lds, k2_lds_plan(K2Cfg<T>::RB, p.G * p.W, NQB), rpg_shift, lam);
   const int stride = gridDim.x;
-  const int rpg_mask = (1 << rpg_shift) - 1;
-  const int octets_per_group = (1 << rpg_shift) >> 3;
-  const float inv_w = 1.0f / (float)p.W;
-
   // next valid work item at or after k (in steps of the grid size)
   auto next_item = [&](int k, int& u, int& blk) -> int {
     for (; k < total_items; k += stride)
@@ -120,297 +442,219 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_redundancy_ker
       }
     return total_items;
   };
-
-  // Per-lane tile-load offsets. Wave w fills KiB w*LOADS + i of a tile; lane
-  // l of load i writes row ROWS_PER_KB*i + l/RC of the wave's rows at slot
-  // l % RC, fetching chunk slot ^ (row & 15). Row & 15 repeats every
-  // 16/ROWS_PER_KB loads, so a few offsets cover them all.
-  constexpr int PER = 16 / C::ROWS_PER_KB;
-  int lofs[PER];
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int r16 = (q * C::ROWS_PER_KB + lane / C::RC) & 15;   // (tile row) & 15 for load i = q mod PER
-    lofs[q] = (lane / C::RC) * C::RB + (((lane % C::RC) ^ r16) << 4);
-  }
-  // Rows first_row.. of unit u into tile buffer buf; rows past the unit
-  // (only in a diagonal tile) repeat its last row.
-  auto tile_load = [&](int u, int n_u, int first_row, int buf, bool clamp) {
-    char* dst = tiles + buf * C::TILE_BYTES + wave * C::LOADS * 1024;
-    const int wrow = first_row + wave * C::LOADS * C::ROWS_PER_KB;   // first row this wave loads
-    if constexpr (P::kRowsContiguous) {
-      if (!clamp) {
-        const char* src = reinterpret_cast<const char*>(p.krow(u, wrow));
-#pragma unroll
-        for (int i = 0; i < C::LOADS; ++i)
-          load16_to_lds(src + i * 1024 + lofs[i % PER], dst + i * 1024);
-        return;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int r = min(wrow + i * C::ROWS_PER_KB + lane / C::RC, n_u - 1);
-      const int chunk_ofs = lofs[i % PER] - (lane / C::RC) * C::RB;
-      load16_to_lds(reinterpret_cast<const char*>(p.krow(u, r)) + chunk_ofs, dst + i * 1024);
-    }
-  };
-  // The unit's window queries (G*w rows, swizzled) and softmax normalisers.
-  auto q_load = [&](int u) {
-    const char* q = reinterpret_cast<const char*>(p.q(u));
-    const int qkb = (gw * C::RB + 1023) / 1024;
-    for (int kb = wave; kb < qkb; kb += 4) {
-      const int n = kb * C::ROWS_PER_KB + lane / C::RC;
-      const int c = (lane % C::RC) ^ (n & 15);
-      const int nn = min(n, gw - 1);
-      load16_to_lds(q + nn * C::RB + c * 16, qlds + kb * 1024);
-    }
-    if (wave == 0 && lane < NQB * 16)
-      load16_to_lds(reinterpret_cast<const char*>(fin) + ((int64_t)u * NQB * 32 + 2 * lane) * 8,
-                    reinterpret_cast<char*>(slds));
-  };
-
-  // Fragment read offsets: rows (A) wr*64 + rb*32 + l32, columns (B)
-  // wc*64 + cb*32 + l32, chunk half*NCH + c. Adding 32 to a row leaves
-  // (row & 15) unchanged, so the second 32 rows/columns sit 32*RB further.
-  int boff[NCH];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) boff[c] = frag_offset<T>(wc * 64 + l32, half * NCH + c);
-  // rows and columns differ by a multiple of 64 rows, which keeps row & 15
-  const int a_minus_b = (wr - wc) * 64 * C::RB;
-
-  auto tile_mma = [&](const char* tb, const u32x4_t (&af)[2][NCH], f32x16_t (&acc)[2][2]) {
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x16_t{};
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const u32x4_t b0 = ld16(tb + boff[c]);
-      const u32x4_t b1 = ld16(tb + boff[c] + 32 * C::RB);
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        mma_chunk<T>(acc[rb][0], af[rb][c], b0);
-        mma_chunk<T>(acc[rb][1], af[rb][c], b1);
-      }
-    }
-  };
-
-  // Importance of one 32-key half of the wave's rows (key = row of kf).
-  // Padding query rows (r >= w or g >= G) have zero queries and zero 1/sum,
-  // so they add nothing; only keys among the last w need the causal test.
-  auto importance_of = [&](const u32x4_t (&kf)[NCH], int key, int n_u, bool causal) -> float {
-    float best = 0.f, run = 0.f;
-    int lane_v = lane;   // re-materialised per item: keeps per-lane masks out of the loop preheader
-    asm volatile("" : "+v"(lane_v));
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      u32x4_t qf[NCH];
-      {
-        const int m = qb * 32 + (lane_v & 31);
-        const int g = m >> rpg_shift, r = m & rpg_mask;
-        const bool qok = g < p.G && r < p.W;
-        const int n = qok ? g * p.W + r : 0;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c)
-          qf[c] = qok ? ld16(qlds + frag_offset<T>(n, half * NCH + c)) : zero16();
-      }
-      f32x16_t acc = {};
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) mma_chunk<T>(acc, qf[c], kf[c]);   // C[query][key]
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        float os = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int v = 4 * t + j;
-          const int m = qb * 32 + acc_row(v, lane_v);
-          const float2 st = slds[m];
-          const float pr = fast_exp2(acc[v] * kLogitScaleLog2 - st.x) * st.y;
-          const float vis = (!causal || key <= n_u - p.W + (m & rpg_mask)) ? 1.f : 0.f;
-          os = fmaf(pr, vis, os);   // arithmetic, not a branch around the exp
-        }
-        os += __shfl_xor(os, 32, 64);
-        run += os;
-        const int o = qb * 4 + t;
-        if (((o + 1) & (octets_per_group - 1)) == 0) {
-          if (o / octets_per_group < p.G) best = fmaxf(best, run * inv_w);
-          run = 0.f;
-        }
-      }
-    }
-    return best;
-  };
-
   int u, blk;
   int k = next_item(blockIdx.x, u, blk);
   if (k >= total_items) return;
   int N = p.n(u);
-  tile_load(u, N, blk * kK2Rows, 0, true);
-  q_load(u);
-  int cur = 0;   // buffer holding the current tile
-
+  tile_load<T>(p, x, u, N, blk * kK2Rows, 0, true);
+  q_load<T>(p, x, u);
+  stats_load<NQB>(fin, x, u);
+  int cur = 0;
   while (true) {
-    const int base = blk * kK2Rows;
-    const int row0 = base + wr * 64;
-    const bool wave_live = row0 < N;
-    const int64_t so = p.score_off(u);
+    Prefetch nx;
     int un = 0, bn = 0;
     const int kn = next_item(k + stride, un, bn);
-    const bool has_next = kn < total_items;
-    const int Nn = has_next ? p.n(un) : 0;
+    nx.valid = kn < total_items;
+    nx.u = un;
+    nx.n = nx.valid ? p.n(un) : 0;
+    nx.first_row = bn * kK2Rows;
+    nx.queries = un != u;   // the same unit keeps its queries and normalisers
+    k2_block<T, NQB>(p, x, cur, u, N, blk, rinv, nx, fin, Z, Rdbg, Idbg);
+    if (!nx.valid) break;
+    k = kn;
+    u = un;
+    blk = bn;
+    N = nx.n;
+  }
+}
 
-    // 1. the diagonal tile (and this unit's queries) have landed
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    u32x4_t af[2][NCH];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int c = 0; c < NCH; ++c)
-        af[rb][c] = ld16(tiles + cur * C::TILE_BYTES + boff[c] + a_minus_b + rb * 32 * C::RB);
+// ---------------------------------------------------------------------------
+// Fused dense kernel: whole units per workgroup.
+template <typename T, int NQB>
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_fused_kernel(
+    DenseProblem<T> p, float* __restrict__ rinv, float* __restrict__ Z, int32_t* __restrict__ kept_all,
+    T* __restrict__ K_out, T* __restrict__ V_out, int64_t out_stride, float* __restrict__ Rdbg,
+    float* __restrict__ Idbg, float lam, int rpg_shift) {
+  using C = K2Cfg<T>;
+  constexpr int NCH = C::NCH;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const K2Lds plan = k2_lds_plan(C::RB, p.G * p.W, NQB);
+  K2Ctx<T> x;
+  x.init(lds, plan, rpg_shift, lam);
+  float2* const sred = reinterpret_cast<float2*>(lds + plan.sred);   // [4][NQB*32]
+  SelectScratch& ssh = *reinterpret_cast<SelectScratch*>(x.tiles);   // tiles are idle in phase T
+  const int N = p.N, B = p.B;
+  const int nb = (N + kK2Rows - 1) / kK2Rows;
+  const int rpg_mask = (1 << rpg_shift) - 1;
 
-    // 2. importance of the block's keys; wave (r, c) takes keys r*64 + c*32 + l32
-    if (wave_live) {
-      const int key = row0 + wc * 32 + l32;
-      const bool causal = base + kK2Rows > N - p.W;   // block reaches the window's keys
-      const float best = (wc == 0) ? importance_of(af[0], key, N, causal)
-                                   : importance_of(af[1], key, N, causal);
-      if (half == 0) imp_l[wr * 64 + wc * 32 + l32] = best;
-    }
-    __syncthreads();   // queries are no longer read: the prefetch below may replace them
+  for (int u = blockIdx.x; u < p.num_units; u += gridDim.x) {
+    const int64_t so = p.score_off(u);
+    int cur = 0;
 
-    // 3. prefetch: tile 0 of this block, or the next item's diagonal tile
-    if (blk > 0) {
-      tile_load(u, N, 0, cur ^ 1, false);
-    } else if (has_next) {
-      tile_load(un, Nn, bn * kK2Rows, cur ^ 1, true);
-      q_load(un);
-    }
-
-    float mx[2][16];
+    // (S) softmax statistics and norms: stream the unit's keys once. Wave w
+    // takes keys 32w..32w+31 of each tile as the A operand of K x Q^T, so each
+    // lane owns one query column and keeps its running max / sum of exp.
+    q_load<T>(p, x, u);
+    tile_load<T>(p, x, u, N, 0, 0, nb == 1);
+    float mrun[NQB], srun[NQB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx[rb][v] = -INFINITY;
-
-    // 4. diagonal step: wave (0,1) lies above the diagonal, (1,0) below it;
-    // (0,0) and (1,1) straddle it and mask per element (j < i)
-    if (wave_live && wc <= wr) {
-      f32x16_t acc[2][2];
-      tile_mma(tiles + cur * C::TILE_BYTES, af, acc);
-      float rc[2];
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int col = base + wc * 64 + cb * 32 + l32;
-        rc[cb] = col < N ? rinv[so + col] : 0.f;
-      }
-      if (wc < wr) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            mx[rb][v] = fmaxf(mx[rb][v], fmaxf(acc[rb][0][v] * rc[0], acc[rb][1][v] * rc[1]));
-      } else {
-        // rows and columns are the same 64 keys: row rb*32 + a follows column
-        // cb*32 + b iff rb > cb, or rb == cb and a > b
-        int lane_v = lane;   // re-materialised per item (see importance_of)
-        asm volatile("" : "+v"(lane_v));
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int cb = 0; cb <= rb; ++cb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const bool ok = (rb > cb) || (acc_row(v, lane_v) > (lane_v & 31));
-              if (ok) mx[rb][v] = fmaxf(mx[rb][v], acc[rb][cb][v] * rc[cb]);
-            }
-      }
+    for (int qb = 0; qb < NQB; ++qb) {
+      mrun[qb] = -INFINITY;
+      srun[qb] = 0.f;
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    cur ^= 1;
-
-    // 5. tiles 0..blk-1, wholly left of the diagonal; tile J is in buffer cur
-    const float* rcol = rinv + so + wc * 64 + l32;
-    for (int J = 0; J < blk; ++J) {
-      if (J + 1 < blk) {
-        tile_load(u, N, (J + 1) * kK2Cols, cur ^ 1, false);
-      } else if (has_next) {
-        tile_load(un, Nn, bn * kK2Rows, cur ^ 1, true);
-        q_load(un);
-      }
-      if (wave_live) {
-        f32x16_t acc[2][2];
-        tile_mma(tiles + cur * C::TILE_BYTES, af, acc);
-        const float r0 = rcol[J * kK2Cols], r1 = rcol[J * kK2Cols + 32];
+    for (int t = 0; t < nb; ++t) {
+      // prefetch the next key tile, or block 0's diagonal tile (= tile 0)
+      if (t + 1 < nb)
+        tile_load<T>(p, x, u, N, (t + 1) * kK2Rows, cur ^ 1, t + 2 == nb);
+      else
+        tile_load<T>(p, x, u, N, 0, cur ^ 1, nb == 1);
+      const char* tb = x.tiles + cur * C::TILE_BYTES;
+      // lane-derived values are re-materialised per tile, so that nothing of
+      // this phase is hoisted out of the unit loop and held through phase R
+      int lane_v = x.lane;
+      asm volatile("" : "+v"(lane_v));
+      const int l32 = lane_v & 31, half = lane_v >> 5;
+      const int kl = x.wave * 32 + l32;                 // tile row of this lane's key
+      const int key = t * kK2Rows + kl;
+      u32x4_t kf[NCH];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+      for (int c = 0; c < NCH; ++c) kf[c] = ld16(tb + frag_offset<T>(kl, half * NCH + c));
+      float ss = 0.f;
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            mx[rb][v] = fmaxf(mx[rb][v], fmaxf(acc[rb][0][v] * r0, acc[rb][1][v] * r1));
+      for (int c = 0; c < NCH; ++c) ss += sumsq_chunk<T>(kf[c]);
+      ss += __shfl_xor(ss, 32, 64);
+      if (half == 0 && key < N) rinv[so + key] = ss > 0.f ? __frsqrt_rn(ss) : 0.f;
+      const bool edge = (t + 1) * kK2Rows > N - p.W;    // tile holds padding or window keys
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int m = qb * 32 + l32;                    // query column of this lane
+        const int g = m >> rpg_shift, r = m & rpg_mask;
+        const bool qok = g < p.G && r < p.W;
+        u32x4_t qf[NCH];
+        const int qn = qok ? g * p.W + r : 0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+          qf[c] = qok ? ld16(x.qlds + frag_offset<T>(qn, half * NCH + c)) : zero16();
+        f32x16_t acc = {};
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) mma_chunk<T>(acc, kf[c], qf[c]);   // C[key][query]
+        const int last = N - p.W + r;                   // last key visible to window query r
+        float lg[16];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int kk = t * kK2Rows + x.wave * 32 + acc_row(v, lane_v);
+          lg[v] = acc[v] * kLogitScaleLog2;
+          if (edge || !qok) lg[v] = (qok && kk <= last) ? lg[v] : -INFINITY;
+          mt = fmaxf(mt, lg[v]);
+        }
+        const float mn = fmaxf(mrun[qb], mt);
+        if (mn != -INFINITY) {
+          float s = (mrun[qb] != -INFINITY) ? srun[qb] * fast_exp2(mrun[qb] - mn) : 0.f;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) s += fast_exp2(lg[v] - mn);
+          srun[qb] = s;
+          mrun[qb] = mn;
+        }
       }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       cur ^= 1;
     }
+    // merge the statistics: the two halves of a wave, then the four waves
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const float m2 = __shfl_xor(mrun[qb], 32, 64);
+      const float s2 = __shfl_xor(srun[qb], 32, 64);
+      const float mm = fmaxf(mrun[qb], m2);
+      float st = 0.f;
+      if (mm != -INFINITY)
+        st = (mrun[qb] != -INFINITY ? srun[qb] * fast_exp2(mrun[qb] - mm) : 0.f) +
+             (m2 != -INFINITY ? s2 * fast_exp2(m2 - mm) : 0.f);
+      if (x.half == 0) sred[x.wave * NQB * 32 + qb * 32 + x.l32] = make_float2(mm, st);
+    }
+    __syncthreads();
+    if (x.tid < NQB * 32) {
+      float mm = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) mm = fmaxf(mm, sred[w * NQB * 32 + x.tid].x);
+      float st = 0.f;
+      if (mm != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float2 e = sred[w * NQB * 32 + x.tid];
+          if (e.x != -INFINITY) st += e.y * fast_exp2(e.x - mm);
+        }
+      }
+      x.slds[x.tid] = (mm != -INFINITY && st > 0.f) ? make_float2(mm, 1.0f / st) : make_float2(0.f, 0.f);
+    }
+    // (block 0's first barrier publishes the normalisers)
 
-    // 6. row maxima. Value j = rb*16 + v of a lane belongs to row
-    // rb*32 + acc_row(v, lane); the 32 lanes of a half share rows. A butterfly
-    // over lane bits 4..0 keeps half of the remaining values at each exchange,
-    // so lane l ends with the max over its half for value j = l & 31.
-    float val[32];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) val[rb * 16 + v] = mx[rb][v];
-    max_butterfly_step<16>(val, lane);
-    max_butterfly_step<8>(val, lane);
-    max_butterfly_step<4>(val, lane);
-    max_butterfly_step<2>(val, lane);
-    max_butterfly_step<1>(val, lane);
-    if (wave_live) {
-      const int rl = wr * 64 + (l32 >> 4) * 32 + acc_row(l32 & 15, lane);   // row within the block
-      comb[wc * kK2Rows + rl] = val[0];
+    // (R) redundancy, importance and Z, block by block
+    for (int blk = 0; blk < nb; ++blk) {
+      Prefetch nx;
+      nx.valid = blk + 1 < nb;
+      nx.u = u;
+      nx.n = N;
+      nx.first_row = (blk + 1) * kK2Rows;
+      nx.queries = false;
+      k2_block<T, NQB>(p, x, cur, u, N, blk, rinv, nx, nullptr, Z, Rdbg, Idbg);
     }
     __syncthreads();
 
-    // 7. R, I and Z for the block's rows
-    if (tid < kK2Rows) {
-      const int row = base + tid;
-      if (row < N) {
-        const float m = fmaxf(comb[tid], comb[kK2Rows + tid]);
-        const float R = (row == 0) ? 0.f : m * rinv[so + row];
-        const float I = imp_l[tid];
-        const float z = lam * I - (1.0f - lam) * R;
-        Z[so + row] = z + 0.0f;   // folds -0 onto +0
-        if (Rdbg != nullptr) Rdbg[so + row] = R;
-        if (Idbg != nullptr) Idbg[so + row] = I;
-      }
-    }
+    // (T) kept indices of the unit
+    int32_t* kept = kept_all + p.kept_off(u);
+    select_block(Z + so, N, B, p.W, kept, ssh);
+    __syncthreads();
 
-    if (!has_next) break;
-    k = kn;
-    u = un;
-    blk = bn;
-    N = Nn;
+    // (G) kept K/V rows
+    gather_rows_block<T>(kept, B, [&](int r) { return p.krow(u, r); },
+                         [&](int r) { return p.vrow(u, r); }, K_out + (int64_t)u * out_stride,
+                         V_out + (int64_t)u * out_stride);
+    __syncthreads();
   }
+}
+
+// ---------------------------------------------------------------------------
+template <typename Kern>
+static hipError_t persistent_grid(Kern kern, int lds_bytes, int max_groups, int* grid) {
+  const void* fn = reinterpret_cast<const void*>(kern);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  int dev = 0, cus = 0, per_cu = 0;
+  if (e == hipSuccess) e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, lds_bytes);
+  if (e != hipSuccess) return e;
+  int g = 8 * ((max(1, per_cu) * cus + 7) / 8);
+  *grid = min(g, max_groups);
+  return hipSuccess;
 }
 
 template <typename T, int NQB, class P>
 static hipError_t run_k2_t(const P& p, int k2_items, const float* rinv, const float* fin, float* Z,
                            float* dbg_R, float* dbg_I, float lam, int rpg_shift, hipStream_t st) {
   const K2Lds plan = k2_lds_plan(Elem<T>::kRowBytes, p.G * p.W, NQB);
-  auto kern = k2_redundancy_kernel<T, NQB, P>;
-  const void* fn = reinterpret_cast<const void*>(kern);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, plan.total);
-  int dev = 0, cus = 0, per_cu = 0;
-  if (e == hipSuccess) e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, plan.total);
+  auto kern = k2_items_kernel<T, NQB, P>;
+  int grid = 0;
+  hipError_t e = persistent_grid(kern, plan.total, 8 * ((k2_items + 7) / 8), &grid);
   if (e != hipSuccess) return e;
-  int grid = 8 * ((max(1, per_cu) * cus + 7) / 8);
-  grid = min(grid, 8 * ((k2_items + 7) / 8));
   return launch("rkv_k2_redundancy", kern, dim3(grid), dim3(256), plan.total, st, p, k2_items, rinv,
                 fin, Z, dbg_R, dbg_I, lam, rpg_shift);
+}
+
+template <typename T, int NQB>
+static hipError_t run_fused_t(const DenseProblem<T>& p, float* rinv, float* Z, int32_t* kept,
+                              T* K_out, T* V_out, int64_t out_stride, float* dbg_R, float* dbg_I,
+                              float lam, int rpg_shift, hipStream_t st) {
+  const K2Lds plan = k2_lds_plan(Elem<T>::kRowBytes, p.G * p.W, NQB);
+  auto kern = k2_fused_kernel<T, NQB>;
+  int grid = 0;
+  hipError_t e = persistent_grid(kern, plan.total, p.num_units, &grid);
+  if (e != hipSuccess) return e;
+  return launch("rkv_fused_step", kern, dim3(grid), dim3(256), plan.total, st, p, rinv, Z, kept,
+                K_out, V_out, out_stride, dbg_R, dbg_I, lam, rpg_shift);
 }
 
 template <typename T, class P>
@@ -429,9 +673,27 @@ hipError_t run_k2(const P& p, int nqb, int k2_items, const float* rinv, const fl
   }
 }
 
-template hipError_t run_k2<bf16_bits, DenseProblem<bf16_bits>>(const DenseProblem<bf16_bits>&, int, int, const float*, const float*, float*, float*, float*, float, int, hipStream_t);
-template hipError_t run_k2<float, DenseProblem<float>>(const DenseProblem<float>&, int, int, const float*, const float*, float*, float*, float*, float, int, hipStream_t);
+template <typename T>
+hipError_t run_fused(const DenseProblem<T>& p, int nqb, float* rinv, float* Z, int32_t* kept,
+                     T* K_out, T* V_out, int64_t out_stride, float* dbg_R, float* dbg_I, float lam,
+                     int rpg_shift, hipStream_t st) {
+  if constexpr (sizeof(T) == 4) {
+    if (nqb == 1)
+      return run_fused_t<T, 1>(p, rinv, Z, kept, K_out, V_out, out_stride, dbg_R, dbg_I, lam, rpg_shift, st);
+    return run_fused_t<T, 2>(p, rinv, Z, kept, K_out, V_out, out_stride, dbg_R, dbg_I, lam, rpg_shift, st);
+  } else {
+    switch (nqb) {
+      case 1: return run_fused_t<T, 1>(p, rinv, Z, kept, K_out, V_out, out_stride, dbg_R, dbg_I, lam, rpg_shift, st);
+      case 2: return run_fused_t<T, 2>(p, rinv, Z, kept, K_out, V_out, out_stride, dbg_R, dbg_I, lam, rpg_shift, st);
+      case 3: return run_fused_t<T, 3>(p, rinv, Z, kept, K_out, V_out, out_stride, dbg_R, dbg_I, lam, rpg_shift, st);
+      default: return run_fused_t<T, 4>(p, rinv, Z, kept, K_out, V_out, out_stride, dbg_R, dbg_I, lam, rpg_shift, st);
+    }
+  }
+}
+
 template hipError_t run_k2<bf16_bits, PagedProblem<bf16_bits>>(const PagedProblem<bf16_bits>&, int, int, const float*, const float*, float*, float*, float*, float, int, hipStream_t);
 template hipError_t run_k2<float, PagedProblem<float>>(const PagedProblem<float>&, int, int, const float*, const float*, float*, float*, float*, float, int, hipStream_t);
+template hipError_t run_fused<bf16_bits>(const DenseProblem<bf16_bits>&, int, float*, float*, int32_t*, bf16_bits*, bf16_bits*, int64_t, float*, float*, float, int, hipStream_t);
+template hipError_t run_fused<float>(const DenseProblem<float>&, int, float*, float*, int32_t*, float*, float*, int64_t, float*, float*, float, int, hipStream_t);
 
 }  // namespace rkv

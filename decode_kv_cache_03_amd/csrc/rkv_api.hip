@@ -125,10 +125,8 @@ using rkv::PagedProblem;
 namespace {
 
 struct DenseLayout {
-  float* rinv;
-  float* z;
-  float* part;
-  float* fin;
+  float* rinv;   // [units][N] 1/||k_t|| (0 for a zero key)
+  float* z;      // [units][N] joint scores when the caller does not ask for them
   size_t bytes;
 };
 
@@ -173,14 +171,9 @@ int check_dense_desc(const rkv_dense_desc* d) {
 DenseLayout dense_layout(const rkv_dense_desc* d, char* base) {
   Carve c{base};
   const size_t units = (size_t)d->num_heads, n = (size_t)d->n_cand;
-  const int nqb = (d->gqa_group << rows_per_group_shift(d->window)) / 32 +
-                  (((d->gqa_group << rows_per_group_shift(d->window)) % 32) ? 1 : 0);
-  const size_t chunks = (n + rkv::kK1Keys - 1) / rkv::kK1Keys;
   DenseLayout L;
   L.rinv = c.take<float>(units * n);
   L.z = c.take<float>(units * n);
-  L.part = c.take<float>(units * chunks * nqb * 32 * 2);
-  L.fin = c.take<float>(units * nqb * 32 * 2);
   L.bytes = std::max<size_t>(c.used, kAlign);
   return L;
 }
@@ -204,27 +197,19 @@ int dense_run(const rkv_dense_desc* d, const void* K, const void* V, const void*
   p.B = d->budget;
   p.G = d->gqa_group;
   p.W = d->window;
-  p.k1_chunks = (d->n_cand + rkv::kK1Keys - 1) / rkv::kK1Keys;
-  p.k2_blocks = (d->n_cand + rkv::kK2Rows - 1) / rkv::kK2Rows;
   const int64_t out_stride = d->out_head_stride ? d->out_head_stride : (int64_t)d->budget * 128;
   const int units = d->num_heads;
   const int nkeep = std::min(d->n_cand, d->budget);
   hipError_t e;
   if (d->n_cand > d->budget) {
-    float* z = dbg_Z ? dbg_Z : L.z;
-    const int rpg_shift = rows_per_group_shift(d->window);
-    const int nqb = nqb_of(d->gqa_group, d->window);
-    e = rkv::run_k1<T>(p, nqb, units * p.k1_chunks, units, L.part, L.fin, L.rinv, rpg_shift, st);
-    if (e != hipSuccess) return hip_fail(e, "importance launch");
-    const int k2_items = 8 * ((units + 7) / 8) * p.k2_blocks;
-    e = rkv::run_k2<T>(p, nqb, k2_items, L.rinv, L.fin, z, dbg_R, dbg_I, d->mix_lambda, rpg_shift, st);
-    if (e != hipSuccess) return hip_fail(e, "redundancy launch");
-    e = rkv::run_k4(p, units, z, kept, 1, st);
-    if (e != hipSuccess) return hip_fail(e, "select launch");
-  } else {
-    e = rkv::run_k4(p, units, L.z, kept, 1, st);   // identity selection
-    if (e != hipSuccess) return hip_fail(e, "select launch");
+    e = rkv::run_fused<T>(p, nqb_of(d->gqa_group, d->window), L.rinv, dbg_Z ? dbg_Z : L.z, kept,
+                          static_cast<T*>(K_out), static_cast<T*>(V_out), out_stride, dbg_R, dbg_I,
+                          d->mix_lambda, rows_per_group_shift(d->window), st);
+    if (e != hipSuccess) return hip_fail(e, "compression launch");
+    return RKV_OK;
   }
+  e = rkv::run_k4(p, units, L.z, kept, 1, st);   // N <= B: identity selection and a plain copy
+  if (e != hipSuccess) return hip_fail(e, "select launch");
   e = rkv::run_k5_dense<T>(p, kept, static_cast<T*>(K_out), static_cast<T*>(V_out), out_stride,
                            nkeep, st);
   if (e != hipSuccess) return hip_fail(e, "gather launch");

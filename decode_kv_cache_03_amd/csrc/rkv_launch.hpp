@@ -36,6 +36,14 @@ template <typename T, class P>
 hipError_t run_k2(const P& p, int nqb, int k2_items, const float* rinv, const float* fin, float* Z,
                   float* dbg_R, float* dbg_I, float lam, int rpg_shift, hipStream_t st);
 
+// Dense caches, whole step in one persistent kernel: Z (and R, I when
+// requested) in Z/dbg_*, kept indices, and the kept K/V rows; rinv is
+// [units][N] scratch. Requires N > B.
+template <typename T>
+hipError_t run_fused(const DenseProblem<T>& p, int nqb, float* rinv, float* Z, int32_t* kept,
+                     T* K_out, T* V_out, int64_t out_stride, float* dbg_R, float* dbg_I, float lam,
+                     int rpg_shift, hipStream_t st);
+
 // Selection: kept indices per unit (ascending), from Z.
 template <class P>
 hipError_t run_k4(const P& p, int units, const float* Z, int32_t* kept, int fill_tail,

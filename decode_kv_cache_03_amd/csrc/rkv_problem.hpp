@@ -4,6 +4,7 @@
 // together. Two layouts are served by the same kernels through these
 // policies:
 //   Dense: unit u has rows K + u*kv_stride + t*128; all units share N and B.
+//          Served by the fused kernel, one unit per workgroup at a time.
 //   Paged: unit u = (s, hk) with s = u / H; row t of the unit lives in page
 //          page_table[s][t >> ps_shift] at slot t & (page_size-1); N and B
 //          are per sequence. Work items are listed by the host.
@@ -25,6 +26,7 @@ struct K2Lds {
   int stats;     // (max, 1/sum) per query row, NQB*32 float2
   int imp;       // importance of the block's 128 keys
   int comb;      // row maxima of the two column-group waves: [2][128] floats
+  int sred;      // per-wave softmax statistics of the fused kernel: [4][NQB*32] float2
   int total;
 };
 
@@ -36,7 +38,8 @@ __host__ __device__ inline K2Lds k2_lds_plan(int row_bytes, int gw, int nqb) {
   L.stats = L.q + qkb * 1024;
   L.imp = L.stats + nqb * 32 * 8;
   L.comb = L.imp + kK2Rows * 4;
-  L.total = L.comb + 2 * kK2Rows * 4;
+  L.sred = L.comb + 2 * kK2Rows * 4;
+  L.total = L.sred + 4 * nqb * 32 * 8;
   return L;
 }
 
@@ -50,9 +53,6 @@ struct DenseProblem {
   const T* Q;              // [units][G][w][128]
   int64_t kv_stride;       // elements between units of K and V
   int num_units, N, B, G, W;
-  int k1_chunks;           // ceil(N / kK1Keys)
-  int k2_blocks;           // ceil(N / kK2Rows)
-
   __device__ int n(int) const { return N; }
   __device__ int budget(int) const { return B; }
   __device__ const T* krow(int u, int t) const { return K + (int64_t)u * kv_stride + (int64_t)t * kD; }
@@ -61,32 +61,10 @@ struct DenseProblem {
   __device__ int64_t score_off(int u) const { return (int64_t)u * N; }
   __device__ int64_t kept_off(int u) const { return (int64_t)u * B; }
 
-  // importance work item -> (unit, chunk); partial-statistics slot
-  __device__ bool k1_item(int b, int& u, int& c) const {
-    u = b / k1_chunks;
-    c = b - u * k1_chunks;
-    return u < num_units;
-  }
-  __device__ int64_t k1_slot(int u, int c) const { return (int64_t)u * k1_chunks + c; }
-  __device__ int k1_nchunks(int) const { return k1_chunks; }
-
-  // redundancy work item -> (unit, row block). The blocks of one unit are
-  // placed on one XCD (workgroups go to XCDs round-robin by index), so the
-  // unit's keys are re-read from that XCD's L2; the longest block goes first.
-  __device__ bool k2_item(int b, int& u, int& blk) const {
-    const int x = b & 7;
-    const int k = b >> 3;
-    const int hl = k / k2_blocks;
-    const int ib = k - hl * k2_blocks;
-    u = hl * 8 + x;
-    blk = k2_blocks - 1 - ib;
-    return u < num_units;
-  }
-  __device__ bool unit_item(int b, int& u) const {
+  __device__ bool select_item(int b, int& u) const {
     u = b;
     return u < num_units;
   }
-  __device__ bool select_item(int b, int& u) const { return unit_item(b, u); }
 };
 
 template <typename T>

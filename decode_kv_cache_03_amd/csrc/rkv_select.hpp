@@ -1,0 +1,122 @@
+// Block-level selection and row gather, shared by the standalone selection
+// and compaction kernels and the fused per-unit kernel.
+//
+// Selection: keep the window (last w candidates) and the B-w candidates with
+// the largest Z among the other N-w, ties to the smaller index, output
+// ascending ("R-KV: decoding-time KV cache compression for reasoning models",
+// hysenlabs page, "What the redundancy scoring actually does at decode
+// time"; sourcepulse summary of R-KV, "How It Works").
+//
+// A radix select on the order-preserving 32-bit image of Z (four 8-bit digit
+// passes over an LDS histogram) finds the exact k-th largest key T and how
+// many keys equal to T are taken; one ordered pass with two block scans then
+// writes every candidate above T and the first `take` candidates equal to T,
+// in index order, followed by the window. No sort and no N-sized buffer.
+#pragma once
+
+#include "rkv_device.hpp"
+
+namespace rkv {
+
+// Shared scratch of select_block: 256 + 4 + 2 uint32.
+struct SelectScratch {
+  uint32_t hist[256];
+  uint32_t scan[4];
+  uint32_t digit, above;
+};
+
+// All 256 threads of the block call this with the same arguments. Requires
+// N > B > W. Writes kept[0..B).
+__device__ __forceinline__ void select_block(const float* __restrict__ z, int N, int B, int W,
+                                             int32_t* __restrict__ kept, SelectScratch& sh) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));   // keeps thread-derived values from being hoisted into callers' loops
+  const int cand = N - W;
+  const int k = B - W;
+  uint32_t prefix = 0, mask = 0, remaining = (uint32_t)k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    sh.hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < cand; i += 256) {
+      const uint32_t key = order_key(z[i]);
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    // thread t looks at digit 255-t; inclusive count of keys with digit >= 255-t
+    const uint32_t c = sh.hist[255 - tid];
+    uint32_t tot;
+    const uint32_t cum = block_inclusive_scan256(c, sh.scan, &tot);
+    if (cum >= remaining && cum - c < remaining) {
+      sh.digit = 255u - (uint32_t)tid;
+      sh.above = cum - c;
+    }
+    __syncthreads();
+    prefix |= sh.digit << shift;
+    mask |= 255u << shift;
+    remaining -= sh.above;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  const uint32_t take_eq = remaining;   // keys equal to T to keep, smallest indices first
+
+  const int per = (cand + 255) / 256;
+  const int lo = min(cand, tid * per), hi = min(cand, lo + per);
+  uint32_t gt = 0, eq = 0;
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t key = order_key(z[i]);
+    gt += key > T;
+    eq += key == T;
+  }
+  uint32_t tot;
+  const uint32_t eq_before = block_inclusive_scan256(eq, sh.scan, &tot) - eq;
+  const uint32_t take = (take_eq > eq_before) ? min(eq, take_eq - eq_before) : 0u;
+  const uint32_t cnt = gt + take;
+  uint32_t pos = block_inclusive_scan256(cnt, sh.scan, &tot) - cnt;
+  uint32_t taken = 0;
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t key = order_key(z[i]);
+    bool keep = key > T;
+    if (key == T && taken < take) {
+      keep = true;
+      ++taken;
+    }
+    if (keep) kept[pos++] = i;
+  }
+  for (int r = tid; r < W; r += 256) kept[k + r] = cand + r;
+}
+
+// Copy rows kept[0..nkeep) of two row sources into consecutive output rows, as
+// 16-byte chunks, eight chunks of each tensor in flight per thread.
+template <typename T, class SrcK, class SrcV>
+__device__ __forceinline__ void gather_rows_block(const int32_t* __restrict__ kept, int nkeep,
+                                                  SrcK srck, SrcV srcv, T* __restrict__ K_out,
+                                                  T* __restrict__ V_out) {
+  constexpr int RC = Elem<T>::kRowChunks;
+  const int total = nkeep * RC;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));   // keeps thread-derived values from being hoisted into callers' loops
+  for (int q0 = 0; q0 < total; q0 += 256 * 8) {
+    u32x4_t kv[8], vv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = q0 + j * 256 + tid;
+      if (q < total) {
+        const int r = q / RC, c = q % RC;
+        const int src = kept[r];
+        kv[j] = ld16(reinterpret_cast<const char*>(srck(src)) + 16 * c);
+        vv[j] = ld16(reinterpret_cast<const char*>(srcv(src)) + 16 * c);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = q0 + j * 256 + tid;
+      if (q < total) {
+        const int r = q / RC, c = q % RC;
+        st16(reinterpret_cast<char*>(K_out + (int64_t)r * kD) + 16 * c, kv[j]);
+        st16(reinterpret_cast<char*>(V_out + (int64_t)r * kD) + 16 * c, vv[j]);
+      }
+    }
+  }
+}
+
+}  // namespace rkv
