@@ -43,14 +43,16 @@ def kernel_work(name, units, n, b, g, w, esize=2):
     bytes: what the step must move at minimum (K read once for scoring, the
     window queries, the kept V rows read, K' and V' written, the indices);
     flops: the cosine contraction over unique pairs, N(N-1)*d per unit.
-    The fused kernel does both; its bound is the one whose time at peak is
-    longer.
+    The dense redundancy kernel also selects and gathers, so it carries both;
+    its bound is the one whose time at peak is longer.
     """
     d = 128
     row = d * esize
     nk = min(n, b)
     flops = units * n * (n - 1) * d
-    if name == "rkv_fused_step":
+    if name == "rkv_k2_compress":
+        # K is read again here after the statistics pass; counted once per
+        # kernel since each must fetch it
         nbytes = units * bytes_per_unit(n, b, g, w, esize)
         if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9):
             return "mfma", flops, "flop"
@@ -74,15 +76,25 @@ def bytes_per_unit(n, b, g, w, esize=2):
     return n * row + g * w * row + nk * row + 2 * nk * row + 4 * nk
 
 
-def source_hash(kernel_file):
-    p = os.path.join(ROOT, "decode_kv_cache_03_amd", "csrc", kernel_file)
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(files):
+    """Hash of the sources a kernel is compiled from (its .hip file and headers)."""
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "decode_kv_cache_03_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
-KERNEL_SOURCES = {"rkv_fused_step": "k2_redundancy.hip",
-                  "rkv_k2_redundancy": "k2_redundancy.hip", "rkv_k5_gather": "k5_compact.hip",
-                  "rkv_k1_stats": "k1_importance.hip", "rkv_k4_select": "k4_select.hip"}
+_HEADERS = ["rkv_device.hpp", "rkv_problem.hpp", "rkv_launch.hpp"]
+KERNEL_SOURCES = {
+    "rkv_k2_compress": ["k2_redundancy.hip", "rkv_select.hpp"] + _HEADERS,
+    "rkv_k2_redundancy": ["k2_redundancy.hip", "rkv_select.hpp"] + _HEADERS,
+    "rkv_k1_stats": ["k1_importance.hip"] + _HEADERS,
+    "rkv_k1_combine": ["k1_importance.hip"] + _HEADERS,
+    "rkv_k4_select": ["k4_select.hip", "rkv_select.hpp"] + _HEADERS,
+    "rkv_k5_gather": ["k5_compact.hip"] + _HEADERS,
+    "rkv_k5_paged_compact": ["k5_compact.hip"] + _HEADERS,
+}
 
 
 def measured_traffic(kernel, workload):
@@ -96,7 +108,7 @@ def measured_traffic(kernel, workload):
         e = data[workload][kernel]
     except (KeyError, ValueError, OSError):
         return None
-    if e.get("source_sha256_16") != source_hash(KERNEL_SOURCES.get(kernel, "")):
+    if kernel not in KERNEL_SOURCES or e.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
         return None
     return e.get("bytes_per_launch")
 
@@ -215,7 +227,7 @@ def main():
             v["tflops"] = amt / (v["avg_ms"] * 1e-3) / 1e12
         elif kb == "hbm":
             v["gbs"] = amt / (v["avg_ms"] * 1e-3) / 1e9
-        if k == "rkv_fused_step":   # the contraction it also carries
+        if k == "rkv_k2_compress":   # the contraction it also carries
             v["tflops"] = units * n * (n - 1) * 128 / (v["avg_ms"] * 1e-3) / 1e12
             v["mfma_frac"] = v["tflops"] / MFMA_BF16_PEAK_TFLOPS
 

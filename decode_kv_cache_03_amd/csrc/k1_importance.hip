@@ -146,12 +146,17 @@ __global__ __launch_bounds__(256) void k1_stats_kernel(P p, float* __restrict__ 
 
 // Per unit and query row: M = max over chunks, S = sum of the chunk sums
 // rescaled to M. Writes (M, 1/S), or (0, 0) for a row that sees no key.
+// Also clears the redundancy kernel's counters, if any: [8] item claims
+// (by workgroup 0), then one arrival counter per scored unit.
 template <int NQB, class P>
 __global__ __launch_bounds__(128) void k1_combine_kernel(P p, const float* __restrict__ part,
-                                                         float* __restrict__ fin, int num_units) {
+                                                         float* __restrict__ fin, int num_units,
+                                                         int32_t* __restrict__ counters) {
   const int u = blockIdx.x;
-  if (u >= num_units || p.n(u) <= p.budget(u)) return;   // unscored unit
   const int t = threadIdx.x;
+  if (counters != nullptr && u == 0 && t < 8) counters[t] = 0;
+  if (u >= num_units || p.n(u) <= p.budget(u)) return;   // unscored unit
+  if (counters != nullptr && t == 0) counters[8 + u] = 0;
   if (t >= NQB * 32) return;
   const int nc = p.k1_nchunks(u);
   const float2* pp = reinterpret_cast<const float2*>(part) + p.k1_slot(u, 0) * (NQB * 32) + t;
@@ -171,32 +176,34 @@ __global__ __launch_bounds__(128) void k1_combine_kernel(P p, const float* __res
 // ---------------------------------------------------------------------------
 template <typename T, int NQB, class P>
 static hipError_t run_k1_t(const P& p, int k1_items, int num_units, float* part, float* fin,
-                           float* rinv, int rpg_shift, hipStream_t st) {
+                           float* rinv, int32_t* counters, int rpg_shift, hipStream_t st) {
   hipError_t e = launch("rkv_k1_stats", k1_stats_kernel<T, NQB, P>, dim3(k1_items), dim3(256), 0, st,
                         p, part, rinv, rpg_shift);
   if (e != hipSuccess) return e;
   return launch("rkv_k1_combine", k1_combine_kernel<NQB, P>, dim3(num_units), dim3(128), 0, st, p,
-                (const float*)part, fin, num_units);
+                (const float*)part, fin, num_units, counters);
 }
 
 template <typename T, class P>
 hipError_t run_k1(const P& p, int nqb, int k1_items, int num_units, float* part, float* fin,
-                  float* rinv, int rpg_shift, hipStream_t st) {
+                  float* rinv, int32_t* counters, int rpg_shift, hipStream_t st) {
   // fp32 inputs are limited to two query blocks on the host (register budget)
   if constexpr (sizeof(T) == 4) {
-    if (nqb == 1) return run_k1_t<T, 1>(p, k1_items, num_units, part, fin, rinv, rpg_shift, st);
-    return run_k1_t<T, 2>(p, k1_items, num_units, part, fin, rinv, rpg_shift, st);
+    if (nqb == 1) return run_k1_t<T, 1>(p, k1_items, num_units, part, fin, rinv, counters, rpg_shift, st);
+    return run_k1_t<T, 2>(p, k1_items, num_units, part, fin, rinv, counters, rpg_shift, st);
   } else {
     switch (nqb) {
-      case 1: return run_k1_t<T, 1>(p, k1_items, num_units, part, fin, rinv, rpg_shift, st);
-      case 2: return run_k1_t<T, 2>(p, k1_items, num_units, part, fin, rinv, rpg_shift, st);
-      case 3: return run_k1_t<T, 3>(p, k1_items, num_units, part, fin, rinv, rpg_shift, st);
-      default: return run_k1_t<T, 4>(p, k1_items, num_units, part, fin, rinv, rpg_shift, st);
+      case 1: return run_k1_t<T, 1>(p, k1_items, num_units, part, fin, rinv, counters, rpg_shift, st);
+      case 2: return run_k1_t<T, 2>(p, k1_items, num_units, part, fin, rinv, counters, rpg_shift, st);
+      case 3: return run_k1_t<T, 3>(p, k1_items, num_units, part, fin, rinv, counters, rpg_shift, st);
+      default: return run_k1_t<T, 4>(p, k1_items, num_units, part, fin, rinv, counters, rpg_shift, st);
     }
   }
 }
 
-template hipError_t run_k1<bf16_bits, PagedProblem<bf16_bits>>(const PagedProblem<bf16_bits>&, int, int, int, float*, float*, float*, int, hipStream_t);
-template hipError_t run_k1<float, PagedProblem<float>>(const PagedProblem<float>&, int, int, int, float*, float*, float*, int, hipStream_t);
+template hipError_t run_k1<bf16_bits, DenseProblem<bf16_bits>>(const DenseProblem<bf16_bits>&, int, int, int, float*, float*, float*, int32_t*, int, hipStream_t);
+template hipError_t run_k1<float, DenseProblem<float>>(const DenseProblem<float>&, int, int, int, float*, float*, float*, int32_t*, int, hipStream_t);
+template hipError_t run_k1<bf16_bits, PagedProblem<bf16_bits>>(const PagedProblem<bf16_bits>&, int, int, int, float*, float*, float*, int32_t*, int, hipStream_t);
+template hipError_t run_k1<float, PagedProblem<float>>(const PagedProblem<float>&, int, int, int, float*, float*, float*, int32_t*, int, hipStream_t);
 
 }  // namespace rkv

@@ -1,5 +1,5 @@
-// Redundancy R, importance I and joint score Z; and the fused dense kernel
-// that runs the whole step per unit.
+// Redundancy R, importance I and joint score Z; for dense caches the same
+// kernel then selects and gathers each unit.
 //
 // Pages: redundancy is measured by the cosine similarity of key vectors and
 // serves to find and prune near-duplicates (sourcepulse summary of R-KV,
@@ -21,8 +21,8 @@
 // Nothing N x N is ever stored: each lane keeps running row maxima in
 // registers.
 //
-// Block = (unit, 128 rows). Column tiles of 128 keys are staged in LDS
-// (double-buffered, XOR-swizzled 16-byte chunks so fragment reads hit
+// Work item = (unit, block of 128 rows). Column tiles of 128 keys are staged
+// in LDS (double-buffered, XOR-swizzled 16-byte chunks so fragment reads hit
 // distinct banks). The 4 waves form a 2x2 grid over each 128x128 step: wave
 // (r, c) holds rows 64r..64r+63 of the block as MFMA A fragments in registers
 // and multiplies them by columns 64c..64c+63 of the tile, as 2x2 tiles of
@@ -36,24 +36,23 @@
 // the end the row maxima are reduced across lanes by a butterfly that halves
 // the values per lane at each exchange.
 //
-// Both kernels are persistent: about two workgroups per CU. The tile stream
-// never stops between blocks: during a block's last step the next block's
-// diagonal tile is already being loaded. Per-lane addresses are computed once
-// (tiles arrive by direct global->LDS loads from a uniform base plus a fixed
-// per-lane offset; fragment reads use fixed per-lane LDS offsets), since the
-// MFMA issue rate is the budget.
+// The kernel is persistent (about two workgroups per CU) and walks a list of
+// items; item k goes to workgroup k mod G with G a multiple of 8, so all
+// blocks of a unit run on one XCD and the unit's keys, re-read once per
+// block, stay in that XCD's L2 (one workgroup per unit would keep ~64 units
+// live per XCD, far more keys than its L2 holds). The tile stream never stops
+// between items: during an item's last step the next item's diagonal tile is
+// already being loaded. Per-lane addresses are computed once (tiles arrive by
+// direct global->LDS loads from a uniform base plus a fixed per-lane offset;
+// fragment reads use fixed per-lane LDS offsets), since the MFMA issue rate
+// is the budget.
 //
-//  * k2_items_kernel walks a list of (unit, block) items; item k goes to
-//    workgroup k mod G (G a multiple of 8, so all blocks of a unit run on one
-//    XCD and share its keys in that XCD's L2). Used for paged caches, whose
-//    ragged units are balanced by the host's longest-first list. Needs the
-//    softmax statistics and norms of a separate pass (k1_importance.hip).
-//  * k2_fused_kernel (dense caches) gives each workgroup whole units and runs
-//    the entire step for each: (S) stream the unit's keys once from memory
-//    for the softmax statistics and norms, (R) all blocks as above with the
-//    tiles re-read from cache, (T) select the kept indices, (G) gather the
-//    kept K/V rows. No state crosses workgroups, and with two workgroups per
-//    CU one's memory phases overlap the other's MFMA phase.
+// Dense caches: after its block's scores are written, each workgroup counts
+// the block in the unit's arrival counter; the one that completes the count
+// selects the unit's kept indices and gathers its kept K/V rows, so those
+// memory-bound phases overlap other workgroups' MFMA work and no workgroup
+// ever waits on another. Paged caches run selection and the in-place
+// compaction as separate launches (k4_select.hip, k5_compact.hip).
 #include "rkv_problem.hpp"
 #include "rkv_launch.hpp"
 #include "rkv_select.hpp"
@@ -275,7 +274,7 @@ struct Prefetch {
 
 // One block (unit u, rows blk*128..): on entry its diagonal tile is in flight
 // into buffer `cur`; on exit `cur` holds the prefetched tile, if any.
-template <typename T, int NQB, class P>
+template <typename T, int NQB, bool kAgentZ, class P>
 __device__ __forceinline__ void k2_block(const P& p, const K2Ctx<T>& x, int& cur, int u, int N,
                                          int blk, const float* __restrict__ rinv,
                                          const Prefetch& nx, const float* __restrict__ fin,
@@ -414,7 +413,12 @@ __device__ __forceinline__ void k2_block(const P& p, const K2Ctx<T>& x, int& cur
       const float R = (row == 0) ? 0.f : m * rinv[so + row];
       const float I = x.imp_l[x.tid];
       const float z = x.lam * I - (1.0f - x.lam) * R;
-      Z[so + row] = z + 0.0f;   // folds -0 onto +0
+      // + 0.0f folds -0 onto +0; Z read by another workgroup of this launch
+      // is stored coherently at agent scope
+      if constexpr (kAgentZ)
+        __hip_atomic_store(Z + so + row, z + 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        Z[so + row] = z + 0.0f;
       if (Rdbg != nullptr) Rdbg[so + row] = R;
       if (Idbg != nullptr) Idbg[so + row] = I;
     }
@@ -422,29 +426,73 @@ __device__ __forceinline__ void k2_block(const P& p, const K2Ctx<T>& x, int& cur
 }
 
 // ---------------------------------------------------------------------------
+// Finishing state of the dense path: the workgroup that completes a unit's
+// last block selects the unit's kept indices and gathers its kept rows.
+template <typename T>
+struct Finish {
+  int32_t* queue;      // [8] items claimed per XCD; cleared by the statistics pass
+  int32_t* arrive;     // [units] blocks completed; cleared by the statistics pass
+  int32_t* kept;       // [units][B]
+  T* K_out;
+  T* V_out;
+  int64_t out_stride;  // elements between units of K_out / V_out
+};
+
 // Persistent kernel over a list of (unit, block) items.
-template <typename T, int NQB, class P>
+//
+// Item order: the paged kernel walks the list statically (item k, k + G,
+// ... with G the grid size). The dense kernel, where a workgroup that
+// finishes a unit has extra work, claims items from a per-XCD counter
+// instead (item 8c + x for the c-th claim on XCD x = blockIdx & 7), so a busy
+// workgroup takes fewer items; a static walk would make it the last arrival
+// of every unit it touches and load it with all their finishes.
+template <typename T, int NQB, class P, bool kFinish>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_items_kernel(
     P p, int total_items, const float* __restrict__ rinv, const float* __restrict__ fin,
     float* __restrict__ Z, float* __restrict__ Rdbg, float* __restrict__ Idbg, float lam,
-    int rpg_shift) {
+    int rpg_shift, Finish<T> fs) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
+  const K2Lds plan = k2_lds_plan(K2Cfg<T>::RB, p.G * p.W, NQB);
   K2Ctx<T> x;
-  x.init(lds, k2_lds_plan(K2Cfg<T>::RB, p.G * p.W, NQB), rpg_shift, lam);
+  x.init(lds, plan, rpg_shift, lam);
+  SelectScratch& ssh = *reinterpret_cast<SelectScratch*>(lds + plan.sel);
+  int* const words = reinterpret_cast<int*>(lds + plan.sel + sizeof(SelectScratch));  // [3]
   const int stride = gridDim.x;
-  // next valid work item at or after k (in steps of the grid size)
-  auto next_item = [&](int k, int& u, int& blk) -> int {
+  const int xcd = blockIdx.x & 7;
+  // Item of claim c (dense) or the next valid item at or after k (paged);
+  // total_items when there is none.
+  auto claimed_item = [&](int c) -> int {
+    const int b = 8 * c + xcd;
+    int u, blk;
+    return (c < total_items && b < total_items && p.k2_item(b, u, blk)) ? b : total_items;
+  };
+  auto static_item = [&](int k) -> int {
+    int u, blk;
     for (; k < total_items; k += stride)
-      if (p.k2_item(k, u, blk)) {
-        u = __builtin_amdgcn_readfirstlane(u);
-        blk = __builtin_amdgcn_readfirstlane(blk);
-        return k;
-      }
+      if (p.k2_item(k, u, blk)) return k;
     return total_items;
   };
-  int u, blk;
-  int k = next_item(blockIdx.x, u, blk);
+  auto decode = [&](int k, int& u, int& blk) {
+    p.k2_item(k, u, blk);
+    u = __builtin_amdgcn_readfirstlane(u);
+    blk = __builtin_amdgcn_readfirstlane(blk);
+  };
+  int k, kn;
+  if constexpr (kFinish) {
+    if (x.tid == 0) {
+      words[0] = atomicAdd(fs.queue + xcd, 1);
+      words[1] = atomicAdd(fs.queue + xcd, 1);
+    }
+    __syncthreads();
+    k = claimed_item(words[0]);
+    kn = claimed_item(words[1]);
+  } else {
+    k = static_item(blockIdx.x);
+    kn = static_item(k + stride);
+  }
   if (k >= total_items) return;
+  int u, blk;
+  decode(k, u, blk);
   int N = p.n(u);
   tile_load<T>(p, x, u, N, blk * kK2Rows, 0, true);
   q_load<T>(p, x, u);
@@ -453,15 +501,59 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_items_kernel(
   while (true) {
     Prefetch nx;
     int un = 0, bn = 0;
-    const int kn = next_item(k + stride, un, bn);
     nx.valid = kn < total_items;
+    if (nx.valid) decode(kn, un, bn);
     nx.u = un;
     nx.n = nx.valid ? p.n(un) : 0;
     nx.first_row = bn * kK2Rows;
     nx.queries = un != u;   // the same unit keeps its queries and normalisers
-    k2_block<T, NQB>(p, x, cur, u, N, blk, rinv, nx, fin, Z, Rdbg, Idbg);
+    k2_block<T, NQB, kFinish>(p, x, cur, u, N, blk, rinv, nx, fin, Z, Rdbg, Idbg);
+    int k_after = total_items;
+    if constexpr (kFinish) {
+      // Count the block once its scores are stored. The workgroup that
+      // brings the count to the unit's number of blocks finishes the unit;
+      // nobody waits for anybody. Scores travel through agent-scope
+      // (coherent) stores and loads, whose completion s_waitcnt orders before
+      // the count, so no cache-wide release or acquire is needed: those
+      // would write back and invalidate the L2 that holds the keys.
+      // The same round trip claims the item after next.
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (x.tid == 0) {
+        words[2] = atomicAdd(fs.arrive + u, 1) == p.k2_team(u) - 1;
+        if (nx.valid) words[0] = atomicAdd(fs.queue + xcd, 1);
+      }
+      __syncthreads();
+      if (nx.valid) k_after = claimed_item(words[0]);
+      if (words[2]) {
+        // The unit's scores and kept indices are staged in the tile buffer
+        // that the prefetch left free, when they fit.
+        const int Bu = p.budget(u), cand = N - p.W;
+        const float* zu = Z + p.score_off(u);
+        int32_t* kept = fs.kept + p.kept_off(u);
+        char* freebuf = x.tiles + (cur ^ 1) * K2Cfg<T>::TILE_BYTES;
+        float* zs = reinterpret_cast<float*>(freebuf);
+        int32_t* ks = reinterpret_cast<int32_t*>(freebuf) + cand;
+        const bool staged = (int64_t)(cand + Bu) * 4 <= K2Cfg<T>::TILE_BYTES;
+        if (staged) {
+          stage_scores(zu, cand, zs);
+          __syncthreads();
+          select_block(zs, N, Bu, p.W, kept, ssh, ks);
+        } else {
+          select_block(zu, N, Bu, p.W, kept, ssh, nullptr, AgentLoad{});
+        }
+        __syncthreads();
+        const int uu = u;
+        gather_rows_block<T>(staged ? ks : kept, Bu, [&](int r) { return p.krow(uu, r); },
+                             [&](int r) { return p.vrow(uu, r); }, fs.K_out + (int64_t)u * fs.out_stride,
+                             fs.V_out + (int64_t)u * fs.out_stride);
+        __syncthreads();   // the staging buffer is a tile buffer again
+      }
+    } else {
+      k_after = static_item(kn + stride);
+    }
     if (!nx.valid) break;
-    k = kn;
+    kn = k_after;
     u = un;
     blk = bn;
     N = nx.n;
@@ -469,231 +561,53 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_items_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Fused dense kernel: whole units per workgroup.
-template <typename T, int NQB>
-__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_fused_kernel(
-    DenseProblem<T> p, float* __restrict__ rinv, float* __restrict__ Z, int32_t* __restrict__ kept_all,
-    T* __restrict__ K_out, T* __restrict__ V_out, int64_t out_stride, float* __restrict__ Rdbg,
-    float* __restrict__ Idbg, float lam, int rpg_shift) {
-  using C = K2Cfg<T>;
-  constexpr int NCH = C::NCH;
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  const K2Lds plan = k2_lds_plan(C::RB, p.G * p.W, NQB);
-  K2Ctx<T> x;
-  x.init(lds, plan, rpg_shift, lam);
-  float2* const sred = reinterpret_cast<float2*>(lds + plan.sred);   // [4][NQB*32]
-  SelectScratch& ssh = *reinterpret_cast<SelectScratch*>(x.tiles);   // tiles are idle in phase T
-  const int N = p.N, B = p.B;
-  const int nb = (N + kK2Rows - 1) / kK2Rows;
-  const int rpg_mask = (1 << rpg_shift) - 1;
-
-  for (int u = blockIdx.x; u < p.num_units; u += gridDim.x) {
-    const int64_t so = p.score_off(u);
-    int cur = 0;
-
-    // (S) softmax statistics and norms: stream the unit's keys once. Wave w
-    // takes keys 32w..32w+31 of each tile as the A operand of K x Q^T, so each
-    // lane owns one query column and keeps its running max / sum of exp.
-    q_load<T>(p, x, u);
-    tile_load<T>(p, x, u, N, 0, 0, nb == 1);
-    float mrun[NQB], srun[NQB];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      mrun[qb] = -INFINITY;
-      srun[qb] = 0.f;
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int t = 0; t < nb; ++t) {
-      // prefetch the next key tile, or block 0's diagonal tile (= tile 0)
-      if (t + 1 < nb)
-        tile_load<T>(p, x, u, N, (t + 1) * kK2Rows, cur ^ 1, t + 2 == nb);
-      else
-        tile_load<T>(p, x, u, N, 0, cur ^ 1, nb == 1);
-      const char* tb = x.tiles + cur * C::TILE_BYTES;
-      // lane-derived values are re-materialised per tile, so that nothing of
-      // this phase is hoisted out of the unit loop and held through phase R
-      int lane_v = x.lane;
-      asm volatile("" : "+v"(lane_v));
-      const int l32 = lane_v & 31, half = lane_v >> 5;
-      const int kl = x.wave * 32 + l32;                 // tile row of this lane's key
-      const int key = t * kK2Rows + kl;
-      u32x4_t kf[NCH];
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) kf[c] = ld16(tb + frag_offset<T>(kl, half * NCH + c));
-      float ss = 0.f;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) ss += sumsq_chunk<T>(kf[c]);
-      ss += __shfl_xor(ss, 32, 64);
-      if (half == 0 && key < N) rinv[so + key] = ss > 0.f ? __frsqrt_rn(ss) : 0.f;
-      const bool edge = (t + 1) * kK2Rows > N - p.W;    // tile holds padding or window keys
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const int m = qb * 32 + l32;                    // query column of this lane
-        const int g = m >> rpg_shift, r = m & rpg_mask;
-        const bool qok = g < p.G && r < p.W;
-        u32x4_t qf[NCH];
-        const int qn = qok ? g * p.W + r : 0;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c)
-          qf[c] = qok ? ld16(x.qlds + frag_offset<T>(qn, half * NCH + c)) : zero16();
-        f32x16_t acc = {};
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) mma_chunk<T>(acc, kf[c], qf[c]);   // C[key][query]
-        const int last = N - p.W + r;                   // last key visible to window query r
-        float lg[16];
-        float mt = -INFINITY;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kk = t * kK2Rows + x.wave * 32 + acc_row(v, lane_v);
-          lg[v] = acc[v] * kLogitScaleLog2;
-          if (edge || !qok) lg[v] = (qok && kk <= last) ? lg[v] : -INFINITY;
-          mt = fmaxf(mt, lg[v]);
-        }
-        const float mn = fmaxf(mrun[qb], mt);
-        if (mn != -INFINITY) {
-          float s = (mrun[qb] != -INFINITY) ? srun[qb] * fast_exp2(mrun[qb] - mn) : 0.f;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) s += fast_exp2(lg[v] - mn);
-          srun[qb] = s;
-          mrun[qb] = mn;
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      cur ^= 1;
-    }
-    // merge the statistics: the two halves of a wave, then the four waves
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const float m2 = __shfl_xor(mrun[qb], 32, 64);
-      const float s2 = __shfl_xor(srun[qb], 32, 64);
-      const float mm = fmaxf(mrun[qb], m2);
-      float st = 0.f;
-      if (mm != -INFINITY)
-        st = (mrun[qb] != -INFINITY ? srun[qb] * fast_exp2(mrun[qb] - mm) : 0.f) +
-             (m2 != -INFINITY ? s2 * fast_exp2(m2 - mm) : 0.f);
-      if (x.half == 0) sred[x.wave * NQB * 32 + qb * 32 + x.l32] = make_float2(mm, st);
-    }
-    __syncthreads();
-    if (x.tid < NQB * 32) {
-      float mm = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) mm = fmaxf(mm, sred[w * NQB * 32 + x.tid].x);
-      float st = 0.f;
-      if (mm != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float2 e = sred[w * NQB * 32 + x.tid];
-          if (e.x != -INFINITY) st += e.y * fast_exp2(e.x - mm);
-        }
-      }
-      x.slds[x.tid] = (mm != -INFINITY && st > 0.f) ? make_float2(mm, 1.0f / st) : make_float2(0.f, 0.f);
-    }
-    // (block 0's first barrier publishes the normalisers)
-
-    // (R) redundancy, importance and Z, block by block
-    for (int blk = 0; blk < nb; ++blk) {
-      Prefetch nx;
-      nx.valid = blk + 1 < nb;
-      nx.u = u;
-      nx.n = N;
-      nx.first_row = (blk + 1) * kK2Rows;
-      nx.queries = false;
-      k2_block<T, NQB>(p, x, cur, u, N, blk, rinv, nx, nullptr, Z, Rdbg, Idbg);
-    }
-    __syncthreads();
-
-    // (T) kept indices of the unit
-    int32_t* kept = kept_all + p.kept_off(u);
-    select_block(Z + so, N, B, p.W, kept, ssh);
-    __syncthreads();
-
-    // (G) kept K/V rows
-    gather_rows_block<T>(kept, B, [&](int r) { return p.krow(u, r); },
-                         [&](int r) { return p.vrow(u, r); }, K_out + (int64_t)u * out_stride,
-                         V_out + (int64_t)u * out_stride);
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------------------
-template <typename Kern>
-static hipError_t persistent_grid(Kern kern, int lds_bytes, int max_groups, int* grid) {
+template <typename T, int NQB, class P>
+static hipError_t run_k2_t(const P& p, int k2_items, const float* rinv, const float* fin, float* Z,
+                           float* dbg_R, float* dbg_I, float lam, int rpg_shift,
+                           const Finish<T>& fs, hipStream_t st) {
+  constexpr bool F = P::kFinishUnits;
+  const K2Lds plan = k2_lds_plan(Elem<T>::kRowBytes, p.G * p.W, NQB);
+  auto kern = k2_items_kernel<T, NQB, P, F>;
   const void* fn = reinterpret_cast<const void*>(kern);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, plan.total);
   int dev = 0, cus = 0, per_cu = 0;
   if (e == hipSuccess) e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, lds_bytes);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, plan.total);
   if (e != hipSuccess) return e;
-  int g = 8 * ((max(1, per_cu) * cus + 7) / 8);
-  *grid = min(g, max_groups);
-  return hipSuccess;
-}
-
-template <typename T, int NQB, class P>
-static hipError_t run_k2_t(const P& p, int k2_items, const float* rinv, const float* fin, float* Z,
-                           float* dbg_R, float* dbg_I, float lam, int rpg_shift, hipStream_t st) {
-  const K2Lds plan = k2_lds_plan(Elem<T>::kRowBytes, p.G * p.W, NQB);
-  auto kern = k2_items_kernel<T, NQB, P>;
-  int grid = 0;
-  hipError_t e = persistent_grid(kern, plan.total, 8 * ((k2_items + 7) / 8), &grid);
-  if (e != hipSuccess) return e;
-  return launch("rkv_k2_redundancy", kern, dim3(grid), dim3(256), plan.total, st, p, k2_items, rinv,
-                fin, Z, dbg_R, dbg_I, lam, rpg_shift);
-}
-
-template <typename T, int NQB>
-static hipError_t run_fused_t(const DenseProblem<T>& p, float* rinv, float* Z, int32_t* kept,
-                              T* K_out, T* V_out, int64_t out_stride, float* dbg_R, float* dbg_I,
-                              float lam, int rpg_shift, hipStream_t st) {
-  const K2Lds plan = k2_lds_plan(Elem<T>::kRowBytes, p.G * p.W, NQB);
-  auto kern = k2_fused_kernel<T, NQB>;
-  int grid = 0;
-  hipError_t e = persistent_grid(kern, plan.total, p.num_units, &grid);
-  if (e != hipSuccess) return e;
-  return launch("rkv_fused_step", kern, dim3(grid), dim3(256), plan.total, st, p, rinv, Z, kept,
-                K_out, V_out, out_stride, dbg_R, dbg_I, lam, rpg_shift);
+  // persistent grid: a multiple of 8 (one XCD per item, see k2_item), no
+  // larger than the work
+  const int grid = min(8 * ((max(1, per_cu) * cus + 7) / 8), 8 * ((k2_items + 7) / 8));
+  return launch(F ? "rkv_k2_compress" : "rkv_k2_redundancy", kern, dim3(grid), dim3(256),
+                plan.total, st, p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, fs);
 }
 
 template <typename T, class P>
 hipError_t run_k2(const P& p, int nqb, int k2_items, const float* rinv, const float* fin, float* Z,
-                  float* dbg_R, float* dbg_I, float lam, int rpg_shift, hipStream_t st) {
+                  float* dbg_R, float* dbg_I, float lam, int rpg_shift, int32_t* counters,
+                  int32_t* kept, T* K_out, T* V_out, int64_t out_stride, hipStream_t st) {
+  const Finish<T> fs{counters, counters ? counters + 8 : nullptr, kept, K_out, V_out, out_stride};
+  if (P::kFinishUnits && counters == nullptr) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 4) {
-    if (nqb == 1) return run_k2_t<T, 1>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, st);
-    return run_k2_t<T, 2>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, st);
+    if (nqb == 1) return run_k2_t<T, 1>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, fs, st);
+    return run_k2_t<T, 2>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, fs, st);
   } else {
     switch (nqb) {
-      case 1: return run_k2_t<T, 1>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, st);
-      case 2: return run_k2_t<T, 2>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, st);
-      case 3: return run_k2_t<T, 3>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, st);
-      default: return run_k2_t<T, 4>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, st);
+      case 1: return run_k2_t<T, 1>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, fs, st);
+      case 2: return run_k2_t<T, 2>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, fs, st);
+      case 3: return run_k2_t<T, 3>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, fs, st);
+      default: return run_k2_t<T, 4>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, fs, st);
     }
   }
 }
 
-template <typename T>
-hipError_t run_fused(const DenseProblem<T>& p, int nqb, float* rinv, float* Z, int32_t* kept,
-                     T* K_out, T* V_out, int64_t out_stride, float* dbg_R, float* dbg_I, float lam,
-                     int rpg_shift, hipStream_t st) {
-  if constexpr (sizeof(T) == 4) {
-    if (nqb == 1)
-      return run_fused_t<T, 1>(p, rinv, Z, kept, K_out, V_out, out_stride, dbg_R, dbg_I, lam, rpg_shift, st);
-    return run_fused_t<T, 2>(p, rinv, Z, kept, K_out, V_out, out_stride, dbg_R, dbg_I, lam, rpg_shift, st);
-  } else {
-    switch (nqb) {
-      case 1: return run_fused_t<T, 1>(p, rinv, Z, kept, K_out, V_out, out_stride, dbg_R, dbg_I, lam, rpg_shift, st);
-      case 2: return run_fused_t<T, 2>(p, rinv, Z, kept, K_out, V_out, out_stride, dbg_R, dbg_I, lam, rpg_shift, st);
-      case 3: return run_fused_t<T, 3>(p, rinv, Z, kept, K_out, V_out, out_stride, dbg_R, dbg_I, lam, rpg_shift, st);
-      default: return run_fused_t<T, 4>(p, rinv, Z, kept, K_out, V_out, out_stride, dbg_R, dbg_I, lam, rpg_shift, st);
-    }
-  }
-}
-
-template hipError_t run_k2<bf16_bits, PagedProblem<bf16_bits>>(const PagedProblem<bf16_bits>&, int, int, const float*, const float*, float*, float*, float*, float, int, hipStream_t);
-template hipError_t run_k2<float, PagedProblem<float>>(const PagedProblem<float>&, int, int, const float*, const float*, float*, float*, float*, float, int, hipStream_t);
-template hipError_t run_fused<bf16_bits>(const DenseProblem<bf16_bits>&, int, float*, float*, int32_t*, bf16_bits*, bf16_bits*, int64_t, float*, float*, float, int, hipStream_t);
-template hipError_t run_fused<float>(const DenseProblem<float>&, int, float*, float*, int32_t*, float*, float*, int64_t, float*, float*, float, int, hipStream_t);
+#define RKV_K2_INST(T, P)                                                                        \
+  template hipError_t run_k2<T, P>(const P&, int, int, const float*, const float*, float*, float*, \
+                                   float*, float, int, int32_t*, int32_t*, T*, T*, int64_t,       \
+                                   hipStream_t);
+RKV_K2_INST(bf16_bits, DenseProblem<bf16_bits>)
+RKV_K2_INST(float, DenseProblem<float>)
+RKV_K2_INST(bf16_bits, PagedProblem<bf16_bits>)
+RKV_K2_INST(float, PagedProblem<float>)
 
 }  // namespace rkv

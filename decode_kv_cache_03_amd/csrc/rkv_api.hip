@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -125,8 +126,11 @@ using rkv::PagedProblem;
 namespace {
 
 struct DenseLayout {
-  float* rinv;   // [units][N] 1/||k_t|| (0 for a zero key)
-  float* z;      // [units][N] joint scores when the caller does not ask for them
+  float* rinv;       // [units][N] 1/||k_t|| (0 for a zero key)
+  float* z;          // [units][N] joint scores when the caller does not ask for them
+  float* part;       // [units][chunks][NQB*32] per-chunk softmax (max, sum)
+  float* fin;        // [units][NQB*32] per query row (max, 1/sum)
+  int32_t* counters; // [8 + units] item claims per XCD, then blocks completed per unit
   size_t bytes;
 };
 
@@ -165,15 +169,24 @@ int check_dense_desc(const rkv_dense_desc* d) {
     return fail(RKV_EINVAL, "out_head_stride %lld is below budget*128", (long long)d->out_head_stride);
   if ((int64_t)d->num_heads * d->n_cand > (int64_t)1 << 40)
     return fail(RKV_EINVAL, "num_heads * n_cand too large");
+  if ((int64_t)(d->num_heads + 7) / 8 * 8 * ((d->n_cand + rkv::kK2Rows - 1) / rkv::kK2Rows) > INT32_MAX)
+    return fail(RKV_EINVAL, "num_heads * ceil(n_cand / 128) must stay below 2^31");
   return RKV_OK;
 }
+
+int nqb_of(int gqa, int window);
 
 DenseLayout dense_layout(const rkv_dense_desc* d, char* base) {
   Carve c{base};
   const size_t units = (size_t)d->num_heads, n = (size_t)d->n_cand;
+  const size_t nqb = (size_t)nqb_of(d->gqa_group, d->window);
+  const size_t chunks = (n + rkv::kK1Keys - 1) / rkv::kK1Keys;
   DenseLayout L;
   L.rinv = c.take<float>(units * n);
   L.z = c.take<float>(units * n);
+  L.part = c.take<float>(units * chunks * nqb * 32 * 2);
+  L.fin = c.take<float>(units * nqb * 32 * 2);
+  L.counters = c.take<int32_t>(8 + units);
   L.bytes = std::max<size_t>(c.used, kAlign);
   return L;
 }
@@ -197,14 +210,23 @@ int dense_run(const rkv_dense_desc* d, const void* K, const void* V, const void*
   p.B = d->budget;
   p.G = d->gqa_group;
   p.W = d->window;
+  p.k1_chunks = (d->n_cand + rkv::kK1Keys - 1) / rkv::kK1Keys;
+  p.k2_blocks = (d->n_cand + rkv::kK2Rows - 1) / rkv::kK2Rows;
   const int64_t out_stride = d->out_head_stride ? d->out_head_stride : (int64_t)d->budget * 128;
   const int units = d->num_heads;
   const int nkeep = std::min(d->n_cand, d->budget);
   hipError_t e;
   if (d->n_cand > d->budget) {
-    e = rkv::run_fused<T>(p, nqb_of(d->gqa_group, d->window), L.rinv, dbg_Z ? dbg_Z : L.z, kept,
-                          static_cast<T*>(K_out), static_cast<T*>(V_out), out_stride, dbg_R, dbg_I,
-                          d->mix_lambda, rows_per_group_shift(d->window), st);
+    float* z = dbg_Z ? dbg_Z : L.z;
+    const int rpg_shift = rows_per_group_shift(d->window);
+    const int nqb = nqb_of(d->gqa_group, d->window);
+    e = rkv::run_k1<T>(p, nqb, units * p.k1_chunks, units, L.part, L.fin, L.rinv, L.counters,
+                       rpg_shift, st);
+    if (e != hipSuccess) return hip_fail(e, "importance launch");
+    const int k2_items = 8 * ((units + 7) / 8) * p.k2_blocks;
+    e = rkv::run_k2<T>(p, nqb, k2_items, L.rinv, L.fin, z, dbg_R, dbg_I, d->mix_lambda, rpg_shift,
+                       L.counters, kept, static_cast<T*>(K_out), static_cast<T*>(V_out), out_stride,
+                       st);
     if (e != hipSuccess) return hip_fail(e, "compression launch");
     return RKV_OK;
   }
@@ -442,10 +464,11 @@ int paged_run(const rkv_paged_desc* d, void* Kp, void* Vp, int32_t* page_table, 
   hipError_t e;
   if (p.unit_count > 0) {
     const int rpg_shift = rows_per_group_shift(d->window);
-    e = rkv::run_k1<T>(p, P.nqb, p.k1_count, p.all_units, L.part, L.fin, L.rinv, rpg_shift, st);
+    e = rkv::run_k1<T>(p, P.nqb, p.k1_count, p.all_units, L.part, L.fin, L.rinv, nullptr,
+                       rpg_shift, st);
     if (e != hipSuccess) return hip_fail(e, "importance launch");
     e = rkv::run_k2<T>(p, P.nqb, p.k2_count, L.rinv, L.fin, z, nullptr, nullptr, d->mix_lambda,
-                       rpg_shift, st);
+                       rpg_shift, nullptr, nullptr, nullptr, nullptr, 0, st);
     if (e != hipSuccess) return hip_fail(e, "redundancy launch");
   }
   e = rkv::run_k4(p, p.all_units, z, kept, 0, st);

@@ -56,6 +56,10 @@ __device__ __forceinline__ u32x4_t zero16() {
   return z;
 }
 
+// Word 3 of a raw buffer resource on gfx950: 32-bit data format, no swizzle;
+// out-of-range accesses are dropped.
+constexpr int kBufferWord3 = 0x00020000;
+
 // 16 bytes per lane from global memory straight into LDS. The 64 lanes of the
 // wave fill 1 KiB of LDS at `lds_dst` in lane order (lane l -> bytes 16l..16l+15);
 // each lane's source address is free. Completion is tracked by vmcnt.

@@ -26,23 +26,22 @@ hipError_t launch(const char* name, void (*kern)(KArgs...), dim3 grid, dim3 bloc
 }
 
 // Softmax statistics of the window queries: rinv [units][N] and, per unit and
-// query row, (max, 1/sum) in fin; part is per-chunk scratch.
+// query row, (max, 1/sum) in fin; part is per-chunk scratch. When counters
+// is not null, also clears the redundancy kernel's counters: [8] per-XCD
+// item claims, then [units] block arrivals (those of scored units).
 template <typename T, class P>
 hipError_t run_k1(const P& p, int nqb, int k1_items, int num_units, float* part, float* fin,
-                  float* rinv, int rpg_shift, hipStream_t st);
+                  float* rinv, int32_t* counters, int rpg_shift, hipStream_t st);
 
 // Redundancy, importance and joint score: Z [units][N] (R, I when requested).
+// Dense caches (P::kFinishUnits): the last block of each unit to finish also
+// selects its kept indices and gathers its kept rows into K_out / V_out;
+// counters (as cleared by run_k1) must then be non-null. Paged caches ignore
+// the last five arguments.
 template <typename T, class P>
 hipError_t run_k2(const P& p, int nqb, int k2_items, const float* rinv, const float* fin, float* Z,
-                  float* dbg_R, float* dbg_I, float lam, int rpg_shift, hipStream_t st);
-
-// Dense caches, whole step in one persistent kernel: Z (and R, I when
-// requested) in Z/dbg_*, kept indices, and the kept K/V rows; rinv is
-// [units][N] scratch. Requires N > B.
-template <typename T>
-hipError_t run_fused(const DenseProblem<T>& p, int nqb, float* rinv, float* Z, int32_t* kept,
-                     T* K_out, T* V_out, int64_t out_stride, float* dbg_R, float* dbg_I, float lam,
-                     int rpg_shift, hipStream_t st);
+                  float* dbg_R, float* dbg_I, float lam, int rpg_shift, int32_t* counters,
+                  int32_t* kept, T* K_out, T* V_out, int64_t out_stride, hipStream_t st);
 
 // Selection: kept indices per unit (ascending), from Z.
 template <class P>

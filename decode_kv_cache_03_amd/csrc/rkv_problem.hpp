@@ -4,13 +4,13 @@
 // together. Two layouts are served by the same kernels through these
 // policies:
 //   Dense: unit u has rows K + u*kv_stride + t*128; all units share N and B.
-//          Served by the fused kernel, one unit per workgroup at a time.
 //   Paged: unit u = (s, hk) with s = u / H; row t of the unit lives in page
 //          page_table[s][t >> ps_shift] at slot t & (page_size-1); N and B
 //          are per sequence. Work items are listed by the host.
 #pragma once
 
 #include "rkv_device.hpp"
+#include "rkv_select.hpp"
 
 namespace rkv {
 
@@ -26,7 +26,7 @@ struct K2Lds {
   int stats;     // (max, 1/sum) per query row, NQB*32 float2
   int imp;       // importance of the block's 128 keys
   int comb;      // row maxima of the two column-group waves: [2][128] floats
-  int sred;      // per-wave softmax statistics of the fused kernel: [4][NQB*32] float2
+  int sel;       // selection scratch of the unit's last block, then 3 words
   int total;
 };
 
@@ -38,8 +38,8 @@ __host__ __device__ inline K2Lds k2_lds_plan(int row_bytes, int gw, int nqb) {
   L.stats = L.q + qkb * 1024;
   L.imp = L.stats + nqb * 32 * 8;
   L.comb = L.imp + kK2Rows * 4;
-  L.sred = L.comb + 2 * kK2Rows * 4;
-  L.total = L.sred + 4 * nqb * 32 * 8;
+  L.sel = L.comb + 2 * kK2Rows * 4;
+  L.total = L.sel + (int)((sizeof(SelectScratch) + 12 + 15) / 16 * 16);
   return L;
 }
 
@@ -48,11 +48,15 @@ constexpr int kLdsBytesPerCU = 160 * 1024;
 template <typename T>
 struct DenseProblem {
   static constexpr bool kRowsContiguous = true;   // rows of a unit are 128 elements apart
+  static constexpr bool kFinishUnits = true;      // the redundancy kernel also selects and gathers
   const T* K;
   const T* V;
   const T* Q;              // [units][G][w][128]
   int64_t kv_stride;       // elements between units of K and V
   int num_units, N, B, G, W;
+  int k1_chunks;           // ceil(N / kK1Keys)
+  int k2_blocks;           // ceil(N / kK2Rows)
+
   __device__ int n(int) const { return N; }
   __device__ int budget(int) const { return B; }
   __device__ const T* krow(int u, int t) const { return K + (int64_t)u * kv_stride + (int64_t)t * kD; }
@@ -61,6 +65,30 @@ struct DenseProblem {
   __device__ int64_t score_off(int u) const { return (int64_t)u * N; }
   __device__ int64_t kept_off(int u) const { return (int64_t)u * B; }
 
+  // importance work item -> (unit, chunk); partial-statistics slot
+  __device__ bool k1_item(int b, int& u, int& c) const {
+    u = b / k1_chunks;
+    c = b - u * k1_chunks;
+    return u < num_units;
+  }
+  __device__ int64_t k1_slot(int u, int c) const { return (int64_t)u * k1_chunks + c; }
+  __device__ int k1_nchunks(int) const { return k1_chunks; }
+
+  // redundancy work item -> (unit, row block). Workgroups go to the 8 XCDs
+  // round-robin by index and the persistent grid is a multiple of 8, so item
+  // b runs on XCD b & 7: all blocks of a unit share one XCD and its L2, and
+  // consecutive units of an XCD are worked on together by its workgroups.
+  // The longest block of a unit comes first.
+  __device__ bool k2_item(int b, int& u, int& blk) const {
+    const int x = b & 7;
+    const int k = b >> 3;
+    const int hl = k / k2_blocks;
+    const int ib = k - hl * k2_blocks;
+    u = hl * 8 + x;
+    blk = k2_blocks - 1 - ib;
+    return u < num_units;
+  }
+  __device__ int k2_team(int) const { return k2_blocks; }   // work items of a unit
   __device__ bool select_item(int b, int& u) const {
     u = b;
     return u < num_units;
@@ -70,6 +98,7 @@ struct DenseProblem {
 template <typename T>
 struct PagedProblem {
   static constexpr bool kRowsContiguous = false;
+  static constexpr bool kFinishUnits = false;     // selection and in-place compaction run after
   const T* Kp;
   const T* Vp;
   const T* Q;                // [S][H][G][w][128]
@@ -122,6 +151,7 @@ struct PagedProblem {
   }
   __device__ int64_t k1_slot(int u, int c) const { return k1_base[u] + c; }
   __device__ int k1_nchunks(int u) const { return (n(u) + kK1Keys - 1) / kK1Keys; }
+  __device__ int k2_team(int u) const { return (n(u) + kK2Rows - 1) / kK2Rows; }
   __device__ bool k2_item(int b, int& u, int& blk) const {
     if (b >= k2_count) return false;
     const int2 it = k2_list[b];

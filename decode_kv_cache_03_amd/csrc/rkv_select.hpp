@@ -1,5 +1,5 @@
 // Block-level selection and row gather, shared by the standalone selection
-// and compaction kernels and the fused per-unit kernel.
+// kernel and the redundancy kernel, which finishes dense units itself.
 //
 // Selection: keep the window (last w candidates) and the B-w candidates with
 // the largest Z among the other N-w, ties to the smaller index, output
@@ -25,10 +25,25 @@ struct SelectScratch {
   uint32_t digit, above;
 };
 
+// Reads of Z: plain loads, or agent-scope coherent loads for scores that
+// other workgroups of the same launch wrote with agent-scope stores.
+struct PlainLoad {
+  __device__ float operator()(const float* p) const { return *p; }
+};
+struct AgentLoad {
+  __device__ float operator()(const float* p) const {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+};
+
 // All 256 threads of the block call this with the same arguments. Requires
-// N > B > W. Writes kept[0..B).
+// N > B > W. Writes kept[0..B), and the same indices to kept_copy unless it
+// is null.
+template <class LoadZ = PlainLoad>
 __device__ __forceinline__ void select_block(const float* __restrict__ z, int N, int B, int W,
-                                             int32_t* __restrict__ kept, SelectScratch& sh) {
+                                             int32_t* __restrict__ kept, SelectScratch& sh,
+                                             int32_t* __restrict__ kept_copy = nullptr,
+                                             LoadZ ldz = LoadZ{}) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));   // keeps thread-derived values from being hoisted into callers' loops
   const int cand = N - W;
@@ -38,7 +53,7 @@ __device__ __forceinline__ void select_block(const float* __restrict__ z, int N,
     sh.hist[tid] = 0;
     __syncthreads();
     for (int i = tid; i < cand; i += 256) {
-      const uint32_t key = order_key(z[i]);
+      const uint32_t key = order_key(ldz(z + i));
       if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
@@ -63,7 +78,7 @@ __device__ __forceinline__ void select_block(const float* __restrict__ z, int N,
   const int lo = min(cand, tid * per), hi = min(cand, lo + per);
   uint32_t gt = 0, eq = 0;
   for (int i = lo; i < hi; ++i) {
-    const uint32_t key = order_key(z[i]);
+    const uint32_t key = order_key(ldz(z + i));
     gt += key > T;
     eq += key == T;
   }
@@ -74,47 +89,83 @@ __device__ __forceinline__ void select_block(const float* __restrict__ z, int N,
   uint32_t pos = block_inclusive_scan256(cnt, sh.scan, &tot) - cnt;
   uint32_t taken = 0;
   for (int i = lo; i < hi; ++i) {
-    const uint32_t key = order_key(z[i]);
+    const uint32_t key = order_key(ldz(z + i));
     bool keep = key > T;
     if (key == T && taken < take) {
       keep = true;
       ++taken;
     }
-    if (keep) kept[pos++] = i;
+    if (keep) {
+      kept[pos] = i;
+      if (kept_copy != nullptr) kept_copy[pos] = i;
+      ++pos;
+    }
   }
-  for (int r = tid; r < W; r += 256) kept[k + r] = cand + r;
+  for (int r = tid; r < W; r += 256) {
+    kept[k + r] = cand + r;
+    if (kept_copy != nullptr) kept_copy[k + r] = cand + r;
+  }
+}
+
+// zs[0..n) = z[0..n) through agent-scope coherent loads, 8 in flight per
+// thread (z written by other workgroups of the same launch; zs in LDS).
+__device__ __forceinline__ void stage_scores(const float* __restrict__ z, int n, float* zs) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const AgentLoad ld;
+  for (int i0 = 0; i0 < n; i0 += 256 * 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + j * 256 + tid;
+      v[j] = i < n ? ld(z + i) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + j * 256 + tid;
+      if (i < n) zs[i] = v[j];
+    }
+  }
 }
 
 // Copy rows kept[0..nkeep) of two row sources into consecutive output rows, as
-// 16-byte chunks, eight chunks of each tensor in flight per thread.
+// 16-byte chunks: per round each thread reads its row indices first, then
+// has U chunks of each tensor in flight, then stores them. Output chunk q
+// sits at byte 16q, so the stores are buffer stores with one per-thread
+// offset and a uniform per-chunk offset: no per-store address registers,
+// whose reuse would make each store wait for the one before.
 template <typename T, class SrcK, class SrcV>
 __device__ __forceinline__ void gather_rows_block(const int32_t* __restrict__ kept, int nkeep,
                                                   SrcK srck, SrcV srcv, T* __restrict__ K_out,
                                                   T* __restrict__ V_out) {
   constexpr int RC = Elem<T>::kRowChunks;
+  constexpr int U = 16;
   const int total = nkeep * RC;
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));   // keeps thread-derived values from being hoisted into callers' loops
-  for (int q0 = 0; q0 < total; q0 += 256 * 8) {
-    u32x4_t kv[8], vv[8];
+  const __amdgpu_buffer_rsrc_t ko = __builtin_amdgcn_make_buffer_rsrc(K_out, 0, total * 16, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vo = __builtin_amdgcn_make_buffer_rsrc(V_out, 0, total * 16, kBufferWord3);
+  for (int q0 = 0; q0 < total; q0 += 256 * U) {
+    // Branch-free: chunks past the end read row kept[0] again and their
+    // stores fall outside the buffer range, which drops them.
+    int src[U];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < U; ++j) {
       const int q = q0 + j * 256 + tid;
-      if (q < total) {
-        const int r = q / RC, c = q % RC;
-        const int src = kept[r];
-        kv[j] = ld16(reinterpret_cast<const char*>(srck(src)) + 16 * c);
-        vv[j] = ld16(reinterpret_cast<const char*>(srcv(src)) + 16 * c);
-      }
+      src[j] = kept[q < total ? q / RC : 0];
     }
+    u32x4_t kv[U], vv[U];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int q = q0 + j * 256 + tid;
-      if (q < total) {
-        const int r = q / RC, c = q % RC;
-        st16(reinterpret_cast<char*>(K_out + (int64_t)r * kD) + 16 * c, kv[j]);
-        st16(reinterpret_cast<char*>(V_out + (int64_t)r * kD) + 16 * c, vv[j]);
-      }
+    for (int j = 0; j < U; ++j) {
+      const int c = (q0 + j * 256 + tid) % RC;
+      kv[j] = ld16(reinterpret_cast<const char*>(srck(src[j])) + 16 * c);
+      vv[j] = ld16(reinterpret_cast<const char*>(srcv(src[j])) + 16 * c);
+    }
+    const int vofs = (q0 + tid) * 16;
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      __builtin_amdgcn_raw_buffer_store_b128(kv[j], ko, vofs, j * 256 * 16, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(vv[j], vo, vofs, j * 256 * 16, 0);
     }
   }
 }
