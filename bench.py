@@ -40,19 +40,17 @@ WORKLOADS = {
 def kernel_work(name, units, n, b, g, w, esize=2):
     """Algorithmic work of one launch of `name`: (bound, amount, unit).
 
-    bytes: what the step must move at minimum (K read once for scoring, the
-    window queries, the kept V rows read, K' and V' written, the indices);
-    flops: the cosine contraction over unique pairs, N(N-1)*d per unit.
-    The dense redundancy kernel also selects and gathers, so it carries both;
-    its bound is the one whose time at peak is longer.
+    bytes: K read once for scoring, the window queries, the kept K and V rows
+    read, K' and V' written, the indices; flops: the cosine contraction over
+    unique pairs, N(N-1)*d per unit. The dense redundancy kernel also selects
+    and gathers, so it carries both; its bound is the one whose time at peak
+    is longer. The statistics kernel is charged its own read of K and Q.
     """
     d = 128
     row = d * esize
     nk = min(n, b)
     flops = units * n * (n - 1) * d
     if name == "rkv_k2_compress":
-        # K is read again here after the statistics pass; counted once per
-        # kernel since each must fetch it
         nbytes = units * bytes_per_unit(n, b, g, w, esize)
         if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9):
             return "mfma", flops, "flop"
@@ -60,7 +58,7 @@ def kernel_work(name, units, n, b, g, w, esize=2):
     if name == "rkv_k2_redundancy":
         return "mfma", flops, "flop"
     if name == "rkv_k5_gather":
-        return "hbm", units * (3 * nk * row + 4 * nk), "byte"
+        return "hbm", units * (4 * nk * row + 4 * nk), "byte"
     if name == "rkv_k1_stats":
         return "hbm", units * (n * row + g * w * row), "byte"
     if name == "rkv_k4_select":
@@ -70,10 +68,10 @@ def kernel_work(name, units, n, b, g, w, esize=2):
 
 def bytes_per_unit(n, b, g, w, esize=2):
     """Algorithmic HBM bytes of the whole step per unit: K read once for
-    scoring, Q_win read, kept V rows read, K' and V' written, indices."""
+    scoring, Q_win read, kept K and V rows read, K' and V' written, indices."""
     row = 128 * esize
     nk = min(n, b)
-    return n * row + g * w * row + nk * row + 2 * nk * row + 4 * nk
+    return n * row + g * w * row + 2 * nk * row + 2 * nk * row + 4 * nk
 
 
 def source_hash(files):
