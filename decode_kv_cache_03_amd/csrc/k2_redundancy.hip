@@ -70,27 +70,6 @@ struct K2Cfg {
   static constexpr int PER = 16 / ROWS_PER_KB;            // tile loads per swizzle period
 };
 
-// Byte offset, inside a tile, of the slot holding chunk `chunk` of tile row n:
-// the slot at position pos holds global chunk pos ^ (n & 15) of the row.
-template <typename T>
-__device__ __forceinline__ int frag_offset(int n, int chunk) {
-  return n * Elem<T>::kRowBytes + ((chunk ^ (n & 15)) << 4);
-}
-
-// One butterfly exchange of the row-max reduction: lanes whose bit W is set
-// keep values W..2W-1 of the current range, the others keep 0..W-1; each
-// receives the half it keeps from the partner lane l ^ W.
-template <int W>
-__device__ __forceinline__ void max_butterfly_step(float (&val)[32], int lane) {
-  const bool upper = (lane & W) != 0;
-#pragma unroll
-  for (int i = 0; i < W; ++i) {
-    const float keep = upper ? val[i + W] : val[i];
-    const float send = upper ? val[i] : val[i + W];
-    val[i] = fmaxf(keep, __shfl_xor(send, W, 64));
-  }
-}
-
 // Per-workgroup context: LDS regions and per-lane constants.
 template <typename T>
 struct K2Ctx {
@@ -426,18 +405,7 @@ __device__ __forceinline__ void k2_block(const P& p, const K2Ctx<T>& x, int& cur
 }
 
 // ---------------------------------------------------------------------------
-// Finishing state of the dense path: the workgroup that completes a unit's
-// last block selects the unit's kept indices and gathers its kept rows.
-template <typename T>
-struct Finish {
-  int32_t* queue;      // [8] items claimed per XCD; cleared by the statistics pass
-  int32_t* arrive;     // [units] blocks completed; cleared by the statistics pass
-  int32_t* kept;       // [units][B]
-  T* K_out;
-  T* V_out;
-  int64_t out_stride;  // elements between units of K_out / V_out
-};
-
+// ---------------------------------------------------------------------------
 // Persistent kernel over a list of (unit, block) items.
 //
 // Item order: the paged kernel walks the list statically (item k, k + G,
@@ -536,15 +504,15 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_items_kernel(
         int32_t* ks = reinterpret_cast<int32_t*>(freebuf) + cand;
         const bool staged = (int64_t)(cand + Bu) * 4 <= K2Cfg<T>::TILE_BYTES;
         if (staged) {
-          stage_scores(zu, cand, zs);
+          stage_scores<256>(zu, cand, zs);
           __syncthreads();
-          select_block(zs, N, Bu, p.W, kept, ssh, ks);
+          select_block<256>(zs, N, Bu, p.W, kept, ssh, ks);
         } else {
-          select_block(zu, N, Bu, p.W, kept, ssh, nullptr, AgentLoad{});
+          select_block<256>(zu, N, Bu, p.W, kept, ssh, nullptr, AgentLoad{});
         }
         __syncthreads();
         const int uu = u;
-        gather_rows_block<T>(staged ? ks : kept, Bu, [&](int r) { return p.krow(uu, r); },
+        gather_rows_block<T, 256>(staged ? ks : kept, Bu, [&](int r) { return p.krow(uu, r); },
                              [&](int r) { return p.vrow(uu, r); }, fs.K_out + (int64_t)u * fs.out_stride,
                              fs.V_out + (int64_t)u * fs.out_stride);
         __syncthreads();   // the staging buffer is a tile buffer again

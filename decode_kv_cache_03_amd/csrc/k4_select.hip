@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void k4_select_kernel(P p, const float* __rest
       for (int r = N + tid; r < B; r += 256) kept[r] = -1;
     return;
   }
-  select_block(Z + p.score_off(u), N, B, p.W, kept, sh);
+  select_block<256>(Z + p.score_off(u), N, B, p.W, kept, sh);
 }
 
 template <class P>

@@ -223,10 +223,16 @@ int dense_run(const rkv_dense_desc* d, const void* K, const void* V, const void*
     e = rkv::run_k1<T>(p, nqb, units * p.k1_chunks, units, L.part, L.fin, L.rinv, L.counters,
                        rpg_shift, st);
     if (e != hipSuccess) return hip_fail(e, "importance launch");
-    const int k2_items = 8 * ((units + 7) / 8) * p.k2_blocks;
-    e = rkv::run_k2<T>(p, nqb, k2_items, L.rinv, L.fin, z, dbg_R, dbg_I, d->mix_lambda, rpg_shift,
-                       L.counters, kept, static_cast<T*>(K_out), static_cast<T*>(V_out), out_stride,
-                       st);
+    if constexpr (sizeof(T) == 2) {
+      e = rkv::run_k2_wide(p, nqb, L.rinv, L.fin, z, dbg_R, dbg_I, d->mix_lambda, rpg_shift,
+                           L.counters, kept, static_cast<T*>(K_out), static_cast<T*>(V_out),
+                           out_stride, st);
+    } else {
+      const int k2_items = 8 * ((units + 7) / 8) * p.k2_blocks;
+      e = rkv::run_k2<T>(p, nqb, k2_items, L.rinv, L.fin, z, dbg_R, dbg_I, d->mix_lambda,
+                         rpg_shift, L.counters, kept, static_cast<T*>(K_out),
+                         static_cast<T*>(V_out), out_stride, st);
+    }
     if (e != hipSuccess) return hip_fail(e, "compression launch");
     return RKV_OK;
   }

@@ -27,6 +27,7 @@ constexpr int kWave = 64;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 typedef uint16_t bf16_bits;    // storage type of a bfloat16 element
 
@@ -48,6 +49,13 @@ template <> struct Elem<float> {
 __device__ __forceinline__ u32x4_t ld16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
+// Streaming 16-byte load: non-temporal, for data read once.
+__device__ __forceinline__ u32x4_t ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+// Cache-policy bits of buffer instructions: non-temporal (streaming).
+constexpr int kCachePolicyStream = 2;
+
 __device__ __forceinline__ void st16(void* p, u32x4_t v) {
   *reinterpret_cast<u32x4_t*>(p) = v;
 }
@@ -116,10 +124,25 @@ __device__ __forceinline__ uint32_t order_key(float z) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Inclusive scan of one uint32 per thread over a 256-thread block.
-// `scratch` must hold 4 uint32 and be shared. Also returns the block total.
-__device__ __forceinline__ uint32_t block_inclusive_scan256(uint32_t v, uint32_t* scratch,
-                                                            uint32_t* total) {
+// Workgroup barrier for LDS written with ds_* instructions. __syncthreads()
+// (and even a workgroup fence limited to LDS) makes every wave first wait for
+// all of its loads in flight, direct global->LDS loads included (s_waitcnt
+// vmcnt(0)), which defeats loads issued ahead. Here each wave only completes
+// its own LDS instructions before the barrier; the memory clobber keeps the
+// compiler from moving memory accesses across it. Data that other waves bring
+// into LDS with direct global->LDS loads is visible after this barrier only if
+// each of them waited for those loads (s_waitcnt vmcnt) before reaching it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Inclusive scan of one uint32 per thread over a block of NT threads
+// (a multiple of 64, at most 1024). `scratch` must hold NT/64 uint32 and be
+// shared. Also returns the block total. All threads must call it.
+template <int NT>
+__device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t* scratch,
+                                                         uint32_t* total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -128,11 +151,41 @@ __device__ __forceinline__ uint32_t block_inclusive_scan256(uint32_t v, uint32_t
   }
   if (lane == 63) scratch[wave] = v;
   __syncthreads();
-  uint32_t w0 = scratch[0], w1 = scratch[1], w2 = scratch[2], w3 = scratch[3];
-  uint32_t before = (wave > 0 ? w0 : 0u) + (wave > 1 ? w1 : 0u) + (wave > 2 ? w2 : 0u);
-  *total = w0 + w1 + w2 + w3;
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t s = scratch[w];
+    before += w < wave ? s : 0u;
+    tot += s;
+  }
+  *total = tot;
   __syncthreads();
   return v + before;
+}
+
+// Byte offset, inside a swizzled LDS tile of 128-element rows, of the slot
+// holding 16-byte chunk `chunk` of row n: the slot at position pos holds
+// chunk pos ^ (n & 15) of the row, so the 16 rows that a fragment read
+// touches at one chunk position hit 16 different banks groups.
+template <typename T>
+__device__ __forceinline__ int frag_offset(int n, int chunk) {
+  return n * Elem<T>::kRowBytes + ((chunk ^ (n & 15)) << 4);
+}
+
+// One exchange of a butterfly max-reduction of 32 values per lane across the
+// 32 lanes of a half-wave: lanes whose bit W is set keep values W..2W-1 of
+// the current range, the others keep 0..W-1; each receives the half it keeps
+// from the partner lane l ^ W. After W = 16, 8, 4, 2, 1, lane l holds in
+// val[0] the max over all lanes of value l & 31.
+template <int W>
+__device__ __forceinline__ void max_butterfly_step(float (&val)[32], int lane) {
+  const bool upper = (lane & W) != 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    const float keep = upper ? val[i + W] : val[i];
+    const float send = upper ? val[i] : val[i + W];
+    val[i] = fmaxf(keep, __shfl_xor(send, W, 64));
+  }
 }
 
 }  // namespace rkv

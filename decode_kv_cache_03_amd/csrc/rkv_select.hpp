@@ -18,10 +18,10 @@
 
 namespace rkv {
 
-// Shared scratch of select_block: 256 + 4 + 2 uint32.
+// Shared scratch of select_block: 256 + 16 + 2 uint32.
 struct SelectScratch {
   uint32_t hist[256];
-  uint32_t scan[4];
+  uint32_t scan[16];   // one per wave, up to 1024 threads
   uint32_t digit, above;
 };
 
@@ -36,32 +36,33 @@ struct AgentLoad {
   }
 };
 
-// All 256 threads of the block call this with the same arguments. Requires
-// N > B > W. Writes kept[0..B), and the same indices to kept_copy unless it
-// is null.
-template <class LoadZ = PlainLoad>
+// All NT threads of the block (NT = 256 or 512) call this with the same
+// arguments. Requires N > B > W. Writes kept[0..B), and the same indices to
+// kept_copy unless it is null.
+template <int NT, class LoadZ = PlainLoad>
 __device__ __forceinline__ void select_block(const float* __restrict__ z, int N, int B, int W,
                                              int32_t* __restrict__ kept, SelectScratch& sh,
                                              int32_t* __restrict__ kept_copy = nullptr,
                                              LoadZ ldz = LoadZ{}) {
+  static_assert(NT >= 256 && NT % 64 == 0, "select_block needs at least 256 threads");
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));   // keeps thread-derived values from being hoisted into callers' loops
   const int cand = N - W;
   const int k = B - W;
   uint32_t prefix = 0, mask = 0, remaining = (uint32_t)k;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    sh.hist[tid] = 0;
+    if (tid < 256) sh.hist[tid] = 0;
     __syncthreads();
-    for (int i = tid; i < cand; i += 256) {
+    for (int i = tid; i < cand; i += NT) {
       const uint32_t key = order_key(ldz(z + i));
       if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
-    // thread t looks at digit 255-t; inclusive count of keys with digit >= 255-t
-    const uint32_t c = sh.hist[255 - tid];
+    // thread t < 256 looks at digit 255-t; inclusive count of keys with digit >= 255-t
+    const uint32_t c = tid < 256 ? sh.hist[255 - tid] : 0u;
     uint32_t tot;
-    const uint32_t cum = block_inclusive_scan256(c, sh.scan, &tot);
-    if (cum >= remaining && cum - c < remaining) {
+    const uint32_t cum = block_inclusive_scan<NT>(c, sh.scan, &tot);
+    if (tid < 256 && cum >= remaining && cum - c < remaining) {
       sh.digit = 255u - (uint32_t)tid;
       sh.above = cum - c;
     }
@@ -74,7 +75,7 @@ __device__ __forceinline__ void select_block(const float* __restrict__ z, int N,
   const uint32_t T = prefix;
   const uint32_t take_eq = remaining;   // keys equal to T to keep, smallest indices first
 
-  const int per = (cand + 255) / 256;
+  const int per = (cand + NT - 1) / NT;
   const int lo = min(cand, tid * per), hi = min(cand, lo + per);
   uint32_t gt = 0, eq = 0;
   for (int i = lo; i < hi; ++i) {
@@ -83,10 +84,10 @@ __device__ __forceinline__ void select_block(const float* __restrict__ z, int N,
     eq += key == T;
   }
   uint32_t tot;
-  const uint32_t eq_before = block_inclusive_scan256(eq, sh.scan, &tot) - eq;
+  const uint32_t eq_before = block_inclusive_scan<NT>(eq, sh.scan, &tot) - eq;
   const uint32_t take = (take_eq > eq_before) ? min(eq, take_eq - eq_before) : 0u;
   const uint32_t cnt = gt + take;
-  uint32_t pos = block_inclusive_scan256(cnt, sh.scan, &tot) - cnt;
+  uint32_t pos = block_inclusive_scan<NT>(cnt, sh.scan, &tot) - cnt;
   uint32_t taken = 0;
   for (int i = lo; i < hi; ++i) {
     const uint32_t key = order_key(ldz(z + i));
@@ -101,7 +102,7 @@ __device__ __forceinline__ void select_block(const float* __restrict__ z, int N,
       ++pos;
     }
   }
-  for (int r = tid; r < W; r += 256) {
+  for (int r = tid; r < W; r += NT) {
     kept[k + r] = cand + r;
     if (kept_copy != nullptr) kept_copy[k + r] = cand + r;
   }
@@ -109,20 +110,21 @@ __device__ __forceinline__ void select_block(const float* __restrict__ z, int N,
 
 // zs[0..n) = z[0..n) through agent-scope coherent loads, 8 in flight per
 // thread (z written by other workgroups of the same launch; zs in LDS).
+template <int NT>
 __device__ __forceinline__ void stage_scores(const float* __restrict__ z, int n, float* zs) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const AgentLoad ld;
-  for (int i0 = 0; i0 < n; i0 += 256 * 8) {
+  for (int i0 = 0; i0 < n; i0 += NT * 8) {
     float v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int i = i0 + j * 256 + tid;
+      const int i = i0 + j * NT + tid;
       v[j] = i < n ? ld(z + i) : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int i = i0 + j * 256 + tid;
+      const int i = i0 + j * NT + tid;
       if (i < n) zs[i] = v[j];
     }
   }
@@ -133,8 +135,11 @@ __device__ __forceinline__ void stage_scores(const float* __restrict__ z, int n,
 // has U chunks of each tensor in flight, then stores them. Output chunk q
 // sits at byte 16q, so the stores are buffer stores with one per-thread
 // offset and a uniform per-chunk offset: no per-store address registers,
-// whose reuse would make each store wait for the one before.
-template <typename T, class SrcK, class SrcV>
+// whose reuse would make each store wait for the one before. V rows and the
+// outputs are touched once, so they are loaded and stored as streaming
+// (non-temporal) accesses that do not displace cached keys; K rows are
+// usually still cached from scoring and are read normally.
+template <typename T, int NT, class SrcK, class SrcV>
 __device__ __forceinline__ void gather_rows_block(const int32_t* __restrict__ kept, int nkeep,
                                                   SrcK srck, SrcV srcv, T* __restrict__ K_out,
                                                   T* __restrict__ V_out) {
@@ -145,27 +150,27 @@ __device__ __forceinline__ void gather_rows_block(const int32_t* __restrict__ ke
   asm volatile("" : "+v"(tid));   // keeps thread-derived values from being hoisted into callers' loops
   const __amdgpu_buffer_rsrc_t ko = __builtin_amdgcn_make_buffer_rsrc(K_out, 0, total * 16, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vo = __builtin_amdgcn_make_buffer_rsrc(V_out, 0, total * 16, kBufferWord3);
-  for (int q0 = 0; q0 < total; q0 += 256 * U) {
+  for (int q0 = 0; q0 < total; q0 += NT * U) {
     // Branch-free: chunks past the end read row kept[0] again and their
     // stores fall outside the buffer range, which drops them.
     int src[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int q = q0 + j * 256 + tid;
+      const int q = q0 + j * NT + tid;
       src[j] = kept[q < total ? q / RC : 0];
     }
     u32x4_t kv[U], vv[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int c = (q0 + j * 256 + tid) % RC;
+      const int c = (q0 + j * NT + tid) % RC;
       kv[j] = ld16(reinterpret_cast<const char*>(srck(src[j])) + 16 * c);
-      vv[j] = ld16(reinterpret_cast<const char*>(srcv(src[j])) + 16 * c);
+      vv[j] = ld16_stream(reinterpret_cast<const char*>(srcv(src[j])) + 16 * c);
     }
     const int vofs = (q0 + tid) * 16;
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      __builtin_amdgcn_raw_buffer_store_b128(kv[j], ko, vofs, j * 256 * 16, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(vv[j], vo, vofs, j * 256 * 16, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(kv[j], ko, vofs, j * NT * 16, kCachePolicyStream);
+      __builtin_amdgcn_raw_buffer_store_b128(vv[j], vo, vofs, j * NT * 16, kCachePolicyStream);
     }
   }
 }
