@@ -217,22 +217,26 @@ int dense_run(const rkv_dense_desc* d, const void* K, const void* V, const void*
   const int nkeep = std::min(d->n_cand, d->budget);
   hipError_t e;
   if (d->n_cand > d->budget) {
-    float* z = dbg_Z ? dbg_Z : L.z;
     const int rpg_shift = rows_per_group_shift(d->window);
     const int nqb = nqb_of(d->gqa_group, d->window);
+    if constexpr (sizeof(T) == 2) {
+      if (rkv::fused_plan_choose(p.N, p.B, p.G * p.W, nqb).total > 0) {
+        e = rkv::run_k2_fused(p, nqb, dbg_Z, dbg_R, dbg_I, d->mix_lambda, rpg_shift, kept,
+                              static_cast<T*>(K_out), static_cast<T*>(V_out), out_stride, st);
+        if (e != hipSuccess) return hip_fail(e, "compression launch");
+        return RKV_OK;
+      }
+    }
+    // units too long for one workgroup's LDS, and fp32: statistics pass, then
+    // XCD-local teams of workgroups per unit
+    float* z = dbg_Z ? dbg_Z : L.z;
     e = rkv::run_k1<T>(p, nqb, units * p.k1_chunks, units, L.part, L.fin, L.rinv, L.counters,
                        rpg_shift, st);
     if (e != hipSuccess) return hip_fail(e, "importance launch");
-    if constexpr (sizeof(T) == 2) {
-      e = rkv::run_k2_wide(p, nqb, L.rinv, L.fin, z, dbg_R, dbg_I, d->mix_lambda, rpg_shift,
-                           L.counters, kept, static_cast<T*>(K_out), static_cast<T*>(V_out),
-                           out_stride, st);
-    } else {
-      const int k2_items = 8 * ((units + 7) / 8) * p.k2_blocks;
-      e = rkv::run_k2<T>(p, nqb, k2_items, L.rinv, L.fin, z, dbg_R, dbg_I, d->mix_lambda,
-                         rpg_shift, L.counters, kept, static_cast<T*>(K_out),
-                         static_cast<T*>(V_out), out_stride, st);
-    }
+    const int k2_items = 8 * ((units + 7) / 8) * p.k2_blocks;
+    e = rkv::run_k2<T>(p, nqb, k2_items, L.rinv, L.fin, z, dbg_R, dbg_I, d->mix_lambda, rpg_shift,
+                       L.counters, kept, static_cast<T*>(K_out), static_cast<T*>(V_out),
+                       out_stride, st);
     if (e != hipSuccess) return hip_fail(e, "compression launch");
     return RKV_OK;
   }

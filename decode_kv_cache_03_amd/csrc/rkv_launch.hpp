@@ -43,12 +43,12 @@ hipError_t run_k2(const P& p, int nqb, int k2_items, const float* rinv, const fl
                   float* dbg_R, float* dbg_I, float lam, int rpg_shift, int32_t* counters,
                   int32_t* kept, T* K_out, T* V_out, int64_t out_stride, hipStream_t st);
 
-// Dense bf16 caches: the same as run_k2 for DenseProblem, by the 8-wave
-// ring-buffered kernel (k2_wide.hip).
-hipError_t run_k2_wide(const DenseProblem<bf16_bits>& p, int nqb, const float* rinv,
-                       const float* fin, float* Z, float* dbg_R, float* dbg_I, float lam,
-                       int rpg_shift, int32_t* counters, int32_t* kept, bf16_bits* K_out,
-                       bf16_bits* V_out, int64_t out_stride, hipStream_t st);
+// Dense bf16 caches whose unit fits the fused kernel's LDS plan
+// (fused_plan_choose): the whole step in one launch (k2_wide.hip), no
+// workspace. dbg_* may be null.
+hipError_t run_k2_fused(const DenseProblem<bf16_bits>& p, int nqb, float* dbg_Z, float* dbg_R,
+                        float* dbg_I, float lam, int rpg_shift, int32_t* kept, bf16_bits* K_out,
+                        bf16_bits* V_out, int64_t out_stride, hipStream_t st);
 
 // Selection: kept indices per unit (ascending), from Z.
 template <class P>

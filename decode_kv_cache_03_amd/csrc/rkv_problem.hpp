@@ -45,47 +45,46 @@ __host__ __device__ inline K2Lds k2_lds_plan(int row_bytes, int gw, int nqb) {
 
 constexpr int kLdsBytesPerCU = 160 * 1024;
 
-// LDS plan of the 8-wave dense bf16 kernel (k2_wide.hip): a ring of `slots`
-// tile slots (a 128-row bf16 tile plus the 1/||k|| of its rows), two slots of
-// window queries and of softmax normalisers, the item's importance and
-// row-max exchange, selection scratch, and optionally the staging area of a
-// unit's scores and kept indices (stage_bytes = 0: selection reads global
-// memory instead).
-struct WidePlan {
-  int slots, q, qbytes, stats, imp, comb, sel, stage, stage_bytes, total;
+// LDS plan of the fused dense bf16 kernel (k2_wide.hip): a ring of `slots`
+// 128-row bf16 tiles, two slots of window queries, the unit's softmax
+// normalisers and their per-wave partials, the unit's 1/||k|| and Z, the
+// kept indices, a block's importance and row-max exchange, and selection
+// scratch.
+struct FusedPlan {
+  int slots, q, qbytes, stats, sred, rn, zs, ks, imp, comb, sel, total;
 };
 
-__host__ __device__ inline WidePlan wide_plan(int gw, int nqb, int slots, int stage_bytes) {
-  WidePlan L;
+__host__ __device__ inline int round16(int64_t x) { return (int)((x + 15) / 16 * 16); }
+
+__host__ __device__ inline FusedPlan fused_plan(int N, int B, int gw, int nqb, int slots) {
+  FusedPlan L;
   L.slots = slots;
-  L.q = slots * (128 * 256 + 512);
+  L.q = slots * 128 * 256;
   L.qbytes = (gw * 256 + 1023) / 1024 * 1024;
   L.stats = L.q + 2 * L.qbytes;
-  L.imp = L.stats + 2 * nqb * 32 * 8;
+  L.sred = L.stats + nqb * 32 * 8;
+  L.rn = L.sred + 4 * nqb * 32 * 8;
+  L.zs = L.rn + round16((int64_t)N * 4);
+  L.ks = L.zs + round16((int64_t)N * 4);
+  L.imp = L.ks + round16((int64_t)B * 4);
   L.comb = L.imp + 256 * 4;
   L.sel = L.comb + 2 * 256 * 4;
-  L.stage = L.sel + (int)((sizeof(SelectScratch) + 12 + 15) / 16 * 16);
-  L.stage_bytes = stage_bytes;
-  L.total = L.stage + stage_bytes;
+  L.total = L.sel + round16(sizeof(SelectScratch));
   return L;
 }
 
-// Deepest ring that fits, preferring to stage the selection in LDS; total = 0
-// if nothing fits. cand = N - w candidates, B kept.
-__host__ __device__ inline WidePlan wide_plan_choose(int gw, int nqb, int cand, int B) {
-  const int stage = (int)(((int64_t)(cand + B) * 4 + 15) / 16 * 16);
-  const int tries[6][2] = {{4, 1}, {3, 1}, {4, 0}, {3, 0}, {2, 1}, {2, 0}};
-  for (int i = 0; i < 6; ++i) {
-    const WidePlan L = wide_plan(gw, nqb, tries[i][0], tries[i][1] ? stage : 0);
+// Deepest ring that fits in a CU's LDS; total = 0 if none does (long units:
+// the item-list kernels serve them).
+__host__ __device__ inline FusedPlan fused_plan_choose(int N, int B, int gw, int nqb) {
+  for (int slots = 4; slots >= 2; --slots) {
+    const FusedPlan L = fused_plan(N, B, gw, nqb, slots);
     if (L.total <= kLdsBytesPerCU) return L;
   }
-  WidePlan none = wide_plan(gw, nqb, 2, 0);
+  FusedPlan none = fused_plan(N, B, gw, nqb, 2);
   none.total = 0;
   return none;
 }
 
-// Finishing state of the dense path: the workgroup that completes a unit's
-// last block selects the unit's kept indices and gathers its kept rows.
 template <typename T>
 struct Finish {
   int32_t* queue;      // [8] items claimed per XCD; cleared by the statistics pass
