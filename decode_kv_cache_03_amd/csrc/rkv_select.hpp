@@ -131,47 +131,58 @@ __device__ __forceinline__ void stage_scores(const float* __restrict__ z, int n,
 }
 
 // Copy rows kept[0..nkeep) of two row sources into consecutive output rows, as
-// 16-byte chunks: per round each thread reads its row indices first, then
-// has U chunks of each tensor in flight, then stores them. Output chunk q
-// sits at byte 16q, so the stores are buffer stores with one per-thread
-// offset and a uniform per-chunk offset: no per-store address registers,
-// whose reuse would make each store wait for the one before. V rows and the
-// outputs are touched once, so they are loaded and stored as streaming
-// (non-temporal) accesses that do not displace cached keys; K rows are
-// usually still cached from scoring and are read normally.
+// 16-byte chunks, in rounds of U chunks of each tensor per thread. Rounds are
+// software-pipelined two deep: the loads of round r+1 are in flight while
+// round r is stored. Output chunk q sits at byte 16q, so the stores are
+// buffer stores with one per-thread offset and a uniform per-chunk offset:
+// no per-store address registers, whose reuse would make each store wait for
+// the one before. V rows and the outputs are touched once, so they are loaded
+// and stored as streaming (non-temporal) accesses that do not displace cached
+// keys; K rows are usually still cached from scoring and are read normally.
+// Branch-free tails: chunks past the end read row kept[0] again and their
+// stores fall outside the buffer range, which drops them.
 template <typename T, int NT, class SrcK, class SrcV>
 __device__ __forceinline__ void gather_rows_block(const int32_t* __restrict__ kept, int nkeep,
                                                   SrcK srck, SrcV srcv, T* __restrict__ K_out,
                                                   T* __restrict__ V_out) {
   constexpr int RC = Elem<T>::kRowChunks;
-  constexpr int U = 16;
+  constexpr int U = 8;
+  constexpr int kRound = NT * U;   // chunks per round
   const int total = nkeep * RC;
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));   // keeps thread-derived values from being hoisted into callers' loops
   const __amdgpu_buffer_rsrc_t ko = __builtin_amdgcn_make_buffer_rsrc(K_out, 0, total * 16, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vo = __builtin_amdgcn_make_buffer_rsrc(V_out, 0, total * 16, kBufferWord3);
-  for (int q0 = 0; q0 < total; q0 += NT * U) {
-    // Branch-free: chunks past the end read row kept[0] again and their
-    // stores fall outside the buffer range, which drops them.
+  auto load_round = [&](int q0, u32x4_t (&kv)[U], u32x4_t (&vv)[U]) {
     int src[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int q = q0 + j * NT + tid;
       src[j] = kept[q < total ? q / RC : 0];
     }
-    u32x4_t kv[U], vv[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int c = (q0 + j * NT + tid) % RC;
       kv[j] = ld16(reinterpret_cast<const char*>(srck(src[j])) + 16 * c);
       vv[j] = ld16_stream(reinterpret_cast<const char*>(srcv(src[j])) + 16 * c);
     }
+  };
+  auto store_round = [&](int q0, const u32x4_t (&kv)[U], const u32x4_t (&vv)[U]) {
     const int vofs = (q0 + tid) * 16;
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       __builtin_amdgcn_raw_buffer_store_b128(kv[j], ko, vofs, j * NT * 16, kCachePolicyStream);
       __builtin_amdgcn_raw_buffer_store_b128(vv[j], vo, vofs, j * NT * 16, kCachePolicyStream);
     }
+  };
+  u32x4_t ka[U], va[U], kb[U], vb[U];
+  if (total > 0) load_round(0, ka, va);
+  for (int q0 = 0; q0 < total; q0 += 2 * kRound) {
+    if (q0 + kRound < total) load_round(q0 + kRound, kb, vb);
+    store_round(q0, ka, va);
+    if (q0 + kRound >= total) break;
+    if (q0 + 2 * kRound < total) load_round(q0 + 2 * kRound, ka, va);
+    store_round(q0 + kRound, kb, vb);
   }
 }
 

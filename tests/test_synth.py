@@ -53,3 +53,28 @@ def test_paged_host_layout():
 
 def test_configs_present():
     assert sorted(CONFIGS) == [0, 1, 2, 3, 4]
+
+
+def test_decode_stream_rows_are_counter_based():
+    """Rows of a step depend only on (seed, unit, step); copy steps equal the
+    source step's fresh key plus small noise."""
+    import torch
+    from synth.decode_gen import DecodeStream
+    s = DecodeStream(3, batch=2, layers=2, kv_heads=2, gqa=2, steps=300, coverage=0.4,
+                     max_back=64, dtype="f32", device="cpu")
+    k1, v1, q1 = s.rows(150)
+    k2, v2, q2 = s.rows(150)
+    assert torch.equal(k1, k2) and torch.equal(v1, v2) and torch.equal(q1, q2)
+    assert k1.shape == (8, 128) and q1.shape == (8, 2, 128)
+    lay = s.layouts
+    assert 0.39 <= (lay >= 0).mean() <= 0.41
+    seq, t = np.argwhere(lay >= 0)[0]
+    src = lay[seq, t]
+    assert 0 < t - src <= 64
+    kt = s.rows(int(t))[0][seq * 4:(seq + 1) * 4]
+    ks = s.rows(int(src))[0][seq * 4:(seq + 1) * 4]
+    diff = (kt - ks).numpy()
+    assert 0.005 < diff.std() < 0.05                       # sigma = 0.02 noise
+    fresh = np.argwhere(lay[seq] < 0)[:, 0]
+    a, b = s.rows(int(fresh[0]))[0], s.rows(int(fresh[1]))[0]
+    assert abs(float(a.std()) - 1.0) < 0.1 and abs(float(torch.corrcoef(torch.stack([a.flatten(), b.flatten()]))[0, 1])) < 0.1
