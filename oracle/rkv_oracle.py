@@ -46,6 +46,22 @@ reasoning in the design notes of the repository):
       slots 0..B_s-1 of its own sequence; pages p >= B_s/page_size of the
       sequence are freed in (sequence, page) ascending order and their page
       table entries become -1.
+
+Variants of those readings, selected by keyword arguments (defaults = R1-R8):
+  symmetric=True   R_i = max over every other candidate j != i of
+                   cos(k_i, k_j): the plain symmetric reading of R1, which
+                   scores both copies of a duplicate as redundant.
+  causal=False     every window query sees all N candidates (R3 without the
+                   in-window causal mask).
+  pool="mean"      I_j = mean over the G query heads of the per-head window
+                   mean (the ablation that replaces max pooling of GQA
+                   attention scores [P3 "Measured effects reported in the
+                   paper", last row]).
+  Head-shared selection (compress_shared): the heads that must evict one
+  token set, as the tensor-parallel ranks of a layer do after their
+  eviction-score all-reduce [P1 "What the redundancy scoring actually does
+  at decode time"], select on the SUM of their Z (an all-reduce's default
+  reduction); the window and the top B-w of that sum are kept by every head.
 """
 from __future__ import annotations
 
@@ -64,11 +80,12 @@ def key_norms(K) -> np.ndarray:
     return np.sqrt(np.sum(K * K, axis=1))
 
 
-def attention_probs(K, Q, window: int) -> np.ndarray:
+def attention_probs(K, Q, window: int, causal: bool = True) -> np.ndarray:
     """Softmax attention of the window queries over the N candidates (reading R3, R4).
 
     K [N, d]; Q [G, w, d] -> P [G, w, N], each row summing to 1 over the keys
-    it can see and 0 on the keys it cannot.
+    it can see and 0 on the keys it cannot. causal=False lets every window
+    query see all N keys.
     """
     K = _f64(K)
     Q = _f64(Q)
@@ -77,48 +94,57 @@ def attention_probs(K, Q, window: int) -> np.ndarray:
     assert w == window
     logits = (Q.reshape(g * w, d) @ K.T) / math.sqrt(d)          # [G*w, N]
     logits = logits.reshape(g, w, n)
-    # Window query r attends to keys 0 .. N-w+r (causal inside the window).
-    visible = np.arange(n)[None, :] <= (n - w + np.arange(w))[:, None]   # [w, N]
-    logits = np.where(visible[None], logits, -np.inf)
+    if causal:
+        # Window query r attends to keys 0 .. N-w+r (causal inside the window).
+        visible = np.arange(n)[None, :] <= (n - w + np.arange(w))[:, None]   # [w, N]
+        logits = np.where(visible[None], logits, -np.inf)
     m = logits.max(axis=2, keepdims=True)
     e = np.exp(logits - m)
     return e / e.sum(axis=2, keepdims=True)
 
 
-def importance(K, Q, window: int) -> np.ndarray:
-    """I_j = max over query heads g of the mean over window queries r of P[g, r, j]."""
-    P = attention_probs(K, Q, window)
-    return P.mean(axis=1).max(axis=0)
+def importance(K, Q, window: int, causal: bool = True, pool: str = "max") -> np.ndarray:
+    """I_j = max (or, pool="mean", mean) over query heads g of the mean over
+    window queries r of P[g, r, j]."""
+    per_head = attention_probs(K, Q, window, causal=causal).mean(axis=1)   # [G, N]
+    if pool == "max":
+        return per_head.max(axis=0)
+    if pool == "mean":
+        return per_head.mean(axis=0)
+    raise ValueError(f"unknown pooling {pool!r}")
 
 
-def redundancy(K) -> np.ndarray:
-    """R_i = max_{j<i} cos(k_i, k_j), R_0 = 0 (readings R1, R2)."""
-    K = _f64(K)
+def _cosines(K, norms, i, cols) -> np.ndarray:
+    """cos(k_i, k_j) for j in cols; 0 where a norm is 0 (reading R2)."""
+    dots = K[cols] @ K[i]
+    denom = norms[cols] * norms[i]
+    return np.divide(dots, denom, out=np.zeros(len(cols)), where=denom > 0)
+
+
+def _redundancy_of(K, norms, i: int, symmetric: bool) -> float:
     n = K.shape[0]
+    if symmetric:
+        cols = np.concatenate([np.arange(i), np.arange(i + 1, n)])
+    else:
+        cols = np.arange(i)
+    if len(cols) == 0:
+        return 0.0
+    return float(_cosines(K, norms, i, cols).max())
+
+
+def redundancy(K, symmetric: bool = False) -> np.ndarray:
+    """R_i = max_{j<i} cos(k_i, k_j), R_0 = 0 (readings R1, R2); with
+    symmetric=True, max over every j != i."""
+    K = _f64(K)
     norms = key_norms(K)
-    R = np.zeros(n)
-    for i in range(1, n):
-        dots = K[:i] @ K[i]
-        denom = norms[:i] * norms[i]
-        cos = np.divide(dots, denom, out=np.zeros(i), where=denom > 0)
-        R[i] = cos.max()
-    return R
+    return np.array([_redundancy_of(K, norms, i, symmetric) for i in range(K.shape[0])])
 
 
-def redundancy_rows(K, rows) -> np.ndarray:
+def redundancy_rows(K, rows, symmetric: bool = False) -> np.ndarray:
     """R_i for the listed rows only (same definition as :func:`redundancy`)."""
     K = _f64(K)
     norms = key_norms(K)
-    out = np.zeros(len(rows))
-    for k, i in enumerate(rows):
-        i = int(i)
-        if i == 0:
-            continue
-        dots = K[:i] @ K[i]
-        denom = norms[:i] * norms[i]
-        cos = np.divide(dots, denom, out=np.zeros(i), where=denom > 0)
-        out[k] = cos.max()
-    return out
+    return np.array([_redundancy_of(K, norms, int(i), symmetric) for i in rows])
 
 
 def joint_score(I, R, lam: float) -> np.ndarray:
@@ -141,11 +167,21 @@ def select(Z, n: int, budget: int, window: int) -> np.ndarray:
     return np.sort(np.concatenate([chosen, np.arange(cand, n)])).astype(np.int64)
 
 
-def compress_head(K, V, Q, budget: int, window: int, lam: float) -> dict:
+def scores_head(K, Q, window: int, lam: float, symmetric: bool = False, causal: bool = True,
+                pool: str = "max"):
+    """(I, R, Z) of one head under the chosen readings."""
+    I = importance(K, Q, window, causal=causal, pool=pool)
+    R = redundancy(K, symmetric=symmetric)
+    return I, R, joint_score(I, R, lam)
+
+
+def compress_head(K, V, Q, budget: int, window: int, lam: float, symmetric: bool = False,
+                  causal: bool = True, pool: str = "max") -> dict:
     """The whole step for one head: scores, selection and the compacted rows.
 
     K, V [N, d]; Q [G, w, d]. Returns dict(kept, K_out, V_out, I, R, Z), the
-    scores being None when N <= budget (nothing is scored).
+    scores being None when N <= budget (nothing is scored). The keyword
+    arguments select the reading variants listed in the module header.
     """
     K = np.asarray(K)
     V = np.asarray(V)
@@ -156,17 +192,41 @@ def compress_head(K, V, Q, budget: int, window: int, lam: float) -> dict:
         kept = np.arange(n, dtype=np.int64)
         return dict(kept=kept, K_out=K[kept].copy(), V_out=V[kept].copy(),
                     I=None, R=None, Z=None)
-    I = importance(K, Q, window)
-    R = redundancy(K)
-    Z = joint_score(I, R, lam)
+    if symmetric or not causal or pool != "max":
+        I, R, Z = scores_head(K, Q, window, lam, symmetric=symmetric, causal=causal, pool=pool)
+    else:
+        I = importance(K, Q, window)
+        R = redundancy(K)
+        Z = joint_score(I, R, lam)
     kept = select(Z, n, budget, window)
     return dict(kept=kept, K_out=K[kept].copy(), V_out=V[kept].copy(), I=I, R=R, Z=Z)
 
 
-def compress_dense(K, V, Q, budget: int, window: int, lam: float, heads=None) -> list:
+def compress_dense(K, V, Q, budget: int, window: int, lam: float, heads=None, **variant) -> list:
     """:func:`compress_head` over heads (all, or the listed ones). K [Bh, N, d]."""
     heads = range(K.shape[0]) if heads is None else heads
-    return [compress_head(K[h], V[h], Q[h], budget, window, lam) for h in heads]
+    return [compress_head(K[h], V[h], Q[h], budget, window, lam, **variant) for h in heads]
+
+
+def compress_shared(K, V, Q, budget: int, window: int, lam: float, **variant) -> dict:
+    """Head-shared selection over the H heads of one group (see the module
+    header): K, V [H, N, d]; Q [H, G, w, d]. Each head's Z is computed as in
+    :func:`compress_head`; the group selects once on Z_sum = sum over heads
+    of Z; every head keeps those indices. Returns dict(kept, K_out [H, B, d],
+    V_out, Z [H, N], Z_sum), scores None when N <= budget."""
+    K = np.asarray(K)
+    V = np.asarray(V)
+    H, n = K.shape[0], K.shape[1]
+    if budget <= window:
+        raise ValueError("budget must exceed window")
+    if n <= budget:
+        kept = np.arange(n, dtype=np.int64)
+        return dict(kept=kept, K_out=K[:, kept].copy(), V_out=V[:, kept].copy(), Z=None,
+                    Z_sum=None)
+    Z = np.stack([scores_head(K[h], Q[h], window, lam, **variant)[2] for h in range(H)])
+    Z_sum = Z.sum(axis=0)
+    kept = select(Z_sum, n, budget, window)
+    return dict(kept=kept, K_out=K[:, kept].copy(), V_out=V[:, kept].copy(), Z=Z, Z_sum=Z_sum)
 
 
 def logical_rows(pages, page_table_row, n: int, head: int, page_size: int) -> np.ndarray:

@@ -21,6 +21,20 @@ Pinned facts and where they come from:
   * structure: output size, window kept, ascending order, K'/V' = gather;
   * paged: page table and free list follow in closed form from lengths and
     budgets; live slots hold the kept rows; nothing else changes.
+
+Pins of the reading variants (symmetric redundancy, importance without the
+in-window causal mask, mean pooling over the GQA heads) and of head-shared
+selection:
+  * the brute force, which implements each variant by its own loops, agrees;
+  * symmetric: the 2-D example's values follow from the angles; both copies
+    of a planted duplicate reach 1; orthogonal keys give 0;
+  * unmasked: zero queries give exactly 1/N for every key; every softmax row
+    covers all N keys;
+  * pooling: with orthogonal unit keys, queries built from logarithms give
+    softmax rows equal to chosen distributions, so max and mean pooling have
+    closed forms;
+  * shared selection: exhaustive search over subsets of the summed scores;
+    heads that are copies of one head select what that head selects alone.
 """
 from __future__ import annotations
 
@@ -294,7 +308,122 @@ def check_paged(seed):
     assert np.array_equal(out["V_pages"][~live], case.V_pages[~live])
 
 
+VARIANTS = [dict(symmetric=True), dict(causal=False), dict(pool="mean"),
+            dict(symmetric=True, causal=False, pool="mean")]
+
+
+def check_bruteforce_variants(seed):
+    K, V, Q, b, w, lam = tiny_case(seed)
+    for var in VARIANTS:
+        o = orc.compress_head(K, V, Q, b, w, lam, **var)
+        r = bf.compress_head_bf(K.tolist(), V.tolist(), Q.tolist(), b, w, lam, **var)
+        _close(o["I"], r["I"])
+        _close(o["R"], r["R"])
+        _close(o["Z"], r["Z"])
+        assert list(o["kept"]) == list(r["kept"]), (var, list(o["kept"]), r["kept"])
+
+
+def check_symmetric_closed_forms(seed):
+    # the 2-D keys of check_hand_example: each key's largest cosine to any
+    # OTHER key, from the angles (k0 parallel to k4; k1 at 45 degrees to k2;
+    # k2 at 45 degrees to k0, k1, k4; k3 orthogonal to k1 and k5, opposite or
+    # obtuse to the rest; k5 orthogonal to k0, k3, k4)
+    K = np.array([[1.0, 0.0], [0.0, 2.0], [3.0, 3.0], [-1.0, 0.0], [2.0, 0.0], [0.0, -1.0]])
+    h = math.sqrt(0.5)
+    _close(orc.redundancy(K, symmetric=True), [1.0, h, h, 0.0, 1.0, 0.0], 1e-15)
+    # lam = 0: Z = -R_sym = [-1, -.71, -.71, 0, -1, 0]; window {5}; keep 3 of
+    # 0..4: 3, then 1 and 2 (tied, both kept)
+    Q = np.zeros((1, 1, 2))
+    assert list(orc.compress_head(K, K, Q, 4, 1, 0.0, symmetric=True)["kept"]) == [1, 2, 3, 5]
+    rng = _rng(seed)
+    # planted duplicate pairs: source and copy both reach cosine 1
+    n, d = 30, 16
+    K = rng.standard_normal((n, d))
+    pairs = [(2, 11), (5, 20), (7, 25)]
+    for a, c in pairs:
+        K[c] = float(rng.choice([0.5, 2.0])) * K[a]
+    R = orc.redundancy(K, symmetric=True)
+    for a, c in pairs:
+        assert abs(R[a] - 1.0) <= 1e-12 and abs(R[c] - 1.0) <= 1e-12, (R[a], R[c])
+    others = [i for i in range(n) if i not in {x for pr in pairs for x in pr}]
+    assert R[others].max() < 1.0 - 1e-6
+    # orthogonal keys: nothing is redundant under either reading
+    basis = np.eye(d)[rng.permutation(d)[:10]] * rng.uniform(0.5, 3.0, size=(10, 1))
+    assert np.array_equal(orc.redundancy(basis, symmetric=True), np.zeros(10))
+
+
+def check_unmasked_closed_forms(seed):
+    rng = _rng(seed)
+    n = int(rng.integers(5, 60))
+    w = int(rng.integers(1, min(8, n)))
+    g = int(rng.integers(1, 5))
+    d = 8
+    K = rng.standard_normal((n, d))
+    for pool in ("max", "mean"):
+        I = orc.importance(K, np.zeros((g, w, d)), w, causal=False, pool=pool)
+        _close(I, np.full(n, 1.0 / n), 1e-14)
+    P = orc.attention_probs(K, 2.0 * rng.standard_normal((g, w, d)), w, causal=False)
+    _close(P.sum(axis=2), np.ones((g, w)), 1e-13)
+    assert np.all(P > 0.0)
+    # a single key aligned with every window query: e^a / (e^a + N - 1) for
+    # every query, so also for the window mean
+    K = np.zeros((n, d))
+    K[:, 1:] = rng.standard_normal((n, d - 1))
+    K[0, 0] = 2.0
+    q = np.zeros((1, w, d))
+    q[0, :, 0] = 3.0
+    a = 6.0 / math.sqrt(d)
+    _close(orc.importance(K, q, w, causal=False)[0], math.exp(a) / (math.exp(a) + n - 1), 1e-14)
+
+
+def check_pooling_closed_forms(seed):
+    """Orthogonal unit keys e_pi(j) and queries whose pi(j)-th component is
+    sqrt(d) * log(a_j): the logits are log a_j, so each softmax row is
+    a / sum(a) exactly (up to exp/log rounding)."""
+    rng = _rng(seed)
+    d = 16
+    n = int(rng.integers(4, d + 1))
+    g = int(rng.integers(2, 5))
+    perm = rng.permutation(d)[:n]
+    K = np.eye(d)[perm]
+    A = rng.uniform(0.1, 5.0, size=(g, n))
+    Q = np.zeros((g, 1, d))
+    Q[:, 0, perm] = math.sqrt(d) * np.log(A)
+    P = A / A.sum(axis=1, keepdims=True)          # [g, n] per-head distributions
+    _close(orc.importance(K, Q, 1), P.max(axis=0), 1e-13)
+    _close(orc.importance(K, Q, 1, pool="mean"), P.mean(axis=0), 1e-13)
+    # identical heads pool alike under either rule
+    Qi = np.repeat(Q[:1], g, axis=0)
+    _close(orc.importance(K, Qi, 1, pool="mean"), orc.importance(K, Qi, 1), 1e-15)
+
+
+def check_shared(seed):
+    rng = _rng(seed)
+    H = int(rng.integers(2, 4))
+    K0, V0, Q0, b, w, lam = tiny_case(seed)
+    n, d = K0.shape
+    Ks = rng.standard_normal((H, n, d))
+    Ks[0] = K0
+    Vs = rng.standard_normal((H, n, d))
+    Qs = rng.standard_normal((H,) + Q0.shape)
+    for var in (dict(), VARIANTS[seed % len(VARIANTS)]):
+        o = orc.compress_shared(Ks, Vs, Qs, b, w, lam, **var)
+        r = bf.compress_shared_bf(Ks.tolist(), Vs.tolist(), Qs.tolist(), b, w, lam, **var)
+        assert list(o["kept"]) == r["kept"], (var, list(o["kept"]), r["kept"])
+        for h in range(H):
+            _close(o["Z"][h], r["Z"][h])
+            assert np.array_equal(o["K_out"][h], Ks[h][o["kept"]])
+            assert np.array_equal(o["V_out"][h], Vs[h][o["kept"]])
+    # copies of one head (2 or 4: the sum of equal values is exact) select
+    # what that head selects alone
+    for copies in (2, 4):
+        rep = lambda x: np.repeat(x[None], copies, axis=0)
+        o = orc.compress_shared(rep(K0), rep(V0), rep(Q0), b, w, lam)
+        assert list(o["kept"]) == list(orc.compress_head(K0, V0, Q0, b, w, lam)["kept"])
+
+
 ALL_CHECKS = [check_bruteforce, check_select_ties, check_lambda_one, check_lambda_zero,
               check_duplicates, check_orthogonal, check_scale_invariance, check_zero_queries,
               check_softmax_rows, check_identical_heads, check_logit_scale, check_hand_example, check_structure,
-              check_paged]
+              check_paged, check_bruteforce_variants, check_symmetric_closed_forms,
+              check_unmasked_closed_forms, check_pooling_closed_forms, check_shared]

@@ -15,6 +15,8 @@ from oracle import rkv_oracle as orc
 
 _orig_probs = orc.attention_probs
 _orig_red = orc.redundancy
+_orig_imp = orc.importance
+_orig_select = orc.select
 
 
 def _probs_variant(K, Q, window, mask_shift=0, scale_pow=0.5, causal=True, swap_r=False):
@@ -49,7 +51,23 @@ def _red_variant(K, mode):
             R[i] = (K[:i] @ K[i]).max() if i else 0.0
         elif mode == "symmetric":
             R[i] = np.delete(C[i], i).max()
+        elif mode == "all":
+            R[i] = C[i].max()
     return R
+
+
+def _shared_variant(K, V, Q, budget, window, lam, mode, **variant):
+    """Head-shared selection with a wrong reduction over heads."""
+    K = np.asarray(K)
+    V = np.asarray(V)
+    n = K.shape[1]
+    if n <= budget:
+        kept = np.arange(n)
+        return dict(kept=kept, K_out=K[:, kept], V_out=V[:, kept], Z=None, Z_sum=None)
+    Z = np.stack([orc.scores_head(K[h], Q[h], window, lam, **variant)[2] for h in range(K.shape[0])])
+    agg = {"first_head": Z[0], "max_over_heads": Z.max(axis=0), "min_over_heads": Z.min(axis=0)}[mode]
+    kept = _orig_select(agg, n, budget, window)
+    return dict(kept=kept, K_out=K[:, kept], V_out=V[:, kept], Z=Z, Z_sum=agg)
 
 
 def _select_variant(Z, n, budget, window, mode):
@@ -71,24 +89,41 @@ def _select_variant(Z, n, budget, window, mode):
 
 
 MUTANTS = {
-    "mean_pool_over_heads": ("importance", lambda K, Q, w: orc.attention_probs(K, Q, w).mean(1).mean(0)),
-    "sum_over_queries": ("importance", lambda K, Q, w: orc.attention_probs(K, Q, w).sum(1).max(0)),
-    "pool_order_swapped": ("importance", lambda K, Q, w: orc.attention_probs(K, Q, w).max(1).mean(0)),
-    "no_causal_mask": ("attention_probs", lambda K, Q, w: _probs_variant(K, Q, w, causal=False)),
-    "mask_off_by_one": ("attention_probs", lambda K, Q, w: _probs_variant(K, Q, w, mask_shift=1)),
-    "mask_reversed": ("attention_probs", lambda K, Q, w: _probs_variant(K, Q, w, swap_r=True)),
-    "scale_1_over_d": ("attention_probs", lambda K, Q, w: _probs_variant(K, Q, w, scale_pow=1.0)),
-    "no_scale": ("attention_probs", lambda K, Q, w: _probs_variant(K, Q, w, scale_pow=0.0)),
-    "red_includes_self": ("redundancy", lambda K: _red_variant(K, "self")),
-    "red_later_tokens": ("redundancy", lambda K: _red_variant(K, "later")),
-    "red_mean": ("redundancy", lambda K: _red_variant(K, "mean")),
-    "red_unnormalised": ("redundancy", lambda K: _red_variant(K, "unnormalised")),
-    "red_symmetric": ("redundancy", lambda K: _red_variant(K, "symmetric")),
+    "mean_pool_over_heads": ("importance", lambda K, Q, w, **kw: orc.attention_probs(K, Q, w).mean(1).mean(0)),
+    "sum_over_queries": ("importance", lambda K, Q, w, **kw: orc.attention_probs(K, Q, w).sum(1).max(0)),
+    "pool_order_swapped": ("importance", lambda K, Q, w, **kw: orc.attention_probs(K, Q, w).max(1).mean(0)),
+    "no_causal_mask": ("attention_probs", lambda K, Q, w, **kw: _probs_variant(K, Q, w, causal=False)),
+    "mask_off_by_one": ("attention_probs", lambda K, Q, w, **kw: _probs_variant(K, Q, w, mask_shift=1)),
+    "mask_reversed": ("attention_probs", lambda K, Q, w, **kw: _probs_variant(K, Q, w, swap_r=True)),
+    "scale_1_over_d": ("attention_probs", lambda K, Q, w, **kw: _probs_variant(K, Q, w, scale_pow=1.0)),
+    "no_scale": ("attention_probs", lambda K, Q, w, **kw: _probs_variant(K, Q, w, scale_pow=0.0)),
+    "red_includes_self": ("redundancy", lambda K, **kw: _red_variant(K, "self")),
+    "red_later_tokens": ("redundancy", lambda K, **kw: _red_variant(K, "later")),
+    "red_mean": ("redundancy", lambda K, **kw: _red_variant(K, "mean")),
+    "red_unnormalised": ("redundancy", lambda K, **kw: _red_variant(K, "unnormalised")),
+    "red_symmetric": ("redundancy", lambda K, **kw: _red_variant(K, "symmetric")),
     "z_sign_flipped": ("joint_score", lambda I, R, lam: lam * np.asarray(I) + (1 - lam) * np.asarray(R)),
     "z_weights_swapped": ("joint_score", lambda I, R, lam: (1 - lam) * np.asarray(I) - lam * np.asarray(R)),
     "window_not_protected": ("select", lambda Z, n, b, w: _select_variant(Z, n, b, w, "no_window")),
     "ties_to_larger_index": ("select", lambda Z, n, b, w: _select_variant(Z, n, b, w, "tie_high")),
     "keeps_lowest": ("select", lambda Z, n, b, w: _select_variant(Z, n, b, w, "lowest")),
+    # reading variants and head-shared selection
+    "symmetric_ignored": ("redundancy", lambda K, symmetric=False: _orig_red(K)),
+    "symmetric_includes_self": ("redundancy", lambda K, symmetric=False:
+                                _red_variant(K, "all") if symmetric else _orig_red(K)),
+    "symmetric_later_only": ("redundancy", lambda K, symmetric=False:
+                             _red_variant(K, "later") if symmetric else _orig_red(K)),
+    "unmasked_ignored": ("attention_probs", lambda K, Q, w, causal=True: _orig_probs(K, Q, w)),
+    "unmasked_off_by_one": ("attention_probs", lambda K, Q, w, causal=True:
+                            _orig_probs(K, Q, w) if causal else _probs_variant(K, Q, w, mask_shift=w - 2)),
+    "mean_pool_ignored": ("importance", lambda K, Q, w, causal=True, pool="max":
+                          _orig_imp(K, Q, w, causal=causal)),
+    "mean_pool_sums": ("importance", lambda K, Q, w, causal=True, pool="max":
+                       _orig_probs(K, Q, w, causal=causal).mean(1).sum(0) if pool == "mean"
+                       else _orig_imp(K, Q, w, causal=causal)),
+    "shared_first_head": ("compress_shared", lambda *a, **kw: _shared_variant(*a, mode="first_head", **kw)),
+    "shared_max_over_heads": ("compress_shared", lambda *a, **kw: _shared_variant(*a, mode="max_over_heads", **kw)),
+    "shared_min_over_heads": ("compress_shared", lambda *a, **kw: _shared_variant(*a, mode="min_over_heads", **kw)),
 }
 
 

@@ -49,6 +49,23 @@ def test_paged_closed_form(seed):
     pins.check_paged(seed)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_bruteforce_variants(seed):
+    pins.check_bruteforce_variants(seed)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_variant_closed_forms(seed):
+    pins.check_symmetric_closed_forms(seed)
+    pins.check_unmasked_closed_forms(seed)
+    pins.check_pooling_closed_forms(seed)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_shared_selection(seed):
+    pins.check_shared(seed)
+
+
 def test_budget_not_above_window_is_invalid():
     import numpy as np
     from oracle import rkv_oracle as orc
