@@ -7,7 +7,11 @@ and the stream. There is no CPU fallback: if the library is not built, or
 the tensors are not on a GPU, these functions raise.
 
 Keyword names follow the R-KV entry point described on the pages
-(``kv_budget``, ``window_size``, ``mix_lambda``).
+(``kv_budget``, ``window_size``, ``mix_lambda``). The reading variants are
+keyword flags: ``symmetric`` (R over every other candidate), ``causal``
+(False: every window query sees all candidates), ``pool`` ("max" or "mean"
+over the GQA heads), and ``select_group`` (head-shared selection over runs of
+that many consecutive units).
 """
 from __future__ import annotations
 
@@ -60,14 +64,26 @@ def _require_cuda(*ts):
             raise ValueError("tensors must be on a GPU (the library has no CPU path)")
 
 
-def dense_desc(num_heads, n_cand, gqa, window, budget, lam, dtype_code, kv_stride=0, out_stride=0):
+def variant_bits(symmetric: bool = False, causal: bool = True, pool: str = "max") -> int:
+    """RKV_VARIANT_* bits of the reading variants (0 = the default readings)."""
+    if pool not in ("max", "mean"):
+        raise ValueError(f"pool must be 'max' or 'mean' (got {pool!r})")
+    return ((_lib.RKV_VARIANT_SYMMETRIC if symmetric else 0)
+            | (0 if causal else _lib.RKV_VARIANT_NO_CAUSAL)
+            | (_lib.RKV_VARIANT_POOL_MEAN if pool == "mean" else 0))
+
+
+def dense_desc(num_heads, n_cand, gqa, window, budget, lam, dtype_code, kv_stride=0, out_stride=0,
+               variant=0, select_group=0):
     return _lib.DenseDesc(num_heads, n_cand, HEAD_DIM, gqa, window, budget, float(lam), dtype_code,
-                          kv_stride, out_stride)
+                          kv_stride, out_stride, variant, select_group)
 
 
-def workspace_size(num_heads, n_cand, gqa_group, window_size, kv_budget, dtype="bf16") -> int:
+def workspace_size(num_heads, n_cand, gqa_group, window_size, kv_budget, dtype="bf16",
+                   select_group: int = 0) -> int:
     code = _lib.RKV_BF16 if dtype in ("bf16", "bfloat16") else _lib.RKV_F32
-    d = dense_desc(num_heads, n_cand, gqa_group, window_size, kv_budget, 0.0, code)
+    d = dense_desc(num_heads, n_cand, gqa_group, window_size, kv_budget, 0.0, code,
+                   select_group=select_group)
     n = _lib.load().rkv_workspace_size(ctypes.byref(d))
     if n == 0:
         raise _lib.RkvError(_lib.RKV_EINVAL, _lib.last_error())
@@ -76,7 +92,8 @@ def workspace_size(num_heads, n_cand, gqa_group, window_size, kv_budget, dtype="
 
 def compress(K, V, Q_win, kv_budget: int, window_size: int = 8, mix_lambda: float = 0.1, *,
              K_out=None, V_out=None, kept_idx=None, debug: bool = False, workspace=None,
-             stream=None) -> CompressResult:
+             stream=None, symmetric: bool = False, causal: bool = True, pool: str = "max",
+             select_group: int = 1) -> CompressResult:
     """Compress every unit of a dense cache (out of place).
 
     K, V: [Bh, N, 128] (rows contiguous; the unit stride may exceed N*128, as
@@ -111,7 +128,8 @@ def compress(K, V, Q_win, kv_budget: int, window_size: int = 8, mix_lambda: floa
     dbg = [torch.empty((bh, n), dtype=torch.float32, device=dev) for _ in range(3)] if debug \
         else [None, None, None]
     d = dense_desc(bh, n, g, window_size, b, mix_lambda, _dtype_code(K),
-                   K.stride(0) if bh > 1 else 0, K_out.stride(0) if bh > 1 else 0)
+                   K.stride(0) if bh > 1 else 0, K_out.stride(0) if bh > 1 else 0,
+                   variant_bits(symmetric, causal, pool), int(select_group))
     lib = _lib.load()
     need = lib.rkv_workspace_size(ctypes.byref(d))
     if need == 0:
@@ -125,9 +143,9 @@ def compress(K, V, Q_win, kv_budget: int, window_size: int = 8, mix_lambda: floa
 
 
 def paged_desc(num_seqs, kv_heads, gqa, window, page_size, max_pages, num_pages, lam, dtype_code,
-               page_stride=0, head_stride=0, slot_stride=0):
+               page_stride=0, head_stride=0, slot_stride=0, variant=0):
     return _lib.PagedDesc(num_seqs, kv_heads, HEAD_DIM, gqa, window, page_size, max_pages, num_pages,
-                          float(lam), dtype_code, page_stride, head_stride, slot_stride)
+                          float(lam), dtype_code, page_stride, head_stride, slot_stride, variant)
 
 
 def _host_i32(x):
@@ -138,7 +156,8 @@ def _host_i32(x):
 
 def compress_paged(K_pages, V_pages, page_table, seq_len, budget, Q_win, free_list, free_count: int,
                    window_size: int = 8, mix_lambda: float = 0.1, *, kept_idx=None,
-                   debug: bool = False, workspace=None, stream=None) -> PagedResult:
+                   debug: bool = False, workspace=None, stream=None, symmetric: bool = False,
+                   causal: bool = True, pool: str = "max") -> PagedResult:
     """Compress a paged cache in place and return freed pages to ``free_list``.
 
     K_pages, V_pages: [P, H, page_size, 128] device tensors (any page/head/slot
@@ -167,7 +186,8 @@ def compress_paged(K_pages, V_pages, page_table, seq_len, budget, Q_win, free_li
     if len(sl) != S or len(bu) != S:
         raise ValueError("seq_len and budget need one entry per sequence")
     d = paged_desc(S, H, g, window_size, ps, int(page_table.shape[1]), P, mix_lambda,
-                   _dtype_code(K_pages), K_pages.stride(0), K_pages.stride(1), K_pages.stride(2))
+                   _dtype_code(K_pages), K_pages.stride(0), K_pages.stride(1), K_pages.stride(2),
+                   variant_bits(symmetric, causal, pool))
     lib = _lib.load()
     need = lib.rkv_paged_workspace_size(ctypes.byref(d), sl_p, bu_p)
     if need == 0:

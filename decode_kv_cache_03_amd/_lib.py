@@ -15,6 +15,9 @@ RKV_EUNSUPPORTED = -4
 RKV_EHIP = -5
 RKV_F32 = 0
 RKV_BF16 = 1
+RKV_VARIANT_SYMMETRIC = 1
+RKV_VARIANT_NO_CAUSAL = 2
+RKV_VARIANT_POOL_MEAN = 4
 
 STATUS_NAMES = {RKV_OK: "RKV_OK", RKV_EINVAL: "RKV_EINVAL", RKV_EWORKSPACE: "RKV_EWORKSPACE",
                 RKV_EFREELIST: "RKV_EFREELIST", RKV_EUNSUPPORTED: "RKV_EUNSUPPORTED",
@@ -29,7 +32,8 @@ class DenseDesc(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("gqa_group", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("budget", ctypes.c_int32),
                 ("mix_lambda", ctypes.c_float), ("dtype", ctypes.c_int32),
-                ("kv_head_stride", ctypes.c_int64), ("out_head_stride", ctypes.c_int64)]
+                ("kv_head_stride", ctypes.c_int64), ("out_head_stride", ctypes.c_int64),
+                ("variant", ctypes.c_uint32), ("select_group", ctypes.c_int32)]
 
 
 class PagedDesc(ctypes.Structure):
@@ -39,7 +43,7 @@ class PagedDesc(ctypes.Structure):
                 ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
                 ("mix_lambda", ctypes.c_float), ("dtype", ctypes.c_int32),
                 ("page_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
-                ("slot_stride", ctypes.c_int64)]
+                ("slot_stride", ctypes.c_int64), ("variant", ctypes.c_uint32)]
 
 
 class RkvError(RuntimeError):

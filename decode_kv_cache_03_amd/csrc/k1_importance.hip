@@ -7,7 +7,9 @@
 // Reasoning Models", atlas.scime.ai summary, "Approach"), and GQA attention
 // is pooled by max, mean pooling being the weaker ablation (same summary,
 // "Measured effects reported in the paper", last row). Window query r sees
-// candidates j <= N-w+r; logits are q.k/sqrt(128).
+// candidates j <= N-w+r; logits are q.k/sqrt(128). Variants: without the
+// causal window every query sees all N candidates; mean instead of max over
+// the GQA heads (the pooling ablation of the same section).
 //
 // This file holds the first two launches; the weights themselves are formed
 // in the redundancy kernel (k2_redundancy.hip), which already holds every key
@@ -89,7 +91,8 @@ __global__ __launch_bounds__(256) void k1_stats_kernel(P p, float* __restrict__ 
       const int m = qb * 32 + (lane & 31);
       const int r = m & rpg_mask;
       const bool qvalid = (m >> rpg_shift) < p.G && r < p.W;
-      const int last = N - p.W + r;    // last key visible to window query r
+      // last key visible to window query r (all keys without the causal window)
+      const int last = p.causal() ? N - p.W + r : N - 1;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int kk = kbase + acc_row(v, lane);

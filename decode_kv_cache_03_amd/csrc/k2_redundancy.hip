@@ -12,7 +12,9 @@
 // Importance is the window queries' softmax attention, mean over a head's
 // queries, max over the GQA group (atlas.scime.ai summary, "Approach" and
 // "Measured effects reported in the paper"). The joint score is
-// Z = lambda*I - (1-lambda)*R (same summary, "Approach").
+// Z = lambda*I - (1-lambda)*R (same summary, "Approach"). Variants: the
+// symmetric R (max over every j != i; each block then sweeps every column
+// tile), no causal window, mean pooling over the GQA heads.
 //
 // The cosine matrix is the one dense contraction of the step (N x N x 128
 // per unit), so it runs on bf16 MFMA with fp32 accumulation on the raw keys
@@ -201,6 +203,7 @@ __device__ __forceinline__ float block_importance(const P& p, const K2Ctx<T>& x,
   const int rpg_mask = (1 << x.rpg_shift) - 1;
   const int octets_per_group = (1 << x.rpg_shift) >> 3;
   const float inv_w = 1.0f / (float)p.W;
+  const bool mean = p.pool_mean();
   float best = 0.f, run = 0.f;
   int lane_v = x.lane;   // re-materialised per call: keeps per-lane masks out of loop preheaders
   asm volatile("" : "+v"(lane_v));
@@ -235,12 +238,12 @@ __device__ __forceinline__ float block_importance(const P& p, const K2Ctx<T>& x,
       run += os;
       const int o = qb * 4 + t;
       if (((o + 1) & (octets_per_group - 1)) == 0) {
-        if (o / octets_per_group < p.G) best = fmaxf(best, run * inv_w);
+        if (o / octets_per_group < p.G) best = mean ? best + run * inv_w : fmaxf(best, run * inv_w);
         run = 0.f;
       }
     }
   }
-  return best;
+  return mean ? best / (float)p.G : best;
 }
 
 // What a block loads during its last step: the next block's diagonal tile,
@@ -253,7 +256,7 @@ struct Prefetch {
 
 // One block (unit u, rows blk*128..): on entry its diagonal tile is in flight
 // into buffer `cur`; on exit `cur` holds the prefetched tile, if any.
-template <typename T, int NQB, bool kAgentZ, class P>
+template <typename T, int NQB, bool kAgentZ, bool kSym, class P>
 __device__ __forceinline__ void k2_block(const P& p, const K2Ctx<T>& x, int& cur, int u, int N,
                                          int blk, const float* __restrict__ rinv,
                                          const Prefetch& nx, const float* __restrict__ fin,
@@ -287,18 +290,27 @@ __device__ __forceinline__ void k2_block(const P& p, const K2Ctx<T>& x, int& cur
   // 2. importance of the block's keys; wave (r, c) takes keys r*64 + c*32 + l32
   if (wave_live) {
     const int key = row0 + x.wc * 32 + x.l32;
-    const bool causal = base + kK2Rows > N - p.W;   // block reaches the window's keys
+    const bool causal = p.causal() && base + kK2Rows > N - p.W;   // block reaches the window's keys
     const float best = (x.wc == 0) ? block_importance<T, NQB>(p, x, af[0], key, N, causal)
                                    : block_importance<T, NQB>(p, x, af[1], key, N, causal);
     if (x.half == 0) x.imp_l[x.wr * 64 + x.wc * 32 + x.l32] = best;
   }
   __syncthreads();   // queries are no longer read: a prefetch may replace them
 
-  // 3. prefetch: tile 0 of this block, or what follows the block
-  if (blk > 0)
-    tile_load<T>(p, x, u, N, 0, cur ^ 1, false);
-  else
+  // column tiles other than the diagonal one: 0..blk-1, and for the
+  // symmetric R also blk+1..nb-1 (the last of which may hold rows past N)
+  constexpr bool sym = kSym;
+  const int nb = (N + kK2Cols - 1) / kK2Cols;
+  const int ncol = sym ? nb - 1 : blk;
+  auto col_tile = [&](int J) { return J < blk ? J : J + 1; };
+
+  // 3. prefetch: the first column tile, or what follows the block
+  if (ncol > 0) {
+    const int t = col_tile(0);
+    tile_load<T>(p, x, u, N, t * kK2Cols, cur ^ 1, (t + 1) * kK2Cols > N);
+  } else {
     prefetch_next();
+  }
 
   float mx[2][16];
 #pragma unroll
@@ -306,59 +318,83 @@ __device__ __forceinline__ void k2_block(const P& p, const K2Ctx<T>& x, int& cur
 #pragma unroll
     for (int v = 0; v < 16; ++v) mx[rb][v] = -INFINITY;
 
-  // 4. diagonal step: wave (0,1) lies above the diagonal, (1,0) below it;
-  // (0,0) and (1,1) straddle it and mask per element (j < i)
-  if (wave_live && x.wc <= x.wr) {
+  // Columns past N (in the unit's last tile) meet rows past N, masked pairs,
+  // or, for the symmetric R, rows below N: there they are masked too.
+  auto masked_update = [&](const f32x16_t (&acc)[2][2], const float (&rc)[2], int col0, bool diag) {
+    int lane_v = x.lane;   // re-materialised (see block_importance)
+    asm volatile("" : "+v"(lane_v));
+    const int l = lane_v & 31;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const bool col_ok = col0 + cb * 32 + l < N;
+        if (!sym && diag && cb > rb) continue;   // wholly above the diagonal
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          // on the diagonal, row rb*32 + a and column cb*32 + b are the same
+          // 64 keys: j < i iff rb > cb, or rb == cb and a > b; j != i iff not
+          // (rb == cb and a == b)
+          const int a = acc_row(v, lane_v);
+          const bool pair_ok = !diag || (sym ? (rb != cb || a != l) : (rb > cb || a > l));
+          if (col_ok && pair_ok) mx[rb][v] = fmaxf(mx[rb][v], acc[rb][cb][v] * rc[cb]);
+        }
+      }
+  };
+
+  // 4. diagonal step: wave (0,1) lies above the diagonal (needed only for
+  // the symmetric R), (1,0) below it; (0,0) and (1,1) straddle it and mask
+  // per element
+  if (wave_live && (sym || x.wc <= x.wr)) {
     f32x16_t acc[2][2];
     tile_mma<T>(x.tiles + cur * C::TILE_BYTES, x, af, acc);
     float rc[2];
+    const int col0 = base + x.wc * 64 + x.l32;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int col = base + x.wc * 64 + cb * 32 + x.l32;
-      rc[cb] = col < N ? rinv[so + col] : 0.f;
-    }
-    if (x.wc < x.wr) {
+    for (int cb = 0; cb < 2; ++cb) rc[cb] = col0 + cb * 32 < N ? rinv[so + col0 + cb * 32] : 0.f;
+    if (x.wc != x.wr && base + kK2Cols <= N) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
           mx[rb][v] = fmaxf(mx[rb][v], fmaxf(acc[rb][0][v] * rc[0], acc[rb][1][v] * rc[1]));
     } else {
-      // rows and columns are the same 64 keys: row rb*32 + a follows column
-      // cb*32 + b iff rb > cb, or rb == cb and a > b
-      int lane_v = x.lane;   // re-materialised (see block_importance)
-      asm volatile("" : "+v"(lane_v));
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int cb = 0; cb <= rb; ++cb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const bool ok = (rb > cb) || (acc_row(v, lane_v) > (lane_v & 31));
-            if (ok) mx[rb][v] = fmaxf(mx[rb][v], acc[rb][cb][v] * rc[cb]);
-          }
+      masked_update(acc, rc, col0 - x.l32, x.wc == x.wr);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   cur ^= 1;
 
-  // 5. tiles 0..blk-1, wholly left of the diagonal; tile J is in buffer cur
+  // 5. the other column tiles: 0..blk-1 lie wholly left of the diagonal;
+  // tile col_tile(J) is in buffer cur
   const float* rcol = rinv + so + x.wc * 64 + x.l32;
-  for (int J = 0; J < blk; ++J) {
-    if (J + 1 < blk)
-      tile_load<T>(p, x, u, N, (J + 1) * kK2Cols, cur ^ 1, false);
-    else
+  for (int J = 0; J < ncol; ++J) {
+    if (J + 1 < ncol) {
+      const int tn = col_tile(J + 1);
+      tile_load<T>(p, x, u, N, tn * kK2Cols, cur ^ 1, (tn + 1) * kK2Cols > N);
+    } else {
       prefetch_next();
+    }
     if (wave_live) {
+      const int t = col_tile(J);
       f32x16_t acc[2][2];
       tile_mma<T>(x.tiles + cur * C::TILE_BYTES, x, af, acc);
-      const float r0 = rcol[J * kK2Cols], r1 = rcol[J * kK2Cols + 32];
+      if ((t + 1) * kK2Cols <= N) {
+        const float r0 = rcol[t * kK2Cols], r1 = rcol[t * kK2Cols + 32];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          mx[rb][v] = fmaxf(mx[rb][v], fmaxf(acc[rb][0][v] * r0, acc[rb][1][v] * r1));
+          for (int v = 0; v < 16; ++v)
+            mx[rb][v] = fmaxf(mx[rb][v], fmaxf(acc[rb][0][v] * r0, acc[rb][1][v] * r1));
+      } else {   // the unit's last, partial tile (symmetric R only)
+        const int col0 = t * kK2Cols + x.wc * 64;
+        float rc[2];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          rc[cb] = col0 + cb * 32 + x.l32 < N ? rinv[so + col0 + cb * 32 + x.l32] : 0.f;
+        masked_update(acc, rc, col0, false);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -389,7 +425,7 @@ __device__ __forceinline__ void k2_block(const P& p, const K2Ctx<T>& x, int& cur
     const int row = base + x.tid;
     if (row < N) {
       const float m = fmaxf(x.comb[x.tid], x.comb[kK2Rows + x.tid]);
-      const float R = (row == 0) ? 0.f : m * rinv[so + row];
+      const float R = (row == 0 && !sym) ? 0.f : m * rinv[so + row];
       const float I = x.imp_l[x.tid];
       const float z = x.lam * I - (1.0f - x.lam) * R;
       // + 0.0f folds -0 onto +0; Z read by another workgroup of this launch
@@ -414,7 +450,7 @@ __device__ __forceinline__ void k2_block(const P& p, const K2Ctx<T>& x, int& cur
 // instead (item 8c + x for the c-th claim on XCD x = blockIdx & 7), so a busy
 // workgroup takes fewer items; a static walk would make it the last arrival
 // of every unit it touches and load it with all their finishes.
-template <typename T, int NQB, class P, bool kFinish>
+template <typename T, int NQB, class P, bool kFinish, bool kSym>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_items_kernel(
     P p, int total_items, const float* __restrict__ rinv, const float* __restrict__ fin,
     float* __restrict__ Z, float* __restrict__ Rdbg, float* __restrict__ Idbg, float lam,
@@ -475,7 +511,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_items_kernel(
     nx.n = nx.valid ? p.n(un) : 0;
     nx.first_row = bn * kK2Rows;
     nx.queries = un != u;   // the same unit keeps its queries and normalisers
-    k2_block<T, NQB, kFinish>(p, x, cur, u, N, blk, rinv, nx, fin, Z, Rdbg, Idbg);
+    k2_block<T, NQB, kFinish, kSym>(p, x, cur, u, N, blk, rinv, nx, fin, Z, Rdbg, Idbg);
     int k_after = total_items;
     if constexpr (kFinish) {
       // Count the block once its scores are stored. The workgroup that
@@ -493,7 +529,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_items_kernel(
       }
       __syncthreads();
       if (nx.valid) k_after = claimed_item(words[0]);
-      if (words[2]) {
+      if (words[2] && fs.select_units) {
         // The unit's scores and kept indices are staged in the tile buffer
         // that the prefetch left free, when they fit.
         const int Bu = p.budget(u), cand = N - p.W;
@@ -535,7 +571,7 @@ static hipError_t run_k2_t(const P& p, int k2_items, const float* rinv, const fl
                            const Finish<T>& fs, hipStream_t st) {
   constexpr bool F = P::kFinishUnits;
   const K2Lds plan = k2_lds_plan(Elem<T>::kRowBytes, p.G * p.W, NQB);
-  auto kern = k2_items_kernel<T, NQB, P, F>;
+  auto kern = p.symmetric() ? k2_items_kernel<T, NQB, P, F, true> : k2_items_kernel<T, NQB, P, F, false>;
   const void* fn = reinterpret_cast<const void*>(kern);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, plan.total);
   int dev = 0, cus = 0, per_cu = 0;
@@ -553,8 +589,10 @@ static hipError_t run_k2_t(const P& p, int k2_items, const float* rinv, const fl
 template <typename T, class P>
 hipError_t run_k2(const P& p, int nqb, int k2_items, const float* rinv, const float* fin, float* Z,
                   float* dbg_R, float* dbg_I, float lam, int rpg_shift, int32_t* counters,
-                  int32_t* kept, T* K_out, T* V_out, int64_t out_stride, hipStream_t st) {
-  const Finish<T> fs{counters, counters ? counters + 8 : nullptr, kept, K_out, V_out, out_stride};
+                  int32_t* kept, T* K_out, T* V_out, int64_t out_stride, int select_units,
+                  hipStream_t st) {
+  const Finish<T> fs{counters, counters ? counters + 8 : nullptr, kept, K_out, V_out, out_stride,
+                     select_units};
   if (P::kFinishUnits && counters == nullptr) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 4) {
     if (nqb == 1) return run_k2_t<T, 1>(p, k2_items, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, fs, st);
@@ -571,7 +609,7 @@ hipError_t run_k2(const P& p, int nqb, int k2_items, const float* rinv, const fl
 
 #define RKV_K2_INST(T, P)                                                                        \
   template hipError_t run_k2<T, P>(const P&, int, int, const float*, const float*, float*, float*, \
-                                   float*, float, int, int32_t*, int32_t*, T*, T*, int64_t,       \
+                                   float*, float, int, int32_t*, int32_t*, T*, T*, int64_t, int,  \
                                    hipStream_t);
 RKV_K2_INST(bf16_bits, DenseProblem<bf16_bits>)
 RKV_K2_INST(float, DenseProblem<float>)

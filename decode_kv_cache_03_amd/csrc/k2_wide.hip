@@ -63,13 +63,16 @@ __device__ __forceinline__ void wait_tiles(int tiles_after) {
 
 // Row block i (0..ni-1) of a unit with nb = ceil(N/128) tiles: first tile t0,
 // nt tiles. Blocks are laid from the end, so only block 0 can be a single
-// tile.
+// tile. A block streams its own tile(s) first, then the `ext` other tiles:
+// 0..t0-1, and for the symmetric R also t0+nt..nb-1.
 struct Block {
-  int t0, nt;
-  __device__ int len() const { return nt + t0; }
-  __device__ int tile(int k) const { return k < nt ? t0 + k : k - nt; }   // own tile(s) first
+  int t0, nt, ext;
+  __device__ int len() const { return nt + ext; }
+  __device__ int tile(int k) const {
+    return k < nt ? t0 + k : (k - nt < t0 ? k - nt : k);
+  }
 };
-__device__ __forceinline__ Block block_of(int i, bool odd) {
+__device__ __forceinline__ Block block_of(int i, bool odd, int nb, bool sym) {
   Block b;
   if (odd) {
     b.t0 = i == 0 ? 0 : 2 * i - 1;
@@ -78,6 +81,7 @@ __device__ __forceinline__ Block block_of(int i, bool odd) {
     b.t0 = 2 * i;
     b.nt = 2;
   }
+  b.ext = sym ? nb - b.nt : b.t0;
   return b;
 }
 
@@ -94,7 +98,7 @@ template <int NQB>
 __device__ __forceinline__ float key_importance(const char* qlds, const u32x2_t* slds,
                                                 const u32x4_t (&kf)[kNch], int key, int n_u,
                                                 int W, int G, int rpg_shift, bool causal,
-                                                int lane) {
+                                                bool mean, int lane) {
   const int rpg_mask = (1 << rpg_shift) - 1;
   const int octets_per_group = (1 << rpg_shift) >> 3;
   const float inv_w = 1.0f / (float)W;
@@ -133,20 +137,20 @@ __device__ __forceinline__ float key_importance(const char* qlds, const u32x2_t*
       run += os;
       const int o = qb * 4 + t;
       if (((o + 1) & (octets_per_group - 1)) == 0) {
-        if (o / octets_per_group < G) best = fmaxf(best, run * inv_w);
+        if (o / octets_per_group < G) best = mean ? best + run * inv_w : fmaxf(best, run * inv_w);
         run = 0.f;
       }
     }
   }
-  return best;
+  return mean ? best / (float)G : best;
 }
 
-template <int NQB>
+template <int NQB, bool kSym>
 __global__ __launch_bounds__(kThreads, 1) void k2f_kernel(
     DenseProblem<bf16_bits> p, float* __restrict__ Zdbg, float* __restrict__ Rdbg,
     float* __restrict__ Idbg, float lam, int rpg_shift, int32_t* __restrict__ kept_all,
     bf16_bits* __restrict__ K_out, bf16_bits* __restrict__ V_out, int64_t out_stride,
-    FusedPlan L) {
+    int score_only, FusedPlan L) {
   using T = bf16_bits;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x;
@@ -158,6 +162,10 @@ __global__ __launch_bounds__(kThreads, 1) void k2f_kernel(
   const int nb = (N + 127) / 128;
   const int ni = (nb + 1) / 2;
   const bool odd = (nb & 1) != 0;
+  constexpr bool sym = kSym;   // symmetric R: every block sweeps every column tile
+  // keys past lim_s are masked in the statistics: padding rows past N, and
+  // keys that a window query cannot see
+  const bool causal = p.causal();
   const int rpg_mask = (1 << rpg_shift) - 1;
   u32x2_t* const stats = reinterpret_cast<u32x2_t*>(lds + L.stats);   // (max, 1/sum) bits
   // per-wave max and sum partials, [4][NQB*32] each, as separate 32-bit
@@ -209,7 +217,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2f_kernel(
       }
       t = ld.k;
     } else {
-      t = block_of(ld.blk, odd).tile(ld.k);
+      t = block_of(ld.blk, odd, nb, sym).tile(ld.k);
     }
     char* slot = lds + issue_slot * kTileBytes;
     const int row0 = t * 128 + wave * 16;   // first tile row this wave loads
@@ -235,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2f_kernel(
         ld.blk = 0;
         ld.k = 0;
       }
-    } else if (++ld.k == block_of(ld.blk, odd).len()) {
+    } else if (++ld.k == block_of(ld.blk, odd, nb, sym).len()) {
       ld.k = 0;
       if (++ld.blk == ni) {
         ld.u += gridDim.x;
@@ -297,7 +305,8 @@ __global__ __launch_bounds__(kThreads, 1) void k2f_kernel(
         u32x4_t kf[kNch];
 #pragma unroll
         for (int k = 0; k < kNch; ++k) kf[k] = ld16(tb + frag_offset<T>(kl, lh * kNch + k));
-        const bool edge = (t + 1) * 128 > N - W;   // tile holds padding or window keys
+        // tile holds padding or keys some window query cannot see
+        const bool edge = (t + 1) * 128 > (causal ? N - W : N);
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
           const int m = qb * 32 + ll;
@@ -311,7 +320,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2f_kernel(
           f32x16_t acc = {};
 #pragma unroll
           for (int k = 0; k < kNch; ++k) mma_chunk<T>(acc, kf[k], qf[k]);   // C[key][query]
-          const int last = N - W + r;   // last key visible to window query r
+          const int last = causal ? N - W + r : N - 1;   // last key visible to window query r
           float lg[16];
           float mt = -INFINITY;
 #pragma unroll
@@ -380,7 +389,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2f_kernel(
 
     // ---------------- phase R: redundancy, importance, Z ----------------
     for (int bi = 0; bi < ni; ++bi) {
-      const Block blk = block_of(bi, odd);
+      const Block blk = block_of(bi, odd, nb, sym);
       const int base = blk.t0 * 128;
       const int r_lo = wr * 64;   // wave's first row within the block
       const bool wave_live = r_lo < blk.nt * 128 && base + r_lo < N;
@@ -402,10 +411,11 @@ __global__ __launch_bounds__(kThreads, 1) void k2f_kernel(
       // 2. importance of the block's keys: wave (r, c) takes keys 64r + 32c + l32
       if (wave_live) {
         const int key = base + r_lo + wc * 32 + l32;
-        const bool causal = base + blk.nt * 128 > N - W;
+        const bool cz = causal && base + blk.nt * 128 > N - W;   // block reaches the window
+        const bool mean = p.pool_mean();
         const float best = wc == 0
-            ? key_importance<NQB>(qlds, stats, af[0], key, N, W, G, rpg_shift, causal, lane)
-            : key_importance<NQB>(qlds, stats, af[1], key, N, W, G, rpg_shift, causal, lane);
+            ? key_importance<NQB>(qlds, stats, af[0], key, N, W, G, rpg_shift, cz, mean, lane)
+            : key_importance<NQB>(qlds, stats, af[1], key, N, W, G, rpg_shift, cz, mean, lane);
         if (half == 0) imp_l[r_lo + wc * 32 + l32] = best;
       }
       // 3. keep the ring full
@@ -417,8 +427,10 @@ __global__ __launch_bounds__(kThreads, 1) void k2f_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx[rb][v] = -INFINITY;
 
-      // one 64x64 sub-block of the wave against tile `t` in `slot`; mode 0 =
-      // full, 1 = diagonal (rows and columns are the same 64 keys: keep j < i)
+      // one 64x64 sub-block of the wave against tile `t` in `slot`. mode 0 =
+      // every pair counts; bit 0 = diagonal (rows and columns are the same 64
+      // keys: keep j < i, or j != i for the symmetric R); bit 1 = the unit's
+      // last tile, whose columns past N are masked
       auto step = [&](const char* slot, int t, int mode) {
         f32x16_t acc[2][2];
 #pragma unroll
@@ -435,8 +447,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2f_kernel(
             mma_chunk<T>(acc[rb][1], af[rb][k], b1);
           }
         }
-        // column norms; columns past N (last tile) only meet rows past N or
-        // masked pairs, so any finite value serves there
+        // column norms (clamped reads: masked columns past N take any value)
         const int col = t * 128 + wc * 64 + l32;
         const float r0 = rn[min(col, N - 1)];
         const float r1 = rn[min(col + 32, N - 1)];
@@ -449,34 +460,51 @@ __global__ __launch_bounds__(kThreads, 1) void k2f_kernel(
         } else {
           int lane_v = lane;   // re-materialised: keeps the masks out of loop preheaders
           asm volatile("" : "+v"(lane_v));
+          const int l = lane_v & 31;
+          const bool diag = (mode & 1) != 0;
           const float rcb[2] = {r0, r1};
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-            for (int cb = 0; cb <= rb; ++cb)
+            for (int cb = 0; cb < 2; ++cb) {
+              if (!sym && diag && cb > rb) continue;   // wholly above the diagonal
+              const bool col_ok = !(mode & 2) || col + cb * 32 < N;
 #pragma unroll
               for (int v = 0; v < 16; ++v) {
-                const bool ok = (rb > cb) || (acc_row(v, lane_v) > (lane_v & 31));
-                if (ok) mx[rb][v] = fmaxf(mx[rb][v], acc[rb][cb][v] * rcb[cb]);
+                // on the diagonal, row rb*32 + a follows column cb*32 + b iff
+                // rb > cb, or rb == cb and a > b; it is the same key iff
+                // rb == cb and a == b
+                const int a = acc_row(v, lane_v);
+                const bool pair_ok = !diag || (sym ? (rb != cb || a != l) : (rb > cb || a > l));
+                if (col_ok && pair_ok) mx[rb][v] = fmaxf(mx[rb][v], acc[rb][cb][v] * rcb[cb]);
               }
+            }
         }
       };
+      // columns past N exist only in the unit's last tile, and only rows that
+      // precede them (symmetric R) must not see them
+      const bool partial_last = sym && N % 128 != 0;
 
       // 4. the block's own tile(s): columns 128d + 64wc against rows r_lo
+      // (columns right of the rows only for the symmetric R)
       for (int d = 0; d < blk.nt; ++d) {
         const int c_lo = 128 * d + 64 * wc;
-        if (wave_live && c_lo <= r_lo) step(slot_ptr(cons_slot, d), blk.t0 + d, c_lo == r_lo ? 1 : 0);
+        const int t = blk.t0 + d;
+        const int mode = (c_lo == r_lo ? 1 : 0) | (partial_last && t == nb - 1 ? 2 : 0);
+        if (wave_live && (sym || c_lo <= r_lo)) step(slot_ptr(cons_slot, d), t, mode);
       }
       c += blk.nt;
       cons_slot = cons_slot + blk.nt >= S ? cons_slot + blk.nt - S : cons_slot + blk.nt;
 
-      // 5. tiles 0..t0-1, wholly left of the block's rows
-      for (int j = 0; j < blk.t0; ++j) {
+      // 5. tiles 0..t0-1, wholly left of the block's rows (and for the
+      // symmetric R the tiles right of it)
+      for (int j = 0; j < blk.ext; ++j) {
         ensure_issued(c, 1);
         wait_tiles(issued - (c + 1));
         lds_barrier();
         refill(c);
-        if (wave_live) step(lds + cons_slot * kTileBytes, j, 0);
+        const int t = blk.tile(blk.nt + j);
+        if (wave_live) step(lds + cons_slot * kTileBytes, t, partial_last && t == nb - 1 ? 2 : 0);
         ++c;
         cons_slot = cons_slot + 1 == S ? 0 : cons_slot + 1;
       }
@@ -504,7 +532,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2f_kernel(
         const int row = base + tid;
         if (tid < blk.nt * 128 && row < N) {
           const float m = fmaxf(comb[tid], comb[256 + tid]);
-          const float R = row == 0 ? 0.f : m * rn[row];
+          const float R = (row == 0 && !sym) ? 0.f : m * rn[row];
           const float I = imp_l[tid];
           const float z = lam * I - (1.0f - lam) * R + 0.0f;   // + 0 folds -0 onto +0
           zs[row] = z;
@@ -517,23 +545,27 @@ __global__ __launch_bounds__(kThreads, 1) void k2f_kernel(
     }
 
     // ---------------- selection and gather ----------------
-    __syncthreads();
-    int32_t* kept = kept_all + p.kept_off(u);
-    select_block<kThreads>(zs, N, B, W, kept, ssh, ks);
-    __syncthreads();
-    gather_rows_block<T, kThreads>(ks, B, [&](int r) { return p.krow(u, r); },
-                                   [&](int r) { return p.vrow(u, r); },
-                                   K_out + (int64_t)u * out_stride, V_out + (int64_t)u * out_stride);
+    // (score_only: Z went to Zdbg; a later launch selects for groups of units)
+    if (!score_only) {
+      __syncthreads();
+      int32_t* kept = kept_all + p.kept_off(u);
+      select_block<kThreads>(zs, N, B, W, kept, ssh, ks);
+      __syncthreads();
+      gather_rows_block<T, kThreads>(ks, B, [&](int r) { return p.krow(u, r); },
+                                     [&](int r) { return p.vrow(u, r); },
+                                     K_out + (int64_t)u * out_stride, V_out + (int64_t)u * out_stride);
+    }
     // ks is next written by the next unit's selection, after the barriers of
     // its statistics and redundancy phases
   }
 }
 
-template <int NQB>
+template <int NQB, bool kSym>
 static hipError_t run_t(const DenseProblem<bf16_bits>& p, float* dbg_Z, float* dbg_R, float* dbg_I,
                         float lam, int rpg_shift, int32_t* kept, bf16_bits* K_out,
-                        bf16_bits* V_out, int64_t out_stride, const FusedPlan& L, hipStream_t st) {
-  auto kern = k2f_kernel<NQB>;
+                        bf16_bits* V_out, int64_t out_stride, int score_only, const FusedPlan& L,
+                        hipStream_t st) {
+  auto kern = k2f_kernel<NQB, kSym>;
   const void* fn = reinterpret_cast<const void*>(kern);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
   int dev = 0, cus = 0;
@@ -542,21 +574,33 @@ static hipError_t run_t(const DenseProblem<bf16_bits>& p, float* dbg_Z, float* d
   if (e != hipSuccess) return e;
   const int grid = min(cus, p.num_units);   // one workgroup per CU, whole units each
   return launch("rkv_k2_compress", kern, dim3(grid), dim3(kThreads), L.total, st, p, dbg_Z, dbg_R,
-                dbg_I, lam, rpg_shift, kept, K_out, V_out, out_stride, L);
+                dbg_I, lam, rpg_shift, kept, K_out, V_out, out_stride, score_only, L);
 }
 
 }  // namespace fused
 
+template <int NQB>
+static hipError_t run_sym(const DenseProblem<bf16_bits>& p, float* dbg_Z, float* dbg_R, float* dbg_I,
+                          float lam, int rpg_shift, int32_t* kept, bf16_bits* K_out,
+                          bf16_bits* V_out, int64_t out_stride, int score_only,
+                          const FusedPlan& L, hipStream_t st) {
+  if (p.symmetric())
+    return fused::run_t<NQB, true>(p, dbg_Z, dbg_R, dbg_I, lam, rpg_shift, kept, K_out, V_out,
+                                   out_stride, score_only, L, st);
+  return fused::run_t<NQB, false>(p, dbg_Z, dbg_R, dbg_I, lam, rpg_shift, kept, K_out, V_out,
+                                  out_stride, score_only, L, st);
+}
+
 hipError_t run_k2_fused(const DenseProblem<bf16_bits>& p, int nqb, float* dbg_Z, float* dbg_R,
                         float* dbg_I, float lam, int rpg_shift, int32_t* kept, bf16_bits* K_out,
-                        bf16_bits* V_out, int64_t out_stride, hipStream_t st) {
+                        bf16_bits* V_out, int64_t out_stride, int score_only, hipStream_t st) {
   const FusedPlan L = fused_plan_choose(p.N, p.B, p.G * p.W, nqb);
-  if (L.total == 0) return hipErrorInvalidValue;
+  if (L.total == 0 || (score_only && dbg_Z == nullptr)) return hipErrorInvalidValue;
   switch (nqb) {
-    case 1: return fused::run_t<1>(p, dbg_Z, dbg_R, dbg_I, lam, rpg_shift, kept, K_out, V_out, out_stride, L, st);
-    case 2: return fused::run_t<2>(p, dbg_Z, dbg_R, dbg_I, lam, rpg_shift, kept, K_out, V_out, out_stride, L, st);
-    case 3: return fused::run_t<3>(p, dbg_Z, dbg_R, dbg_I, lam, rpg_shift, kept, K_out, V_out, out_stride, L, st);
-    default: return fused::run_t<4>(p, dbg_Z, dbg_R, dbg_I, lam, rpg_shift, kept, K_out, V_out, out_stride, L, st);
+    case 1: return run_sym<1>(p, dbg_Z, dbg_R, dbg_I, lam, rpg_shift, kept, K_out, V_out, out_stride, score_only, L, st);
+    case 2: return run_sym<2>(p, dbg_Z, dbg_R, dbg_I, lam, rpg_shift, kept, K_out, V_out, out_stride, score_only, L, st);
+    case 3: return run_sym<3>(p, dbg_Z, dbg_R, dbg_I, lam, rpg_shift, kept, K_out, V_out, out_stride, score_only, L, st);
+    default: return run_sym<4>(p, dbg_Z, dbg_R, dbg_I, lam, rpg_shift, kept, K_out, V_out, out_stride, score_only, L, st);
   }
 }
 

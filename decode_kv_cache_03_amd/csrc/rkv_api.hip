@@ -131,6 +131,7 @@ struct DenseLayout {
   float* part;       // [units][chunks][NQB*32] per-chunk softmax (max, sum)
   float* fin;        // [units][NQB*32] per query row (max, 1/sum)
   int32_t* counters; // [8 + units] item claims per XCD, then blocks completed per unit
+  float* zsum;       // [units / select_group][N] summed scores of head-shared selection
   size_t bytes;
 };
 
@@ -171,6 +172,12 @@ int check_dense_desc(const rkv_dense_desc* d) {
     return fail(RKV_EINVAL, "num_heads * n_cand too large");
   if ((int64_t)(d->num_heads + 7) / 8 * 8 * ((d->n_cand + rkv::kK2Rows - 1) / rkv::kK2Rows) > INT32_MAX)
     return fail(RKV_EINVAL, "num_heads * ceil(n_cand / 128) must stay below 2^31");
+  if (d->variant & ~rkv::kVariantMask)
+    return fail(RKV_EINVAL, "unknown variant bits 0x%x", (unsigned)(d->variant & ~rkv::kVariantMask));
+  if (d->select_group < 0) return fail(RKV_EINVAL, "select_group must be >= 0 (got %d)", d->select_group);
+  if (d->select_group > 1 && d->num_heads % d->select_group != 0)
+    return fail(RKV_EINVAL, "num_heads (%d) must be a multiple of select_group (%d)", d->num_heads,
+                d->select_group);
   return RKV_OK;
 }
 
@@ -187,6 +194,7 @@ DenseLayout dense_layout(const rkv_dense_desc* d, char* base) {
   L.part = c.take<float>(units * chunks * nqb * 32 * 2);
   L.fin = c.take<float>(units * nqb * 32 * 2);
   L.counters = c.take<int32_t>(8 + units);
+  L.zsum = d->select_group > 1 ? c.take<float>(units / (size_t)d->select_group * n) : nullptr;
   L.bytes = std::max<size_t>(c.used, kAlign);
   return L;
 }
@@ -212,6 +220,7 @@ int dense_run(const rkv_dense_desc* d, const void* K, const void* V, const void*
   p.W = d->window;
   p.k1_chunks = (d->n_cand + rkv::kK1Keys - 1) / rkv::kK1Keys;
   p.k2_blocks = (d->n_cand + rkv::kK2Rows - 1) / rkv::kK2Rows;
+  p.variant = d->variant;
   const int64_t out_stride = d->out_head_stride ? d->out_head_stride : (int64_t)d->budget * 128;
   const int units = d->num_heads;
   const int nkeep = std::min(d->n_cand, d->budget);
@@ -219,25 +228,40 @@ int dense_run(const rkv_dense_desc* d, const void* K, const void* V, const void*
   if (d->n_cand > d->budget) {
     const int rpg_shift = rows_per_group_shift(d->window);
     const int nqb = nqb_of(d->gqa_group, d->window);
+    // head-shared selection: units are scored alone, then each group selects
+    // once on its summed scores and every unit gathers its own rows
+    const int group = d->select_group > 1 ? d->select_group : 1;
+    const bool shared = group > 1;
+    float* z = dbg_Z ? dbg_Z : L.z;
+    bool scored = false;
     if constexpr (sizeof(T) == 2) {
       if (rkv::fused_plan_choose(p.N, p.B, p.G * p.W, nqb).total > 0) {
-        e = rkv::run_k2_fused(p, nqb, dbg_Z, dbg_R, dbg_I, d->mix_lambda, rpg_shift, kept,
-                              static_cast<T*>(K_out), static_cast<T*>(V_out), out_stride, st);
+        e = rkv::run_k2_fused(p, nqb, shared ? z : dbg_Z, dbg_R, dbg_I, d->mix_lambda, rpg_shift,
+                              kept, static_cast<T*>(K_out), static_cast<T*>(V_out), out_stride,
+                              shared ? 1 : 0, st);
         if (e != hipSuccess) return hip_fail(e, "compression launch");
-        return RKV_OK;
+        scored = true;
       }
     }
-    // units too long for one workgroup's LDS, and fp32: statistics pass, then
-    // XCD-local teams of workgroups per unit
-    float* z = dbg_Z ? dbg_Z : L.z;
-    e = rkv::run_k1<T>(p, nqb, units * p.k1_chunks, units, L.part, L.fin, L.rinv, L.counters,
-                       rpg_shift, st);
-    if (e != hipSuccess) return hip_fail(e, "importance launch");
-    const int k2_items = 8 * ((units + 7) / 8) * p.k2_blocks;
-    e = rkv::run_k2<T>(p, nqb, k2_items, L.rinv, L.fin, z, dbg_R, dbg_I, d->mix_lambda, rpg_shift,
-                       L.counters, kept, static_cast<T*>(K_out), static_cast<T*>(V_out),
-                       out_stride, st);
-    if (e != hipSuccess) return hip_fail(e, "compression launch");
+    if (!scored) {
+      // units too long for one workgroup's LDS, and fp32: statistics pass,
+      // then XCD-local teams of workgroups per unit
+      e = rkv::run_k1<T>(p, nqb, units * p.k1_chunks, units, L.part, L.fin, L.rinv, L.counters,
+                         rpg_shift, st);
+      if (e != hipSuccess) return hip_fail(e, "importance launch");
+      const int k2_items = 8 * ((units + 7) / 8) * p.k2_blocks;
+      e = rkv::run_k2<T>(p, nqb, k2_items, L.rinv, L.fin, z, dbg_R, dbg_I, d->mix_lambda, rpg_shift,
+                         L.counters, kept, static_cast<T*>(K_out), static_cast<T*>(V_out),
+                         out_stride, shared ? 0 : 1, st);
+      if (e != hipSuccess) return hip_fail(e, "compression launch");
+    }
+    if (shared) {
+      e = rkv::run_k4_group(p, group, z, L.zsum, kept, st);
+      if (e != hipSuccess) return hip_fail(e, "shared selection launch");
+      e = rkv::run_k5_dense<T>(p, kept, static_cast<T*>(K_out), static_cast<T*>(V_out), out_stride,
+                               nkeep, st);
+      if (e != hipSuccess) return hip_fail(e, "gather launch");
+    }
     return RKV_OK;
   }
   e = rkv::run_k4(p, units, L.z, kept, 1, st);   // N <= B: identity selection and a plain copy
@@ -312,6 +336,8 @@ int check_paged(const rkv_paged_desc* d, const int32_t* seq_len, const int32_t* 
   if (d->max_pages_per_seq < 1) return fail(RKV_EINVAL, "max_pages_per_seq must be >= 1");
   if (d->num_pages < 1) return fail(RKV_EINVAL, "num_pages must be >= 1");
   if ((int64_t)d->num_seqs * d->num_kv_heads > (1 << 30)) return fail(RKV_EINVAL, "too many units");
+  if (d->variant & ~rkv::kVariantMask)
+    return fail(RKV_EINVAL, "unknown variant bits 0x%x", (unsigned)(d->variant & ~rkv::kVariantMask));
   const int64_t slot = d->slot_stride ? d->slot_stride : 128;
   const int64_t head = d->head_stride ? d->head_stride : (int64_t)d->page_size * 128;
   const int64_t page = d->page_stride ? d->page_stride : (int64_t)d->num_kv_heads * d->page_size * 128;
@@ -470,6 +496,7 @@ int paged_run(const rkv_paged_desc* d, void* Kp, void* Vp, int32_t* page_table, 
   p.unit_list = L.unit_list;
   p.unit_count = (int)P.unit_list.size();
   p.all_units = d->num_seqs * d->num_kv_heads;
+  p.variant = d->variant;
   float* z = dbg_Z ? dbg_Z : L.z;
   hipError_t e;
   if (p.unit_count > 0) {
@@ -478,7 +505,7 @@ int paged_run(const rkv_paged_desc* d, void* Kp, void* Vp, int32_t* page_table, 
                        rpg_shift, st);
     if (e != hipSuccess) return hip_fail(e, "importance launch");
     e = rkv::run_k2<T>(p, P.nqb, p.k2_count, L.rinv, L.fin, z, nullptr, nullptr, d->mix_lambda,
-                       rpg_shift, nullptr, nullptr, nullptr, nullptr, 0, st);
+                       rpg_shift, nullptr, nullptr, nullptr, nullptr, 0, 0, st);
     if (e != hipSuccess) return hip_fail(e, "redundancy launch");
   }
   e = rkv::run_k4(p, p.all_units, z, kept, 0, st);

@@ -34,26 +34,35 @@ hipError_t run_k1(const P& p, int nqb, int k1_items, int num_units, float* part,
                   float* rinv, int32_t* counters, int rpg_shift, hipStream_t st);
 
 // Redundancy, importance and joint score: Z [units][N] (R, I when requested).
-// Dense caches (P::kFinishUnits): the last block of each unit to finish also
-// selects its kept indices and gathers its kept rows into K_out / V_out;
-// counters (as cleared by run_k1) must then be non-null. Paged caches ignore
-// the last five arguments.
+// Dense caches (P::kFinishUnits): with select_units != 0, the last block of
+// each unit to finish also selects its kept indices and gathers its kept rows
+// into K_out / V_out; counters (as cleared by run_k1) must be non-null.
+// Paged caches ignore the last six arguments.
 template <typename T, class P>
 hipError_t run_k2(const P& p, int nqb, int k2_items, const float* rinv, const float* fin, float* Z,
                   float* dbg_R, float* dbg_I, float lam, int rpg_shift, int32_t* counters,
-                  int32_t* kept, T* K_out, T* V_out, int64_t out_stride, hipStream_t st);
+                  int32_t* kept, T* K_out, T* V_out, int64_t out_stride, int select_units,
+                  hipStream_t st);
 
 // Dense bf16 caches whose unit fits the fused kernel's LDS plan
 // (fused_plan_choose): the whole step in one launch (k2_wide.hip), no
-// workspace. dbg_* may be null.
+// workspace. dbg_* may be null. With score_only the kernel writes Z (dbg_Z,
+// then required) and neither selects nor gathers.
 hipError_t run_k2_fused(const DenseProblem<bf16_bits>& p, int nqb, float* dbg_Z, float* dbg_R,
                         float* dbg_I, float lam, int rpg_shift, int32_t* kept, bf16_bits* K_out,
-                        bf16_bits* V_out, int64_t out_stride, hipStream_t st);
+                        bf16_bits* V_out, int64_t out_stride, int score_only, hipStream_t st);
 
 // Selection: kept indices per unit (ascending), from Z.
 template <class P>
 hipError_t run_k4(const P& p, int units, const float* Z, int32_t* kept, int fill_tail,
                   hipStream_t st);
+
+// Head-shared selection: each run of `group` consecutive units selects once,
+// on the sum of their Z (zsum: [units / group][N] scratch), and every unit of
+// the run receives those kept indices.
+template <typename T>
+hipError_t run_k4_group(const DenseProblem<T>& p, int group, const float* Z, float* zsum,
+                        int32_t* kept, hipStream_t st);
 
 // Dense gather of the kept rows into K_out / V_out.
 template <typename T>

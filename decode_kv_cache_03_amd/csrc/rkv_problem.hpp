@@ -85,6 +85,20 @@ __host__ __device__ inline FusedPlan fused_plan_choose(int N, int B, int gw, int
   return none;
 }
 
+// Reading variants of a call (bits as in rkv.h): the defaults are R over
+// earlier candidates, the causal window and max pooling over the GQA heads.
+constexpr uint32_t kVariantSymmetric = 1u;   // R_i over every j != i
+constexpr uint32_t kVariantNoCausal = 2u;    // every window query sees all N keys
+constexpr uint32_t kVariantPoolMean = 4u;    // mean over the G heads instead of max
+constexpr uint32_t kVariantMask = 7u;
+
+struct VariantBits {
+  uint32_t variant = 0;
+  __host__ __device__ bool symmetric() const { return (variant & kVariantSymmetric) != 0; }
+  __host__ __device__ bool causal() const { return (variant & kVariantNoCausal) == 0; }
+  __host__ __device__ bool pool_mean() const { return (variant & kVariantPoolMean) != 0; }
+};
+
 template <typename T>
 struct Finish {
   int32_t* queue;      // [8] items claimed per XCD; cleared by the statistics pass
@@ -93,10 +107,11 @@ struct Finish {
   T* K_out;
   T* V_out;
   int64_t out_stride;  // elements between units of K_out / V_out
+  int select_units;    // 0: scores only (a later launch selects for groups of units)
 };
 
 template <typename T>
-struct DenseProblem {
+struct DenseProblem : VariantBits {
   static constexpr bool kRowsContiguous = true;   // rows of a unit are 128 elements apart
   static constexpr bool kFinishUnits = true;      // the redundancy kernel also selects and gathers
   const T* K;
@@ -146,7 +161,7 @@ struct DenseProblem {
 };
 
 template <typename T>
-struct PagedProblem {
+struct PagedProblem : VariantBits {
   static constexpr bool kRowsContiguous = false;
   static constexpr bool kFinishUnits = false;     // selection and in-place compaction run after
   const T* Kp;

@@ -68,6 +68,24 @@ extern "C" {
 #define RKV_F32 0
 #define RKV_BF16 1
 
+/* Reading variants: bits of the `variant` field of both descriptors; 0
+ * selects the readings stated at the top of this file. Each replaces one
+ * step the pages leave open by its alternative:
+ *   RKV_VARIANT_SYMMETRIC  R_i = max over every other candidate j != i of
+ *                          cos(k_i, k_j), so both copies of a duplicate score
+ *                          as redundant (the plain symmetric reading; the
+ *                          default follows P1's "similar to what is already
+ *                          retained"). Scores the whole N x N cosine matrix:
+ *                          twice the MFMA work of the default.
+ *   RKV_VARIANT_NO_CAUSAL  every window query sees all N candidates.
+ *   RKV_VARIANT_POOL_MEAN  I_j = mean over the G query heads instead of the
+ *                          max (the pooling ablation of P3 "Measured effects
+ *                          reported in the paper", last row).
+ * Other bits are RKV_EINVAL. */
+#define RKV_VARIANT_SYMMETRIC 1u
+#define RKV_VARIANT_NO_CAUSAL 2u
+#define RKV_VARIANT_POOL_MEAN 4u
+
 /* Dense layout: unit h has K[h], V[h] = N rows of 128 contiguous elements,
  * consecutive rows 128 elements apart, consecutive units kv_head_stride
  * elements apart. */
@@ -82,6 +100,18 @@ typedef struct rkv_dense_desc {
   int32_t dtype;           /* RKV_BF16 or RKV_F32 */
   int64_t kv_head_stride;  /* elements between units in K and V; 0 means N*128 */
   int64_t out_head_stride; /* elements between units in K_out, V_out; 0 means B*128 */
+  uint32_t variant;        /* RKV_VARIANT_* bits; 0 = the default readings */
+  int32_t select_group;    /* 0 or 1: every unit selects its own tokens. g > 1:
+                              head-shared selection: each run of g consecutive
+                              units (e.g. the KV heads of one layer of one
+                              sequence) keeps ONE token set, the window plus the
+                              top B-w by the sum of the g units' Z, and every
+                              unit of the run gathers its own rows of it. This
+                              is what the eviction-score all-reduce across
+                              tensor-parallel ranks does so that every rank
+                              evicts the same tokens [P1 "What the redundancy
+                              scoring ..."]; an all-reduce sums. num_heads must
+                              be a multiple of g. Summed in unit order in fp32. */
 } rkv_dense_desc;
 
 /* Bytes of workspace rkv_compress needs for `desc` (with all debug outputs
@@ -93,14 +123,16 @@ size_t rkv_workspace_size(const rkv_dense_desc* desc);
  *   K, V       device [num_heads][N][128] (unit stride kv_head_stride), dtype
  *   Q_win      device [num_heads][G][w][128] contiguous, dtype; row (g, r) is
  *              window query r (r = 0 oldest, w-1 newest) of query head g
- *   kept_idx   device int32 [num_heads][B]: kept candidate indices ascending;
+ *   kept_idx   device int32 [num_heads][B]: kept candidate indices ascending
+ *              (identical rows within a select_group run);
  *              when N < B, entries N..B-1 are set to -1
  *   K_out, V_out  device [num_heads][B][128] (unit stride out_head_stride);
  *              row r = row kept_idx[r] of the input; rows >= min(N, B) are
  *              not written. Must not overlap K or V.
  *   dbg_I, dbg_R, dbg_Z  device float [num_heads][N] or NULL; when given and
- *              N > B they receive I, R and Z (window entries included; Z with
- *              -0 written as +0). Not written when N <= B.
+ *              N > B they receive each unit's own I, R and Z (window entries
+ *              included; Z with -0 written as +0; not the group sum of
+ *              head-shared selection). Not written when N <= B.
  *   workspace  device, >= rkv_workspace_size(desc) bytes, 256-byte aligned
  *   stream     hipStream_t
  * Returns RKV_OK or a negative status. */
@@ -128,6 +160,7 @@ typedef struct rkv_paged_desc {
   int64_t page_stride;       /* elements; 0 means H*page_size*128 */
   int64_t head_stride;       /* elements; 0 means page_size*128 */
   int64_t slot_stride;       /* elements; 0 means 128 */
+  uint32_t variant;          /* RKV_VARIANT_* bits; 0 = the default readings */
 } rkv_paged_desc;
 
 /* Workspace bytes for rkv_compress_paged with these host lengths/budgets;

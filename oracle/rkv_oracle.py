@@ -236,13 +236,14 @@ def logical_rows(pages, page_table_row, n: int, head: int, page_size: int) -> np
 
 
 def compress_paged(K_pages, V_pages, page_table, seq_len, budget, Q, free_list,
-                   window: int, lam: float, page_size: int) -> dict:
+                   window: int, lam: float, page_size: int, **variant) -> dict:
     """Paged compression with page return (reading R8).
 
     K_pages, V_pages [P, H, page_size, d]; page_table [S, maxp]; seq_len,
     budget [S]; Q [S, H, G, w, d]; free_list: the free page ids before the
     call. Returns dict(K_pages, V_pages, page_table, free_list, kept) where
     kept[s][h] are the kept logical indices and the pages are new arrays.
+    The keyword arguments select the reading variants, as in compress_head.
     """
     Kp = np.array(K_pages, copy=True)
     Vp = np.array(V_pages, copy=True)
@@ -259,7 +260,7 @@ def compress_paged(K_pages, V_pages, page_table, seq_len, budget, Q, free_list,
         for h in range(heads):
             Kl = logical_rows(K_pages, page_table[s], n, h, page_size)
             Vl = logical_rows(V_pages, page_table[s], n, h, page_size)
-            res = compress_head(Kl, Vl, np.asarray(Q)[s, h], b, window, lam)
+            res = compress_head(Kl, Vl, np.asarray(Q)[s, h], b, window, lam, **variant)
             kept = res["kept"]
             kept_s.append(kept)
             if n <= b:

@@ -63,6 +63,10 @@ def call_dense(lib, d, ws_bytes=1 << 30, K=FAKE, V=ctypes.c_void_p(0x20000000),
     ("gqa_group", 17, _lib.RKV_EUNSUPPORTED),
     ("kv_head_stride", 1000, _lib.RKV_EINVAL),
     ("out_head_stride", 1000, _lib.RKV_EINVAL),
+    ("variant", 8, _lib.RKV_EINVAL),
+    ("variant", 0x80000001, _lib.RKV_EINVAL),
+    ("select_group", -1, _lib.RKV_EINVAL),
+    ("select_group", 3, _lib.RKV_EINVAL),        # 4 units are not a multiple of 3
 ])
 def test_dense_desc_errors(lib, field, value, code):
     d = dense(**{field: value})
@@ -108,6 +112,31 @@ def test_zero_heads_needs_nothing(lib):
     assert lib.rkv_workspace_size(ctypes.byref(d)) > 0
     assert lib.rkv_compress(ctypes.byref(d), None, None, None, None, None, None, None, None, None,
                             None, 0, None) == _lib.RKV_OK
+
+
+def test_variants_and_groups_accepted(lib):
+    for v in range(8):
+        assert lib.rkv_workspace_size(ctypes.byref(dense(variant=v))) > 0
+    plain = lib.rkv_workspace_size(ctypes.byref(dense(select_group=1)))
+    assert lib.rkv_workspace_size(ctypes.byref(dense(select_group=0))) == plain
+    # head-shared selection adds the summed scores of each group
+    assert lib.rkv_workspace_size(ctypes.byref(dense(select_group=2))) >= plain + 2 * 1152 * 4
+    assert lib.rkv_workspace_size(ctypes.byref(dense(select_group=4))) > plain
+
+
+def test_struct_layouts_match_header():
+    """Field order and offsets of the ctypes views follow rkv.h (natural
+    alignment: 8-byte members at multiples of 8)."""
+    d = _lib.DenseDesc
+    assert [f[0] for f in d._fields_] == ["num_heads", "n_cand", "head_dim", "gqa_group", "window",
+                                          "budget", "mix_lambda", "dtype", "kv_head_stride",
+                                          "out_head_stride", "variant", "select_group"]
+    assert d.kv_head_stride.offset == 32 and d.variant.offset == 48 and ctypes.sizeof(d) == 56
+    p = _lib.PagedDesc
+    assert p.page_stride.offset == 40 and p.variant.offset == 64 and ctypes.sizeof(p) == 72
+    text = open(os.path.join(ROOT, "include", "rkv.h")).read()
+    for name in ("variant;", "select_group;"):
+        assert name in text
 
 
 def test_workspace_grows_with_units(lib):
@@ -167,7 +196,7 @@ def test_paged_free_list_overflow(lib):
 
 @pytest.mark.parametrize("field,value", [("page_size", 12), ("page_size", 0), ("num_kv_heads", 0),
                                          ("head_dim", 96), ("window", 0), ("num_pages", 0),
-                                         ("slot_stride", 64)])
+                                         ("slot_stride", 64), ("variant", 16)])
 def test_paged_desc_errors(lib, field, value):
     d = paged(**{field: value})
     rc, _ = call_paged(lib, d, [100, 50, 70], [64, 32, 48])
