@@ -11,7 +11,14 @@ roofline of the kernel that takes the most time (measured live with HIP
 events around each of its launches in the timed region), and the CPU oracle's
 rate on a bounded sample.
 
-python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama-event|qwen|llama-layer]
+python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama-event|qwen|llama-layer|decode-loop]
+                [--symmetric] [--no-causal] [--pool mean] [--select-group G] [--graph]
+
+The last four select the reading variants (symmetric redundancy, no causal
+window, mean pooling over the GQA heads) and head-shared selection over runs
+of G consecutive units (G = 8: the KV heads of one layer of one sequence); the
+workload name then carries them as a suffix. --graph captures one
+compression call in a HIP graph (torch.cuda.CUDAGraph) and times its replays.
 """
 from __future__ import annotations
 
@@ -38,21 +45,27 @@ WORKLOADS = {
 }
 
 
-def kernel_work(name, units, n, b, g, w, esize=2):
+def kernel_work(name, units, n, b, g, w, esize=2, symmetric=False, group=1):
     """Algorithmic work of one launch of `name`: (bound, amount, unit).
 
     bytes: K read once for scoring, the window queries, the kept K and V rows
     read, K' and V' written, the indices; flops: the cosine contraction over
-    unique pairs, N(N-1)*d per unit. The dense redundancy kernel also selects
-    and gathers, so it carries both; its bound is the one whose time at peak
-    is longer. The statistics kernel is charged its own read of K and Q.
+    unique pairs, N(N-1)*d per unit (2N(N-1)*d for the symmetric R, which
+    needs every ordered pair). The dense redundancy kernel also selects and
+    gathers, so it carries both; its bound is the one whose time at peak is
+    longer. Under head-shared selection (group > 1) it only scores: K and Q
+    read, Z written; selection and gather are launches of their own. The
+    statistics kernel is charged its own read of K and Q.
     """
     d = 128
     row = d * esize
     nk = min(n, b)
-    flops = units * n * (n - 1) * d
+    flops = units * n * (n - 1) * d * (2 if symmetric else 1)
     if name == "rkv_k2_compress":
-        nbytes = units * bytes_per_unit(n, b, g, w, esize)
+        if group > 1:
+            nbytes = units * (n * row + g * w * row + 4 * n)
+        else:
+            nbytes = units * bytes_per_unit(n, b, g, w, esize)
         if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9):
             return "mfma", flops, "flop"
         return "hbm", nbytes, "byte"
@@ -64,6 +77,8 @@ def kernel_work(name, units, n, b, g, w, esize=2):
         return "hbm", units * (n * row + g * w * row), "byte"
     if name == "rkv_k4_select":
         return "hbm", units * (4 * n + 4 * b), "byte"
+    if name == "rkv_k4_group_select":
+        return "hbm", units * (4 * (n - w) + 4 * b), "byte"
     return None, 0, None
 
 
@@ -91,6 +106,7 @@ KERNEL_SOURCES = {
     "rkv_k1_stats": ["k1_importance.hip"] + _HEADERS,
     "rkv_k1_combine": ["k1_importance.hip"] + _HEADERS,
     "rkv_k4_select": ["k4_select.hip", "rkv_select.hpp"] + _HEADERS,
+    "rkv_k4_group_select": ["k4_select.hip", "rkv_select.hpp"] + _HEADERS,
     "rkv_k5_gather": ["k5_compact.hip"] + _HEADERS,
     "rkv_k5_paged_compact": ["k5_compact.hip"] + _HEADERS,
 }
@@ -112,8 +128,9 @@ def measured_traffic(kernel, workload):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(case, budget_s=15.0, max_units=400):
-    """The oracle as it stands, on sampled units copied to the host."""
+def cpu_baseline(case, budget_s=15.0, max_units=400, variant=None, group=1):
+    """The oracle as it stands, on sampled units (or groups of units under
+    head-shared selection) copied to the host."""
     import numpy as np
     from oracle import rkv_oracle as orc
     try:
@@ -121,23 +138,29 @@ def cpu_baseline(case, budget_s=15.0, max_units=400):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
+    variant = variant or {}
     rng = np.random.default_rng(0)
-    order = rng.permutation(case.num_heads)[:max_units]
+    order = rng.permutation(case.num_heads // group)[:max_units]
     done = 0
     t0 = time.perf_counter()
     elapsed = 0.0
-    for h in order:
-        K = case.K[int(h)].float().cpu().numpy()
-        V = case.V[int(h)].float().cpu().numpy()
-        Q = case.Q[int(h)].float().cpu().numpy()
+    for gi in order:
+        sl = slice(int(gi) * group, (int(gi) + 1) * group)
+        K = case.K[sl].float().cpu().numpy()
+        V = case.V[sl].float().cpu().numpy()
+        Q = case.Q[sl].float().cpu().numpy()
         s = time.perf_counter()
-        orc.compress_head(K, V, Q, case.budget, case.window, case.lam)
+        if group > 1:
+            orc.compress_shared(K, V, Q, case.budget, case.window, case.lam, **variant)
+        else:
+            orc.compress_head(K[0], V[0], Q[0], case.budget, case.window, case.lam, **variant)
         elapsed += time.perf_counter() - s
-        done += 1
+        done += group
         if time.perf_counter() - t0 > budget_s:
             break
+    what = f"{done // group} groups of {group} units" if group > 1 else f"{done} units"
     return {"value": done / elapsed, "unit": "KV-heads/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} units drawn at random from the same {case.num_heads}-unit cache "
+            "sample": f"{what} drawn at random from the same {case.num_heads}-unit cache "
                       f"(N={case.n}), float64 numpy oracle, timed per unit excluding the copy "
                       f"to the host"}
 
@@ -209,6 +232,13 @@ def main():
     ap.add_argument("--lam", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--symmetric", action="store_true", help="R over every other candidate")
+    ap.add_argument("--no-causal", action="store_true", help="window queries see all candidates")
+    ap.add_argument("--pool", default="max", choices=["max", "mean"], help="GQA pooling of I")
+    ap.add_argument("--select-group", type=int, default=1,
+                    help="head-shared selection over runs of this many consecutive units")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the compression call in a HIP graph and time its replays")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy kernel three times, so "
                          "memory counters can be scaled against a known byte count")
@@ -232,8 +262,17 @@ def main():
                           "copy_calibration_bytes_written": dst.numel() * 2}), file=sys.stderr)
         del src, dst
 
-    wl = WORKLOADS[args.workload]
+    wl = dict(WORKLOADS[args.workload])
     c = CONFIGS[wl["cfg"]]
+    variant = dict(symmetric=args.symmetric, causal=not args.no_causal, pool=args.pool)
+    group = max(1, args.select_group)
+    suffix = "".join(s for s, on in (("+symmetric", args.symmetric), ("+no-causal", args.no_causal),
+                                     ("+pool-mean", args.pool == "mean"),
+                                     (f"+shared{group}", group > 1)) if on)
+    if suffix and args.workload == "decode-loop":
+        print("the decode-loop workload runs the default readings only", file=sys.stderr)
+        sys.exit(2)
+    wl["name"] += suffix
     if args.workload == "decode-loop":
         run_decode_loop(args, wl, c, rkv)
         return
@@ -245,31 +284,59 @@ def main():
     K_out = torch.empty((units, b, 128), dtype=case.K.dtype, device="cuda")
     V_out = torch.empty_like(K_out)
     kept = torch.empty((units, b), dtype=torch.int32, device="cuda")
-    ws = torch.empty(rkv.workspace_size(units, n, g, w, b), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(rkv.workspace_size(units, n, g, w, b, select_group=group), dtype=torch.uint8,
+                     device="cuda")
     torch.cuda.synchronize()
 
-    def step():
+    def call():
         rkv.compress(case.K, case.V, case.Q, b, w, lam, K_out=K_out, V_out=V_out, kept_idx=kept,
-                     workspace=ws)
+                     workspace=ws, select_group=group, **variant)
+
+    step = call
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call()
+        step = graph.replay
+        wl["name"] += "+graph"
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     rkv.timing_enable(True)
     torch.cuda.synchronize()
+    evs = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        if args.graph:
+            # replays carry no library events: time each on the stream it runs on
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step()
+            e1.record()
+            evs.append((e0, e1))
+        else:
+            step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     times = rkv.timing_read()
     rkv.timing_enable(False)
+    if args.graph:
+        # the graph of a single-unit-selection call holds one launch
+        # (rkv_k2_compress) on the fused path; otherwise the replay is named
+        name = "rkv_k2_compress" if (group == 1 and c["dtype"] == "bf16") else "graph_replay"
+        times = {name: (len(evs), sum(a.elapsed_time(b_) for a, b_ in evs))}
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = units / (ms_per_step * 1e-3)
     kernels = {k: {"launches": v[0], "avg_ms": v[1] / max(v[0], 1)} for k, v in times.items()}
     dom = max(times, key=lambda k: times[k][1])
-    bound, amount, _ = kernel_work(dom, units, n, b, g, w)
+    bound, amount, _ = kernel_work(dom, units, n, b, g, w, symmetric=args.symmetric, group=group)
     avg_s = kernels[dom]["avg_ms"] * 1e-3
     if bound == "mfma":
         achieved = amount / avg_s / 1e12
@@ -282,18 +349,19 @@ def main():
     roof["kernel"] = dom
     roof["traffic"] = measured_traffic(dom, wl["name"])
     for k, v in kernels.items():
-        kb, amt, _ = kernel_work(k, units, n, b, g, w)
+        kb, amt, _ = kernel_work(k, units, n, b, g, w, symmetric=args.symmetric, group=group)
         if kb == "mfma":
             v["tflops"] = amt / (v["avg_ms"] * 1e-3) / 1e12
         elif kb == "hbm":
             v["gbs"] = amt / (v["avg_ms"] * 1e-3) / 1e9
         if k == "rkv_k2_compress":   # the contraction it also carries
-            v["tflops"] = units * n * (n - 1) * 128 / (v["avg_ms"] * 1e-3) / 1e12
+            pairs = n * (n - 1) * (2 if args.symmetric else 1)
+            v["tflops"] = units * pairs * 128 / (v["avg_ms"] * 1e-3) / 1e12
             v["mfma_frac"] = v["tflops"] / MFMA_BF16_PEAK_TFLOPS
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, budget_s=args.cpu_seconds)
+        cpu = cpu_baseline(case, budget_s=args.cpu_seconds, variant=variant, group=group)
 
     step_bytes = units * bytes_per_unit(n, b, g, w)
     out = {
@@ -303,7 +371,9 @@ def main():
         "config": {"workload": wl["name"], "units": units, "n_cand": n, "kv_budget": b,
                    "window_size": w, "mix_lambda": lam, "gqa_group": g, "head_dim": 128,
                    "batch": c["batch"], "layers": c["layers"], "kv_heads": c["kv_heads"],
-                   "key_repeat_coverage": round(case.meta["coverage"], 4)},
+                   "key_repeat_coverage": round(case.meta["coverage"], 4),
+                   "symmetric": args.symmetric, "causal_window": not args.no_causal,
+                   "gqa_pool": args.pool, "select_group": group},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,

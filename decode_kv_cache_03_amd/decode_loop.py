@@ -23,6 +23,17 @@ unit per step), as in batched decoding of equal-length sequences.
 
 Every step of the compression itself runs in the HIP library (rkv_compress);
 this driver only moves rows into place and decides when to call it.
+
+With ``use_graph`` the compression call is captured once per ping-pong
+parity into a HIP graph (through torch.cuda.CUDAGraph) and replayed at every
+later event, the analogue of the piecewise CUDA-graph capture the pages
+mention for the serving port ("R-KV: decoding-time KV cache compression for
+reasoning models", hysenlabs page, "Three install paths with different levels
+of commitment"). The window queries are first copied, in time order, into a
+fixed buffer outside the graph, since their ring position moves between
+events; every other argument of the call is a fixed buffer already. The
+library issues no memset or host copy on the dense path, so the captured
+launches are the whole call.
 """
 from __future__ import annotations
 
@@ -32,7 +43,7 @@ from . import HEAD_DIM, compress, workspace_size
 class DecodeLoop:
     def __init__(self, units: int, gqa_group: int, kv_budget: int = 1024, window_size: int = 8,
                  divide_length: int = 128, mix_lambda: float = 0.1, dtype=None, device="cuda",
-                 capacity: int = 0):
+                 capacity: int = 0, use_graph: bool = False):
         import torch
         self.units, self.gqa, self.budget, self.window = units, gqa_group, kv_budget, window_size
         self.divide_length, self.lam = divide_length, mix_lambda
@@ -58,6 +69,9 @@ class DecodeLoop:
             dname = "bf16" if dt == torch.bfloat16 else "f32"
             nbytes = workspace_size(units, cap, gqa_group, window_size, kv_budget, dname)
             self._ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.use_graph = bool(use_graph) and self.active
+        self._qbuf = torch.zeros_like(self._q) if self.use_graph else None
+        self._graphs = [None, None]        # captured compression per parity
         self.on_event = None               # callback(loop) before each compression
 
     @property
@@ -91,16 +105,41 @@ class DecodeLoop:
             return True
         return False
 
+    def _compress_call(self, cur: int, q):
+        nxt = 1 - cur
+        compress(self._K[cur][:, :self.capacity], self._V[cur][:, :self.capacity], q,
+                 self.budget, self.window, self.lam,
+                 K_out=self._K[nxt][:, :self.budget], V_out=self._V[nxt][:, :self.budget],
+                 kept_idx=self._kept, workspace=self._ws)
+
+    def _compress_graphed(self, cur: int):
+        import torch
+        self._qbuf.copy_(self.window_queries())
+        g = self._graphs[cur]
+        if g is None:
+            # one eager call on a side stream first, as capture requires
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                self._compress_call(cur, self._qbuf)
+            torch.cuda.current_stream().wait_stream(side)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self._compress_call(cur, self._qbuf)
+            self._graphs[cur] = g
+        g.replay()
+
     def compress(self):
         """Compress every unit from `length` rows to kv_budget rows."""
         if self.on_event is not None:
             self.on_event(self)
-        nxt = 1 - self._cur
-        compress(self._K[self._cur][:, :self.length], self._V[self._cur][:, :self.length],
-                 self.window_queries(), self.budget, self.window, self.lam,
-                 K_out=self._K[nxt][:, :self.budget], V_out=self._V[nxt][:, :self.budget],
-                 kept_idx=self._kept, workspace=self._ws)
-        self._cur = nxt
+        if self.length != self.capacity:
+            raise RuntimeError("compression runs on a full buffer")
+        if self.use_graph:
+            self._compress_graphed(self._cur)
+        else:
+            self._compress_call(self._cur, self.window_queries())
+        self._cur = 1 - self._cur
         self.length = self.budget
         self.events += 1
 
