@@ -30,6 +30,12 @@
 //    keys are scored for importance from the same fragments;
 //  * Z stays in LDS; the selection runs on it, and the gather reads the kept
 //    indices from LDS.
+// Variants: for the symmetric R (a separate instantiation) every block also
+// sweeps the tiles right of it and masks only j == i on its diagonal and
+// columns past N in the last tile; without the causal window the statistics
+// and weights mask only padding keys; mean pooling sums the heads' window
+// means and divides by G. Under head-shared selection the kernel stops after
+// writing Z (a later launch selects for each group of units and gathers).
 #include "rkv_problem.hpp"
 #include "rkv_launch.hpp"
 #include "rkv_select.hpp"
