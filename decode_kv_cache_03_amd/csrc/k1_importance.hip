@@ -17,7 +17,8 @@
 //   k1_stats     per (unit, 256-key chunk): logits on MFMA with the keys as
 //                the A operand, so each lane owns one query column and its
 //                running max / sum of exp stay in registers; also writes
-//                1/||k|| for every key.
+//                1/||k|| for every key, and for paged bf16 units copies the
+//                keys to contiguous rows for the long-unit kernel.
 //   k1_combine   per unit: merges the chunks' (max, sum) per query row into
 //                (max, 1/sum).
 // A query row's normaliser needs every key before any weight can be formed,
@@ -78,6 +79,14 @@ __global__ __launch_bounds__(256) void k1_stats_kernel(P p, float* __restrict__ 
     const bool kvalid = key < N;
     u32x4_t kf[NCH];
     load_half_row<T>(kf, kvalid ? p.krow(u, key) : p.krow(u, 0), half, kvalid);
+    // paged units scored by the long-unit kernel: their keys to contiguous rows
+    if (kvalid) {
+      T* dst = p.copy_dst(u, key);
+      if (dst != nullptr) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) st16(reinterpret_cast<char*>(dst) + half * (NCH * 16) + 16 * c, kf[c]);
+      }
+    }
     float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) ss += sumsq_chunk<T>(kf[c]);

@@ -1,0 +1,414 @@
+// Long units (bf16): redundancy, importance and Z of one 512-row block per
+// work item, by an 8-wave workgroup per CU that streams the unit's key tiles
+// through an LDS ring.
+//
+// Same arithmetic as the other scoring kernels (pages and readings cited in
+// k2_redundancy.hip): R_i = max_{j<i} cos(k_i, k_j) (every j != i for the
+// symmetric variant) on bf16 MFMA with fp32 accumulation, the norms applied
+// in the fp32 epilogue; importance from the softmax normalisers of the
+// statistics pass (k1_importance.hip); Z = lambda*I - (1-lambda)*R. Selection
+// and compaction run as separate launches.
+//
+// Why a separate kernel: a unit of N keys needs N^2/2 cosine pairs but only
+// N rows of keys, so for long units the contraction is MFMA-bound as long as
+// each key tile fetched from memory feeds enough rows. The item kernels of
+// k2_redundancy.hip feed 128 rows per 32 KiB tile; here a block holds 512
+// rows (wave w: rows 64w..64w+63, both 64-column halves of every tile), so a
+// tile carries 512 flop per byte fetched.
+//
+// Shape:
+//  * tiles (128 rows, 32 KiB, XOR-swizzled chunks) stream through a ring of
+//    up to 4 LDS slots by direct global->LDS loads; a step waits only for its
+//    own tile (the wait counts the loads issued after it), and the stream
+//    runs on across items; each item's window queries and softmax normalisers
+//    come with its first tile, into one of two parity buffers;
+//  * an item streams its own tiles in descending order (each wave takes its
+//    rows as A fragments, its row norms and its keys' importance when its own
+//    tile arrives; tiles of lower rows come later, so every wave that needs a
+//    tile as columns holds its fragments already), then tiles 0..t0-1; the
+//    symmetric variant adds the tiles right of the block and, at the end, the
+//    own tiles above each wave's rows again;
+//  * column norms come from the B fragments of the step itself (the sum of
+//    squares of the 16 chunks each lane already reads), so no global norm
+//    array is read inside the stream;
+//  * work items go to workgroups in order of decreasing cost, alternating
+//    direction each round (a greedy longest-first schedule): item k of round
+//    r is k = r*G + b for workgroup b on even rounds, r*G + G-1-b on odd ones.
+#include "rkv_problem.hpp"
+#include "rkv_launch.hpp"
+#include "rkv_stream.hpp"
+
+namespace rkv {
+namespace longu {
+
+using stream::key_importance;
+using stream::kLoadsPerTile;
+using stream::kNch;
+using stream::wait_tiles;
+
+constexpr int kThreads = 512;
+constexpr int kRowBytes = 256;
+constexpr int kTileBytes = 128 * kRowBytes;
+
+// Tile order of an item: own tiles t0..t0+nt-1 descending, then the `ext`
+// other tiles ascending (0..t0-1; symmetric: also t0+nt..nb-1), then, for the
+// symmetric variant, own tiles t0+1..t0+nt-1 again.
+struct Geo {
+  int t0, nt, nb, ext, again;
+  __device__ int len() const { return nt + ext + again; }
+  __device__ int tile(int k) const {
+    if (k < nt) return t0 + nt - 1 - k;
+    const int j = k - nt;
+    if (j < ext) return j < t0 ? j : j + nt;
+    return t0 + 1 + (j - ext);
+  }
+};
+__device__ __forceinline__ Geo geo_of(int n, int blk, bool sym) {
+  Geo g;
+  g.nb = (n + 127) / 128;
+  g.t0 = 4 * blk;
+  g.nt = min(4, g.nb - g.t0);
+  g.ext = sym ? g.nb - g.nt : g.t0;
+  g.again = sym ? g.nt - 1 : 0;
+  return g;
+}
+
+__device__ __forceinline__ int sched(int r, int b, int G) {
+  return r * G + ((r & 1) ? G - 1 - b : b);
+}
+
+template <int NQB, bool kSym, class P>
+__global__ __launch_bounds__(kThreads, 1) void k2l_kernel(P p, const float* __restrict__ fin,
+                                                         float* __restrict__ Z,
+                                                         float* __restrict__ Rdbg,
+                                                         float* __restrict__ Idbg, float lam,
+                                                         int rpg_shift, LongPlan L) {
+  using T = bf16_bits;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr bool sym = kSym;
+  const int S = L.slots;
+  const int W = p.W, G = p.G, gw = G * W;
+  const bool causal = p.causal(), mean = p.pool_mean();
+  const int count = p.long_count();
+  const int grid = gridDim.x, bid = blockIdx.x;
+  const T* rows = p.long_rows();
+  constexpr int kStatsBytes = NQB * 32 * 8;
+
+  // Tile load q (0..3) of wave w fills KiB 4w + q of a slot: tile row
+  // 16w + 4q + lane/16 at chunk position lane % 16, fetching chunk
+  // (lane % 16) ^ (row & 15) of that row.
+  int lofs[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r16 = (4 * q + lane / 16) & 15;
+    lofs[q] = (lane / 16) * kRowBytes + (((lane % 16) ^ r16) << 4);
+  }
+  int boff[kNch];   // B fragments: rows l32 (+32) of a 64-column half, chunk half*8 + c
+#pragma unroll
+  for (int c = 0; c < kNch; ++c) boff[c] = frag_offset<T>(l32, half * kNch + c);
+
+  // ---- loader: this workgroup's items, tile by tile, into the ring ----
+  struct LdPos {
+    int r, par, k;
+    bool valid;
+    LongItem it;
+    Geo g;
+  };
+  auto fetch = [&](int r, LongItem& it, Geo& g) -> bool {
+    const int k = sched(r, bid, grid);
+    if (k >= count) return false;
+    it = p.long_item(k);
+    it.u = __builtin_amdgcn_readfirstlane(it.u);
+    it.blk = __builtin_amdgcn_readfirstlane(it.blk);
+    it.n = __builtin_amdgcn_readfirstlane(it.n);
+    g = geo_of(it.n, it.blk, sym);
+    return true;
+  };
+  LdPos ld;
+  ld.r = 0;
+  ld.par = 0;
+  ld.k = 0;
+  ld.valid = fetch(0, ld.it, ld.g);
+  int issued = 0, issue_slot = 0;
+  // The loader runs at most one item ahead of the consumer: the queries and
+  // normalisers of two items share the two parity buffers.
+  int ld_limit = 2;
+  auto issue_next = [&]() -> bool {
+    if (!ld.valid || ld.r >= ld_limit) return false;
+    int lane_v = lane;   // per call: keeps lane-derived values out of the callers' loops
+    asm volatile("" : "+v"(lane_v));
+    const LongItem& it = ld.it;
+    if (ld.k == 0) {   // the item's window queries and normalisers, ahead of its first tile
+      const char* q = reinterpret_cast<const char*>(p.q(it.u));
+      const int qkb = L.qbytes / 1024;
+      char* qdst = lds + L.q + ld.par * L.qbytes;
+      for (int kb = wave; kb < qkb; kb += 8) {
+        const int n = kb * 4 + lane_v / 16;
+        const int c = (lane_v % 16) ^ (n & 15);
+        load16_to_lds(q + min(n, gw - 1) * kRowBytes + c * 16, qdst + kb * 1024);
+      }
+      if (wave == 0 && lane_v < NQB * 16)
+        load16_to_lds(reinterpret_cast<const char*>(fin) + ((int64_t)it.u * NQB * 32) * 8 + lane_v * 16,
+                      lds + L.stats + ld.par * kStatsBytes);
+    }
+    const int t = ld.g.tile(ld.k);
+    char* slot = lds + issue_slot * kTileBytes;
+    const T* urows = rows + it.row_base;
+    const int row0 = t * 128 + wave * 16;   // first tile row this wave loads
+    if ((t + 1) * 128 <= it.n) {
+      const char* src = reinterpret_cast<const char*>(urows + (int64_t)row0 * kD);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) load16_to_lds(src + q * 1024 + lofs[q], slot + wave * 4096 + q * 1024);
+    } else {   // the unit's last tile: rows past n repeat row n-1
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = min(row0 + 4 * q + lane_v / 16, it.n - 1);
+        const int chunk_ofs = lofs[q] - (lane_v / 16) * kRowBytes;
+        load16_to_lds(reinterpret_cast<const char*>(urows + (int64_t)r * kD) + chunk_ofs,
+                      slot + wave * 4096 + q * 1024);
+      }
+    }
+    ++issued;
+    issue_slot = issue_slot + 1 == S ? 0 : issue_slot + 1;
+    if (++ld.k == ld.g.len()) {
+      ld.k = 0;
+      ++ld.r;
+      ld.par ^= 1;
+      ld.valid = fetch(ld.r, ld.it, ld.g);
+    }
+    return true;
+  };
+  auto refill = [&](int c) {
+    while (issued - c < S && issue_next()) {
+    }
+  };
+  // Tile c is needed next. When the last refill could not issue it (the
+  // loader held at an item boundary), its slot was freed by a step that every
+  // wave finished only after a barrier: take one, then issue.
+  auto ensure_issued = [&](int c) {
+    if (issued < c + 1) {
+      lds_barrier();
+      refill(c);
+    }
+  };
+
+  int c = 0, cons_slot = 0;   // tiles consumed, c % S
+  refill(0);
+
+  int par = 0;
+  for (int r = 0;; ++r, par ^= 1) {
+    LongItem it;
+    Geo g;
+    if (!fetch(r, it, g)) break;
+    ld_limit = r + 2;
+    const int n = it.n;
+    const char* qlds = lds + L.q + par * L.qbytes;
+    const u32x2_t* st = reinterpret_cast<const u32x2_t*>(lds + L.stats + par * kStatsBytes);
+    const int base = g.t0 * 128;
+    const int r_lo = wave * 64;   // wave's first row within the block
+    const int own = wave >> 1;    // block tile holding the wave's rows
+    const int hw = wave & 1;      // which 64-row half of it
+    const bool wave_live = r_lo < g.nt * 128 && base + r_lo < n;
+    // columns past n exist only in the last tile; only rows that precede them
+    // (symmetric R) must not see them
+    const bool partial_last = sym && n % 128 != 0;
+
+    u32x4_t af[2][kNch];
+    float mx[2][16];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx[rb][v] = -INFINITY;
+    float rnr[2] = {0.f, 0.f}, imp[2] = {0.f, 0.f};   // rows rb*32 + l32 of the wave
+
+    // the wave's 64 rows against columns 64ch.. of tile t in `slot`. mode bit
+    // 0: the columns are the wave's own rows (keep j < i, or j != i for the
+    // symmetric R); bit 1: mask columns past n
+    auto half_step = [&](const char* slot, int t, int ch, int mode) {
+      f32x16_t acc[2][2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x16_t{};
+      const char* bs = slot + ch * 64 * kRowBytes;
+      float ss0 = 0.f, ss1 = 0.f;
+#pragma unroll
+      for (int k = 0; k < kNch; ++k) {
+        const u32x4_t b0 = ld16(bs + boff[k]);
+        const u32x4_t b1 = ld16(bs + boff[k] + 32 * kRowBytes);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          mma_chunk<T>(acc[rb][0], af[rb][k], b0);
+          mma_chunk<T>(acc[rb][1], af[rb][k], b1);
+        }
+        ss0 += sumsq_chunk<T>(b0);
+        ss1 += sumsq_chunk<T>(b1);
+      }
+      // 1/||k|| of this lane's two columns (the halves hold the two halves of a row)
+      ss0 += __shfl_xor(ss0, 32, 64);
+      ss1 += __shfl_xor(ss1, 32, 64);
+      const float r0 = ss0 > 0.f ? __frsqrt_rn(ss0) : 0.f;
+      const float r1 = ss1 > 0.f ? __frsqrt_rn(ss1) : 0.f;
+      if (mode == 0) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            mx[rb][v] = fmaxf(mx[rb][v], fmaxf(acc[rb][0][v] * r0, acc[rb][1][v] * r1));
+      } else {
+        int lane_m = lane;   // re-materialised: keeps the masks out of loop preheaders
+        asm volatile("" : "+v"(lane_m));
+        const int l = lane_m & 31;
+        const bool diag = (mode & 1) != 0;
+        const int col = t * 128 + ch * 64 + l;
+        const float rcb[2] = {r0, r1};
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) {
+            if (!sym && diag && cb > rb) continue;   // wholly above the diagonal
+            const bool col_ok = !(mode & 2) || col + cb * 32 < n;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              // on the diagonal, row rb*32 + a follows column cb*32 + b iff
+              // rb > cb, or rb == cb and a > b; it is the same key iff
+              // rb == cb and a == b
+              const int a = acc_row(v, lane_m);
+              const bool pair_ok = !diag || (sym ? (rb != cb || a != l) : (rb > cb || a > l));
+              if (col_ok && pair_ok) mx[rb][v] = fmaxf(mx[rb][v], acc[rb][cb][v] * rcb[cb]);
+            }
+          }
+      }
+    };
+
+    const int len = g.len();
+    for (int k = 0; k < len; ++k) {
+      ensure_issued(c);
+      wait_tiles(issued - (c + 1));
+      lds_barrier();
+      refill(c);
+      const char* slot = lds + cons_slot * kTileBytes;
+      const int t = g.tile(k);
+      const int cm = (partial_last && t == g.nb - 1) ? 2 : 0;
+      // modes of the two 64-column halves for this wave (-1: not needed)
+      int m0 = -1, m1 = -1;
+      if (k < g.nt) {
+        // own tile d, descending
+        const int d = g.nt - 1 - k;
+        if (wave_live && own == d) {
+          const int arow = hw * 64 + l32;
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            float ss = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < kNch; ++kk) {
+              af[rb][kk] = ld16(slot + frag_offset<T>(arow + rb * 32, half * kNch + kk));
+              ss += sumsq_chunk<T>(af[rb][kk]);
+            }
+            ss += __shfl_xor(ss, 32, 64);
+            rnr[rb] = ss > 0.f ? __frsqrt_rn(ss) : 0.f;
+          }
+          // only keys among the last w need the causal test
+          const bool cz = causal && base + (d + 1) * 128 > n - W;
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            imp[rb] = key_importance<NQB>(qlds, st, af[rb], base + r_lo + rb * 32 + l32, n, W, G,
+                                          rpg_shift, cz, mean, lane);
+          // half hw of this tile holds the wave's own rows; the other half
+          // lies left of them (hw = 1) or right of them (hw = 0: symmetric R)
+          m0 = (hw == 0 ? 1 : 0) | cm;
+          m1 = hw == 1 ? (1 | cm) : (sym ? cm : -1);
+        } else if (own > d) {   // the tile lies wholly left of the wave's rows
+          m0 = m1 = cm;
+        }
+      } else if (k < g.nt + g.ext || own < t - g.t0) {
+        // other tiles; last (symmetric R), own tiles right of the wave's rows
+        m0 = m1 = cm;
+      }
+      if (wave_live && m0 >= 0) half_step(slot, t, 0, m0);
+      if (wave_live && m1 >= 0) half_step(slot, t, 1, m1);
+      ++c;
+      cons_slot = cons_slot + 1 == S ? 0 : cons_slot + 1;
+    }
+
+    // row maxima over all columns; value j = rb*16 + v of a lane belongs to
+    // row rb*32 + acc_row(v, lane); lane l ends with value l & 31, i.e. the
+    // wave's 64 rows one per lane
+    float val[32];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) val[rb * 16 + v] = mx[rb][v];
+    max_butterfly_step<16>(val, lane);
+    max_butterfly_step<8>(val, lane);
+    max_butterfly_step<4>(val, lane);
+    max_butterfly_step<2>(val, lane);
+    max_butterfly_step<1>(val, lane);
+    if (wave_live) {
+      const int rl = (l32 >> 4) * 32 + acc_row(l32 & 15, lane);   // row within the wave
+      const int src = rl & 31;                                     // lane holding its norm
+      const float n0 = __shfl(rnr[0], src, 64), n1 = __shfl(rnr[1], src, 64);
+      const float i0 = __shfl(imp[0], src, 64), i1 = __shfl(imp[1], src, 64);
+      const int row = base + r_lo + rl;
+      if (row < n) {
+        const float R = (row == 0 && !sym) ? 0.f : val[0] * (rl >= 32 ? n1 : n0);
+        const float I = rl >= 32 ? i1 : i0;
+        const float z = lam * I - (1.0f - lam) * R + 0.0f;   // + 0 folds -0 onto +0
+        const int64_t so = it.score_off;
+        Z[so + row] = z;
+        if (Rdbg != nullptr) Rdbg[so + row] = R;
+        if (Idbg != nullptr) Idbg[so + row] = I;
+      }
+    }
+  }
+  // every load this workgroup issued was consumed: the ring is empty
+}
+
+template <int NQB, bool kSym, class P>
+static hipError_t run_t(const P& p, int count, const float* fin, float* Z, float* dbg_R,
+                        float* dbg_I, float lam, int rpg_shift, const LongPlan& L,
+                        hipStream_t st) {
+  auto kern = k2l_kernel<NQB, kSym, P>;
+  const void* fn = reinterpret_cast<const void*>(kern);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
+  int dev = 0, cus = 0;
+  if (e == hipSuccess) e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int grid = min(cus, count);
+  return launch("rkv_k2_long", kern, dim3(grid), dim3(kThreads), L.total, st, p, fin, Z, dbg_R,
+                dbg_I, lam, rpg_shift, L);
+}
+
+template <int NQB, class P>
+static hipError_t run_sym(const P& p, int count, const float* fin, float* Z, float* dbg_R,
+                          float* dbg_I, float lam, int rpg_shift, const LongPlan& L,
+                          hipStream_t st) {
+  if (p.symmetric())
+    return run_t<NQB, true>(p, count, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
+  return run_t<NQB, false>(p, count, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
+}
+
+}  // namespace longu
+
+template <class P>
+hipError_t run_k2_long(const P& p, int nqb, int count, const float* fin, float* Z, float* dbg_R,
+                       float* dbg_I, float lam, int rpg_shift, hipStream_t st) {
+  const LongPlan L = long_plan_choose(p.G * p.W, nqb);
+  if (L.total == 0) return hipErrorInvalidValue;
+  if (count <= 0) return hipSuccess;
+  switch (nqb) {
+    case 1: return longu::run_sym<1>(p, count, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
+    case 2: return longu::run_sym<2>(p, count, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
+    case 3: return longu::run_sym<3>(p, count, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
+    default: return longu::run_sym<4>(p, count, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
+  }
+}
+
+template hipError_t run_k2_long<DenseProblem<bf16_bits>>(const DenseProblem<bf16_bits>&, int, int, const float*, float*, float*, float*, float, int, hipStream_t);
+template hipError_t run_k2_long<PagedProblem<bf16_bits>>(const PagedProblem<bf16_bits>&, int, int, const float*, float*, float*, float*, float, int, hipStream_t);
+
+}  // namespace rkv

@@ -244,16 +244,30 @@ int dense_run(const rkv_dense_desc* d, const void* K, const void* V, const void*
       }
     }
     if (!scored) {
-      // units too long for one workgroup's LDS, and fp32: statistics pass,
-      // then XCD-local teams of workgroups per unit
+      // units too long for one workgroup's LDS, and fp32: statistics pass first
       e = rkv::run_k1<T>(p, nqb, units * p.k1_chunks, units, L.part, L.fin, L.rinv, L.counters,
                          rpg_shift, st);
       if (e != hipSuccess) return hip_fail(e, "importance launch");
-      const int k2_items = 8 * ((units + 7) / 8) * p.k2_blocks;
-      e = rkv::run_k2<T>(p, nqb, k2_items, L.rinv, L.fin, z, dbg_R, dbg_I, d->mix_lambda, rpg_shift,
-                         L.counters, kept, static_cast<T*>(K_out), static_cast<T*>(V_out),
-                         out_stride, shared ? 0 : 1, st);
-      if (e != hipSuccess) return hip_fail(e, "compression launch");
+      if constexpr (sizeof(T) == 2) {
+        // bf16: 512-row blocks by the long-unit kernel, then selection and gather
+        const int count = units * ((p.N + 511) / 512);
+        e = rkv::run_k2_long(p, nqb, count, L.fin, z, dbg_R, dbg_I, d->mix_lambda, rpg_shift, st);
+        if (e != hipSuccess) return hip_fail(e, "redundancy launch");
+        if (!shared) {
+          e = rkv::run_k4(p, units, z, kept, 1, st);
+          if (e != hipSuccess) return hip_fail(e, "select launch");
+          e = rkv::run_k5_dense<T>(p, kept, static_cast<T*>(K_out), static_cast<T*>(V_out),
+                                   out_stride, nkeep, st);
+          if (e != hipSuccess) return hip_fail(e, "gather launch");
+        }
+      } else {
+        // fp32: XCD-local teams of workgroups per unit, the last one finishing it
+        const int k2_items = 8 * ((units + 7) / 8) * p.k2_blocks;
+        e = rkv::run_k2<T>(p, nqb, k2_items, L.rinv, L.fin, z, dbg_R, dbg_I, d->mix_lambda,
+                           rpg_shift, L.counters, kept, static_cast<T*>(K_out),
+                           static_cast<T*>(V_out), out_stride, shared ? 0 : 1, st);
+        if (e != hipSuccess) return hip_fail(e, "compression launch");
+      }
     }
     if (shared) {
       e = rkv::run_k4_group(p, group, z, L.zsum, kept, st);
@@ -318,9 +332,11 @@ namespace {
 struct PagedPlan {
   // host-side metadata, uploaded in one copy
   std::vector<int32_t> seq_len, bud, free_off, unit_list;
-  std::vector<int64_t> score_base, kept_base, k1_base;
+  std::vector<int64_t> score_base, kept_base, k1_base, kc_base;
   std::vector<int2> k1_list, k2_list;
+  std::vector<rkv::LongItem> long_list;
   int64_t total_scores = 0, total_kept = 0, total_chunks = 0;
+  int64_t kc_elems = 0;   // contiguous key copy of the scored units (bf16, long-unit kernel)
   int32_t freed = 0;
   int nqb = 1;
 };
@@ -365,6 +381,13 @@ void paged_plan(const rkv_paged_desc* d, const int32_t* seq_len, const int32_t* 
   P.score_base.resize(S);
   P.kept_base.resize(S);
   P.k1_base.assign((size_t)S * H, 0);
+  P.kc_base.assign((size_t)S * H, 0);
+  P.long_list.clear();
+  P.kc_elems = 0;
+  const bool bf16 = d->dtype == RKV_BF16;
+  const bool sym = (d->variant & rkv::kVariantSymmetric) != 0;
+  struct Costed { int64_t cost; rkv::LongItem it; };
+  std::vector<Costed> litems;
   P.unit_list.clear();
   P.k1_list.clear();
   P.k2_list.clear();
@@ -389,6 +412,17 @@ void paged_plan(const rkv_paged_desc* d, const int32_t* seq_len, const int32_t* 
         for (int c = 0; c < nch; ++c) P.k1_list.push_back(make_int2(u, c));
         ch += nch;
         scored.push_back({u, (n + rkv::kK2Rows - 1) / rkv::kK2Rows, n});
+        if (bf16) {
+          // long-unit kernel: contiguous copy of the unit's keys, 512-row items
+          P.kc_base[u] = P.kc_elems;
+          const int nb = (n + 127) / 128, nb5 = (n + 511) / 512;
+          for (int blk = 0; blk < nb5; ++blk) {
+            rkv::LongItem it{u, blk, n, 0, P.kc_elems, sc - (int64_t)H * n + (int64_t)hk * n};
+            const int64_t tiles = sym ? nb + std::min(4, nb - 4 * blk) - 1 : std::min(nb, 4 * blk + 4);
+            litems.push_back({tiles, it});
+          }
+          P.kc_elems += (int64_t)n * 128;
+        }
       }
     }
   }
@@ -403,6 +437,10 @@ void paged_plan(const rkv_paged_desc* d, const int32_t* seq_len, const int32_t* 
   for (auto& v : q) longest = std::max(longest, v.size());
   for (size_t k = 0; k < longest; ++k)
     for (int x = 0; x < 8; ++x) P.k2_list.push_back(k < q[x].size() ? q[x][k] : make_int2(-1, 0));
+  // long-unit items in order of decreasing work (ties: unit, then block)
+  std::stable_sort(litems.begin(), litems.end(),
+                   [](const Costed& a, const Costed& b) { return a.cost > b.cost; });
+  for (const Costed& c : litems) P.long_list.push_back(c.it);
   P.total_scores = sc;
   P.total_kept = kp;
   P.total_chunks = ch;
@@ -419,6 +457,9 @@ struct PagedLayout {
   int64_t* k1_base;
   int2* k1_list;
   int2* k2_list;
+  int64_t* kc_base;
+  rkv::LongItem* long_list;
+  void* kc;            // contiguous key copy (not uploaded)
   float* rinv;
   float* z;
   float* part;
@@ -440,7 +481,10 @@ PagedLayout paged_layout(const rkv_paged_desc* d, const PagedPlan& P, char* base
   L.k1_base = c.take<int64_t>(U);
   L.k1_list = c.take<int2>(P.k1_list.size());
   L.k2_list = c.take<int2>(P.k2_list.size());
+  L.kc_base = c.take<int64_t>(U);
+  L.long_list = c.take<rkv::LongItem>(P.long_list.size());
   L.meta_bytes = c.used;
+  L.kc = c.take<uint16_t>((size_t)P.kc_elems);
   L.rinv = c.take<float>(P.total_scores);
   L.z = c.take<float>(P.total_scores);
   L.part = c.take<float>((size_t)P.total_chunks * P.nqb * 32 * 2);
@@ -464,6 +508,8 @@ void pack_meta(const PagedPlan& P, const PagedLayout& L, const char* base, std::
   put(L.k1_base, P.k1_base.data(), P.k1_base.size() * 8);
   put(L.k1_list, P.k1_list.data(), P.k1_list.size() * sizeof(int2));
   put(L.k2_list, P.k2_list.data(), P.k2_list.size() * sizeof(int2));
+  put(L.kc_base, P.kc_base.data(), P.kc_base.size() * 8);
+  put(L.long_list, P.long_list.data(), P.long_list.size() * sizeof(rkv::LongItem));
 }
 
 template <typename T>
@@ -501,11 +547,21 @@ int paged_run(const rkv_paged_desc* d, void* Kp, void* Vp, int32_t* page_table, 
   hipError_t e;
   if (p.unit_count > 0) {
     const int rpg_shift = rows_per_group_shift(d->window);
+    if constexpr (sizeof(T) == 2) {   // the statistics pass also copies the keys
+      p.Kc = static_cast<T*>(L.kc);
+      p.kc_base = L.kc_base;
+      p.long_list = L.long_list;
+      p.long_cnt = (int)P.long_list.size();
+    }
     e = rkv::run_k1<T>(p, P.nqb, p.k1_count, p.all_units, L.part, L.fin, L.rinv, nullptr,
                        rpg_shift, st);
     if (e != hipSuccess) return hip_fail(e, "importance launch");
-    e = rkv::run_k2<T>(p, P.nqb, p.k2_count, L.rinv, L.fin, z, nullptr, nullptr, d->mix_lambda,
-                       rpg_shift, nullptr, nullptr, nullptr, nullptr, 0, 0, st);
+    if constexpr (sizeof(T) == 2)
+      e = rkv::run_k2_long(p, P.nqb, p.long_cnt, L.fin, z, nullptr, nullptr, d->mix_lambda,
+                           rpg_shift, st);
+    else
+      e = rkv::run_k2<T>(p, P.nqb, p.k2_count, L.rinv, L.fin, z, nullptr, nullptr, d->mix_lambda,
+                         rpg_shift, nullptr, nullptr, nullptr, nullptr, 0, 0, st);
     if (e != hipSuccess) return hip_fail(e, "redundancy launch");
   }
   e = rkv::run_k4(p, p.all_units, z, kept, 0, st);

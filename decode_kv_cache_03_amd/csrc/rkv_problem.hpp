@@ -99,6 +99,40 @@ struct VariantBits {
   __host__ __device__ bool pool_mean() const { return (variant & kVariantPoolMean) != 0; }
 };
 
+// Work item of the long-unit kernel (k2_long.hip): rows 512*blk .. of unit
+// u, whose n candidates lie at row_base (elements) in contiguous 128-element
+// rows, scores at score_off.
+struct LongItem {
+  int32_t u, blk, n, pad;
+  int64_t row_base, score_off;
+};
+
+// LDS plan of the long-unit kernel: a ring of `slots` 128-row bf16 tiles, and
+// per item parity the window queries and the softmax normalisers.
+struct LongPlan {
+  int slots, q, qbytes, stats, total;
+};
+
+__host__ __device__ inline LongPlan long_plan(int gw, int nqb, int slots) {
+  LongPlan L;
+  L.slots = slots;
+  L.q = slots * 128 * 256;
+  L.qbytes = (gw * 256 + 1023) / 1024 * 1024;
+  L.stats = L.q + 2 * L.qbytes;
+  L.total = L.stats + 2 * nqb * 32 * 8;
+  return L;
+}
+
+__host__ __device__ inline LongPlan long_plan_choose(int gw, int nqb) {
+  for (int slots = 4; slots >= 2; --slots) {
+    const LongPlan L = long_plan(gw, nqb, slots);
+    if (L.total <= 160 * 1024) return L;
+  }
+  LongPlan none = long_plan(gw, nqb, 2);
+  none.total = 0;
+  return none;
+}
+
 template <typename T>
 struct Finish {
   int32_t* queue;      // [8] items claimed per XCD; cleared by the statistics pass
@@ -158,6 +192,23 @@ struct DenseProblem : VariantBits {
     u = b;
     return u < num_units;
   }
+
+  // long-unit kernel items, in order of decreasing work: block index
+  // descending (a block sweeps its own tiles and every tile left of it)
+  __device__ int long_count() const { return num_units * ((N + 511) / 512); }
+  __device__ LongItem long_item(int k) const {
+    const int nb5 = (N + 511) / 512;
+    LongItem it;
+    it.blk = nb5 - 1 - k / num_units;
+    it.u = k - (k / num_units) * num_units;
+    it.n = N;
+    it.pad = 0;
+    it.row_base = (int64_t)it.u * kv_stride;
+    it.score_off = (int64_t)it.u * N;
+    return it;
+  }
+  __device__ const T* long_rows() const { return K; }
+  __device__ T* copy_dst(int, int) const { return nullptr; }   // rows are contiguous already
 };
 
 template <typename T>
@@ -182,6 +233,13 @@ struct PagedProblem : VariantBits {
   const int32_t* unit_list;  // units with N > B (compaction)
   int unit_count;
   int all_units;             // S * H
+  // long-unit kernel: the statistics pass copies each scored unit's keys to
+  // contiguous rows Kc + kc_base[u]; items listed by the host in order of
+  // decreasing work
+  T* Kc = nullptr;
+  const int64_t* kc_base = nullptr;
+  const LongItem* long_list = nullptr;
+  int long_cnt = 0;
 
   __device__ int n(int u) const { return seq_len[u / H]; }
   __device__ int budget(int u) const { return bud[u / H]; }
@@ -233,6 +291,27 @@ struct PagedProblem : VariantBits {
   __device__ bool select_item(int b, int& u) const {
     u = b;
     return b < all_units;
+  }
+  __device__ int long_count() const { return long_cnt; }
+  // read through the constant address space so that a uniform index gives a
+  // scalar load: a vector load here would make the long-unit kernel wait for
+  // every tile load in flight
+  __device__ LongItem long_item(int k) const {
+    typedef const __attribute__((address_space(4))) LongItem* ConstItems;
+    const ConstItems l = (ConstItems)long_list + k;
+    LongItem it;
+    it.u = l->u;
+    it.blk = l->blk;
+    it.n = l->n;
+    it.pad = 0;
+    it.row_base = l->row_base;
+    it.score_off = l->score_off;
+    return it;
+  }
+  __device__ const T* long_rows() const { return Kc; }
+  // where the statistics pass copies row t of unit u (null: no copy)
+  __device__ T* copy_dst(int u, int t) const {
+    return Kc != nullptr ? Kc + kc_base[u] + (int64_t)t * kD : nullptr;
   }
 };
 

@@ -74,7 +74,8 @@ SHAPES = [
     (300, 200, 8, 2, 0.1, "f32", 2),
     (260, 100, 8, 6, 0.1, "f32", 1),       # fp32 with two query blocks
     (5000, 4000, 8, 4, 0.1, "bf16", 1),    # fused kernel with a 2-slot tile ring
-    (8000, 6000, 8, 4, 0.1, "bf16", 1),    # unit too long for one workgroup: team path
+    (8000, 6000, 8, 4, 0.1, "bf16", 1),    # unit too long for one workgroup: long-unit kernel
+    (7777, 6000, 8, 4, 0.1, "bf16", 2),    # long-unit kernel, ragged last tile and block
 ]
 
 
