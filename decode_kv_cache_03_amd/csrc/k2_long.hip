@@ -28,9 +28,9 @@
 //    tile as columns holds its fragments already), then tiles 0..t0-1; the
 //    symmetric variant adds the tiles right of the block and, at the end, the
 //    own tiles above each wave's rows again;
-//  * column norms come from the B fragments of the step itself (the sum of
-//    squares of the 16 chunks each lane already reads), so no global norm
-//    array is read inside the stream;
+//  * the 1/||k|| of a tile's rows (from the statistics pass) travel with the
+//    tile into the ring, one 4-byte direct load per lane of 16 lanes per
+//    wave, so each wave issues 5 loads per tile and the waits count 5;
 //  * work items go to workgroups in order of decreasing cost, alternating
 //    direction each round (a greedy longest-first schedule): item k of round
 //    r is k = r*G + b for workgroup b on even rounds, r*G + G-1-b on odd ones.
@@ -77,8 +77,11 @@ __device__ __forceinline__ int sched(int r, int b, int G) {
   return r * G + ((r & 1) ? G - 1 - b : b);
 }
 
+constexpr int kPer = kLoadsPerTile + 1;   // loads per wave per tile: 4 of keys, 1 of norms
+
 template <int NQB, bool kSym, class P>
-__global__ __launch_bounds__(kThreads, 1) void k2l_kernel(P p, const float* __restrict__ fin,
+__global__ __launch_bounds__(kThreads, 1) void k2l_kernel(P p, const float* __restrict__ rinv,
+                                                         const float* __restrict__ fin,
                                                          float* __restrict__ Z,
                                                          float* __restrict__ Rdbg,
                                                          float* __restrict__ Idbg, float lam,
@@ -157,6 +160,13 @@ __global__ __launch_bounds__(kThreads, 1) void k2l_kernel(P p, const float* __re
     const int t = ld.g.tile(ld.k);
     char* slot = lds + issue_slot * kTileBytes;
     const T* urows = rows + it.row_base;
+    // 1/||k|| of tile rows 16w.. (rows past n repeat row n-1), 16 lanes x 4 bytes
+    if (lane_v < 16) {
+      const int rr = min(t * 128 + wave * 16 + lane_v, it.n - 1);
+      __builtin_amdgcn_global_load_lds(rinv + it.score_off + rr,
+                                       (__attribute__((address_space(3))) void*)(lds + L.rn + issue_slot * 512 + wave * 64),
+                                       4, 0, 0);
+    }
     const int row0 = t * 128 + wave * 16;   // first tile row this wave loads
     if ((t + 1) * 128 <= it.n) {
       const char* src = reinterpret_cast<const char*>(urows + (int64_t)row0 * kD);
@@ -227,14 +237,13 @@ __global__ __launch_bounds__(kThreads, 1) void k2l_kernel(P p, const float* __re
     // the wave's 64 rows against columns 64ch.. of tile t in `slot`. mode bit
     // 0: the columns are the wave's own rows (keep j < i, or j != i for the
     // symmetric R); bit 1: mask columns past n
-    auto half_step = [&](const char* slot, int t, int ch, int mode) {
+    auto half_step = [&](const char* slot, const float* rns, int t, int ch, int mode) {
       f32x16_t acc[2][2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x16_t{};
       const char* bs = slot + ch * 64 * kRowBytes;
-      float ss0 = 0.f, ss1 = 0.f;
 #pragma unroll
       for (int k = 0; k < kNch; ++k) {
         const u32x4_t b0 = ld16(bs + boff[k]);
@@ -244,14 +253,10 @@ __global__ __launch_bounds__(kThreads, 1) void k2l_kernel(P p, const float* __re
           mma_chunk<T>(acc[rb][0], af[rb][k], b0);
           mma_chunk<T>(acc[rb][1], af[rb][k], b1);
         }
-        ss0 += sumsq_chunk<T>(b0);
-        ss1 += sumsq_chunk<T>(b1);
       }
-      // 1/||k|| of this lane's two columns (the halves hold the two halves of a row)
-      ss0 += __shfl_xor(ss0, 32, 64);
-      ss1 += __shfl_xor(ss1, 32, 64);
-      const float r0 = ss0 > 0.f ? __frsqrt_rn(ss0) : 0.f;
-      const float r1 = ss1 > 0.f ? __frsqrt_rn(ss1) : 0.f;
+      // 1/||k|| of this lane's two columns
+      const float r0 = rns[ch * 64 + l32];
+      const float r1 = rns[ch * 64 + 32 + l32];
       if (mode == 0) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
@@ -287,10 +292,11 @@ __global__ __launch_bounds__(kThreads, 1) void k2l_kernel(P p, const float* __re
     const int len = g.len();
     for (int k = 0; k < len; ++k) {
       ensure_issued(c);
-      wait_tiles(issued - (c + 1));
+      wait_tiles<kPer>(issued - (c + 1));
       lds_barrier();
       refill(c);
       const char* slot = lds + cons_slot * kTileBytes;
+      const float* rns = reinterpret_cast<const float*>(lds + L.rn + cons_slot * 512);
       const int t = g.tile(k);
       const int cm = (partial_last && t == g.nb - 1) ? 2 : 0;
       // modes of the two 64-column halves for this wave (-1: not needed)
@@ -302,14 +308,10 @@ __global__ __launch_bounds__(kThreads, 1) void k2l_kernel(P p, const float* __re
           const int arow = hw * 64 + l32;
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb) {
-            float ss = 0.f;
 #pragma unroll
-            for (int kk = 0; kk < kNch; ++kk) {
+            for (int kk = 0; kk < kNch; ++kk)
               af[rb][kk] = ld16(slot + frag_offset<T>(arow + rb * 32, half * kNch + kk));
-              ss += sumsq_chunk<T>(af[rb][kk]);
-            }
-            ss += __shfl_xor(ss, 32, 64);
-            rnr[rb] = ss > 0.f ? __frsqrt_rn(ss) : 0.f;
+            rnr[rb] = rns[arow + rb * 32];
           }
           // only keys among the last w need the causal test
           const bool cz = causal && base + (d + 1) * 128 > n - W;
@@ -328,8 +330,8 @@ __global__ __launch_bounds__(kThreads, 1) void k2l_kernel(P p, const float* __re
         // other tiles; last (symmetric R), own tiles right of the wave's rows
         m0 = m1 = cm;
       }
-      if (wave_live && m0 >= 0) half_step(slot, t, 0, m0);
-      if (wave_live && m1 >= 0) half_step(slot, t, 1, m1);
+      if (wave_live && m0 >= 0) half_step(slot, rns, t, 0, m0);
+      if (wave_live && m1 >= 0) half_step(slot, rns, t, 1, m1);
       ++c;
       cons_slot = cons_slot + 1 == S ? 0 : cons_slot + 1;
     }
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2l_kernel(P p, const float* __re
 }
 
 template <int NQB, bool kSym, class P>
-static hipError_t run_t(const P& p, int count, const float* fin, float* Z, float* dbg_R,
+static hipError_t run_t(const P& p, int count, const float* rinv, const float* fin, float* Z, float* dbg_R,
                         float* dbg_I, float lam, int rpg_shift, const LongPlan& L,
                         hipStream_t st) {
   auto kern = k2l_kernel<NQB, kSym, P>;
@@ -379,36 +381,36 @@ static hipError_t run_t(const P& p, int count, const float* fin, float* Z, float
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   const int grid = min(cus, count);
-  return launch("rkv_k2_long", kern, dim3(grid), dim3(kThreads), L.total, st, p, fin, Z, dbg_R,
+  return launch("rkv_k2_long", kern, dim3(grid), dim3(kThreads), L.total, st, p, rinv, fin, Z, dbg_R,
                 dbg_I, lam, rpg_shift, L);
 }
 
 template <int NQB, class P>
-static hipError_t run_sym(const P& p, int count, const float* fin, float* Z, float* dbg_R,
-                          float* dbg_I, float lam, int rpg_shift, const LongPlan& L,
+static hipError_t run_sym(const P& p, int count, const float* rinv, const float* fin, float* Z,
+                          float* dbg_R, float* dbg_I, float lam, int rpg_shift, const LongPlan& L,
                           hipStream_t st) {
   if (p.symmetric())
-    return run_t<NQB, true>(p, count, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
-  return run_t<NQB, false>(p, count, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
+    return run_t<NQB, true>(p, count, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
+  return run_t<NQB, false>(p, count, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
 }
 
 }  // namespace longu
 
 template <class P>
-hipError_t run_k2_long(const P& p, int nqb, int count, const float* fin, float* Z, float* dbg_R,
-                       float* dbg_I, float lam, int rpg_shift, hipStream_t st) {
+hipError_t run_k2_long(const P& p, int nqb, int count, const float* rinv, const float* fin, float* Z,
+                       float* dbg_R, float* dbg_I, float lam, int rpg_shift, hipStream_t st) {
   const LongPlan L = long_plan_choose(p.G * p.W, nqb);
   if (L.total == 0) return hipErrorInvalidValue;
   if (count <= 0) return hipSuccess;
   switch (nqb) {
-    case 1: return longu::run_sym<1>(p, count, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
-    case 2: return longu::run_sym<2>(p, count, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
-    case 3: return longu::run_sym<3>(p, count, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
-    default: return longu::run_sym<4>(p, count, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
+    case 1: return longu::run_sym<1>(p, count, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
+    case 2: return longu::run_sym<2>(p, count, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
+    case 3: return longu::run_sym<3>(p, count, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
+    default: return longu::run_sym<4>(p, count, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
   }
 }
 
-template hipError_t run_k2_long<DenseProblem<bf16_bits>>(const DenseProblem<bf16_bits>&, int, int, const float*, float*, float*, float*, float, int, hipStream_t);
-template hipError_t run_k2_long<PagedProblem<bf16_bits>>(const PagedProblem<bf16_bits>&, int, int, const float*, float*, float*, float*, float, int, hipStream_t);
+template hipError_t run_k2_long<DenseProblem<bf16_bits>>(const DenseProblem<bf16_bits>&, int, int, const float*, const float*, float*, float*, float*, float, int, hipStream_t);
+template hipError_t run_k2_long<PagedProblem<bf16_bits>>(const PagedProblem<bf16_bits>&, int, int, const float*, const float*, float*, float*, float*, float, int, hipStream_t);
 
 }  // namespace rkv

@@ -251,7 +251,8 @@ int dense_run(const rkv_dense_desc* d, const void* K, const void* V, const void*
       if constexpr (sizeof(T) == 2) {
         // bf16: 512-row blocks by the long-unit kernel, then selection and gather
         const int count = units * ((p.N + 511) / 512);
-        e = rkv::run_k2_long(p, nqb, count, L.fin, z, dbg_R, dbg_I, d->mix_lambda, rpg_shift, st);
+        e = rkv::run_k2_long(p, nqb, count, L.rinv, L.fin, z, dbg_R, dbg_I, d->mix_lambda, rpg_shift,
+                             st);
         if (e != hipSuccess) return hip_fail(e, "redundancy launch");
         if (!shared) {
           e = rkv::run_k4(p, units, z, kept, 1, st);
@@ -557,7 +558,7 @@ int paged_run(const rkv_paged_desc* d, void* Kp, void* Vp, int32_t* page_table, 
                        rpg_shift, st);
     if (e != hipSuccess) return hip_fail(e, "importance launch");
     if constexpr (sizeof(T) == 2)
-      e = rkv::run_k2_long(p, P.nqb, p.long_cnt, L.fin, z, nullptr, nullptr, d->mix_lambda,
+      e = rkv::run_k2_long(p, P.nqb, p.long_cnt, L.rinv, L.fin, z, nullptr, nullptr, d->mix_lambda,
                            rpg_shift, st);
     else
       e = rkv::run_k2<T>(p, P.nqb, p.k2_count, L.rinv, L.fin, z, nullptr, nullptr, d->mix_lambda,

@@ -54,10 +54,11 @@ hipError_t run_k2_fused(const DenseProblem<bf16_bits>& p, int nqb, float* dbg_Z,
 
 // Long units (bf16): Z (R, I when requested) of every unit, one 512-row
 // block per work item (k2_long.hip); `count` = p.long_count(). Needs the
-// normalisers `fin` of run_k1; rows are read from p.long_rows().
+// norms `rinv` and normalisers `fin` of run_k1; rows are read from
+// p.long_rows().
 template <class P>
-hipError_t run_k2_long(const P& p, int nqb, int count, const float* fin, float* Z, float* dbg_R,
-                       float* dbg_I, float lam, int rpg_shift, hipStream_t st);
+hipError_t run_k2_long(const P& p, int nqb, int count, const float* rinv, const float* fin, float* Z,
+                       float* dbg_R, float* dbg_I, float lam, int rpg_shift, hipStream_t st);
 
 // Selection: kept indices per unit (ascending), from Z.
 template <class P>

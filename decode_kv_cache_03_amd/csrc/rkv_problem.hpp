@@ -107,16 +107,18 @@ struct LongItem {
   int64_t row_base, score_off;
 };
 
-// LDS plan of the long-unit kernel: a ring of `slots` 128-row bf16 tiles, and
-// per item parity the window queries and the softmax normalisers.
+// LDS plan of the long-unit kernel: a ring of `slots` 128-row bf16 tiles with
+// the 1/||k|| of their rows, and per item parity the window queries and the
+// softmax normalisers.
 struct LongPlan {
-  int slots, q, qbytes, stats, total;
+  int slots, rn, q, qbytes, stats, total;
 };
 
 __host__ __device__ inline LongPlan long_plan(int gw, int nqb, int slots) {
   LongPlan L;
   L.slots = slots;
-  L.q = slots * 128 * 256;
+  L.rn = slots * 128 * 256;
+  L.q = L.rn + slots * 128 * 4;
   L.qbytes = (gw * 256 + 1023) / 1024 * 1024;
   L.stats = L.q + 2 * L.qbytes;
   L.total = L.stats + 2 * nqb * 32 * 8;

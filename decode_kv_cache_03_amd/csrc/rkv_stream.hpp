@@ -24,17 +24,19 @@ constexpr int kLoadsPerTile = 4;     // per wave: 4 x 1 KiB of a 32 KiB tile
 constexpr int vm_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // Wait until every tile issued up to the one a step needs has landed:
-// `tiles_after` tiles were issued after it. Other memory operations issued
-// meanwhile only make the wait longer.
+// `tiles_after` tiles were issued after it, each as kPer loads per wave.
+// Other memory operations issued meanwhile only make the wait longer.
+template <int kPer = kLoadsPerTile>
 __device__ __forceinline__ void wait_tiles(int tiles_after) {
+  static_assert(3 * kPer <= 63, "vmcnt holds 6 bits");
   if (tiles_after <= 0)
     __builtin_amdgcn_s_waitcnt(vm_imm(0));
   else if (tiles_after == 1)
-    __builtin_amdgcn_s_waitcnt(vm_imm(kLoadsPerTile));
+    __builtin_amdgcn_s_waitcnt(vm_imm(kPer));
   else if (tiles_after == 2)
-    __builtin_amdgcn_s_waitcnt(vm_imm(2 * kLoadsPerTile));
+    __builtin_amdgcn_s_waitcnt(vm_imm(2 * kPer));
   else
-    __builtin_amdgcn_s_waitcnt(vm_imm(3 * kLoadsPerTile));
+    __builtin_amdgcn_s_waitcnt(vm_imm(3 * kPer));
 }
 
 // Importance of one key per lane from the lane's key fragments (both halves
