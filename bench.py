@@ -111,6 +111,7 @@ KERNEL_SOURCES = {
     "rkv_k4_group_select": ["k4_select.hip", "rkv_select.hpp"] + _HEADERS,
     "rkv_k5_gather": ["k5_compact.hip"] + _HEADERS,
     "rkv_k5_paged_compact": ["k5_compact.hip"] + _HEADERS,
+    "rkv_free_pages": ["k5_compact.hip"] + _HEADERS,
 }
 
 
