@@ -1,5 +1,5 @@
-// Redundancy R, importance I and joint score Z; for dense caches the same
-// kernel then selects and gathers each unit.
+// Redundancy R, importance I and joint score Z of fp32 caches; for dense
+// caches the same kernel then selects and gathers each unit.
 //
 // Pages: redundancy is measured by the cosine similarity of key vectors and
 // serves to find and prune near-duplicates (sourcepulse summary of R-KV,
@@ -17,8 +17,8 @@
 // tile), no causal window, mean pooling over the GQA heads.
 //
 // The cosine matrix is the one dense contraction of the step (N x N x 128
-// per unit), so it runs on bf16 MFMA with fp32 accumulation on the raw keys
-// (bf16 products are exact in fp32); the norms 1/||k|| are applied in the
+// per unit), so it runs on fp32 MFMA (v_mfma_f32_32x32x2_f32) on the raw
+// keys; the norms 1/||k|| are applied in the
 // fp32 epilogue, which keeps the cosine within fp32 rounding of exact.
 // Nothing N x N is ever stored: each lane keeps running row maxima in
 // registers.
@@ -611,9 +611,9 @@ hipError_t run_k2(const P& p, int nqb, int k2_items, const float* rinv, const fl
   template hipError_t run_k2<T, P>(const P&, int, int, const float*, const float*, float*, float*, \
                                    float*, float, int, int32_t*, int32_t*, T*, T*, int64_t, int,  \
                                    hipStream_t);
-RKV_K2_INST(bf16_bits, DenseProblem<bf16_bits>)
+// bf16 caches are scored by k2_wide.hip (dense units that fit a CU's LDS)
+// and k2_long.hip (longer dense units, paged caches)
 RKV_K2_INST(float, DenseProblem<float>)
-RKV_K2_INST(bf16_bits, PagedProblem<bf16_bits>)
 RKV_K2_INST(float, PagedProblem<float>)
 
 }  // namespace rkv

@@ -203,3 +203,31 @@ def test_qwen_full_size_lambda_sweep(rkv):
         case.lam = lam
         sample = [int(x) for x in rng.choice(case.num_heads, 2, replace=False)]
         _device_case_checks(rkv, case, sample, f"qwen lam={lam}")
+
+
+def test_longest_unit_sampled(rkv):
+    """Two dense units of 32768 candidates (the longest sequences of the paged
+    workload), scored by the long-unit kernel: the oracle on all importance
+    values and on 96 sampled rows of R and Z; the selection is the unique one
+    for the device's own scores."""
+    import torch
+    n, b, w, lam = 32768, 8192, 8, 0.1
+    case = dense_case_device(9, 1, 1, 2, 4, n, b, w, lam, "bf16", 0.4, 0.02)
+    res = rkv.compress(case.K, case.V, case.Q, b, w, lam, debug=True)
+    torch.cuda.synchronize()
+    kept = res.kept_idx
+    idx = kept.long()[..., None].expand(-1, -1, 128)
+    assert par.bits_equal(res.K_out, torch.gather(case.K, 1, idx))
+    assert par.bits_equal(res.V_out, torch.gather(case.V, 1, idx))
+    rng = np.random.default_rng(9)
+    for h in range(2):
+        Kh = par.to_host_f32(case.K[h])
+        Qh = par.to_host_f32(case.Q[h])
+        I_ref = orc.importance(Kh, Qh, w)
+        par.assert_close(res.I[h].cpu().numpy(), I_ref, par.TOL_I, f"unit {h} I")
+        rows = np.concatenate([[0, 1, 127, 128, 511, 512, n - w - 1], rng.choice(n - w, 89, replace=False)])
+        R_ref = orc.redundancy_rows(Kh, rows)
+        par.assert_close(res.R[h].cpu().numpy()[rows], R_ref, par.TOL_RZ, f"unit {h} R")
+        z = res.Z[h].cpu().numpy()
+        par.assert_close(z[rows], lam * I_ref[rows] - (1 - lam) * R_ref, par.TOL_RZ, f"unit {h} Z")
+        assert np.array_equal(kept[h].cpu().numpy(), orc.select(z.astype(np.float64), n, b, w))
