@@ -43,6 +43,11 @@ def _check(case, res, heads=None, what=""):
                        Z[h] if Z is not None else None, what=f"{what} head {h}")
         if n < b:
             assert np.all(kept[h, n:] == -1)
+        elif Z is not None and n > b:
+            # given the device's own scores the selection is unique: it must
+            # be exactly the window plus the top by (Z desc, index asc)
+            assert np.array_equal(kept[h], orc.select(Z[h].astype(np.float64), n, b, case.window)), \
+                f"{what} head {h}: selection differs from the device scores' top-k"
 
 
 def test_tiny_fp32(rkv):

@@ -215,3 +215,25 @@ def test_paged_ragged_full_size(rkv):
     kept = kept_all[off[s] + h * b: off[s] + (h + 1) * b].cpu().numpy()
     # given the device scores, the selection is unique: window + top by (Z, index)
     assert np.array_equal(kept, orc.select(z.astype(np.float64), n, b, case.window))
+
+
+def test_two_runs_are_bit_identical(rkv):
+    """Same inputs twice: kept indices, scores, pages, page table and free
+    list (including its order) are bit-identical."""
+    import torch
+    case = paged_case_host(26, LENS, FRACS, kv_heads=2, gqa=2, window=8, lam=0.1)
+    outs = []
+    for _ in range(2):
+        res, ref, Kp, Vp, table, fl, junk = _run_host_case(rkv, case, free_prefix=2)
+        outs.append((res.kept_idx.clone(), res.Z.clone(), Kp.clone(), Vp.clone(), table.clone(),
+                     fl.clone(), res.free_count))
+    a, b = outs
+    assert torch.equal(a[0], b[0])
+    # scores exist only for sequences that were compressed (N > B)
+    _, zoff = _kept_offsets(case.seq_len, case.budget, case.kv_heads)
+    for s_, (n, bud) in enumerate(zip(case.seq_len, case.budget)):
+        if n > bud:
+            sl = slice(zoff[s_], zoff[s_] + case.kv_heads * int(n))
+            assert torch.equal(a[1][sl].view(torch.int32), b[1][sl].view(torch.int32)), f"seq {s_}"
+    assert par.bits_equal(a[2], b[2]) and par.bits_equal(a[3], b[3])
+    assert torch.equal(a[4], b[4]) and torch.equal(a[5], b[5]) and a[6] == b[6]
