@@ -354,7 +354,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the compression step is per-unit independent and "
-              f"this build has no multi-GPU path); got --gpus {args.gpus}", file=sys.stderr)
+              f"the library has no multi-GPU path); got --gpus {args.gpus}", file=sys.stderr)
         sys.exit(2)
 
     import torch
