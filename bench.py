@@ -46,6 +46,16 @@ WORKLOADS = {
 }
 
 
+# launch labels of the kernels that run the whole dense step in one launch
+# (register-resident keys for short units, the LDS tile ring otherwise)
+WHOLE_STEP = ("rkv_k2_resident", "rkv_k2_compress")
+
+
+def whole_step_label(times):
+    """The whole-step kernel among the timed launches (None if neither ran)."""
+    return next((k for k in WHOLE_STEP if k in times), None)
+
+
 def kernel_work(name, units, n, b, g, w, esize=2, symmetric=False, group=1):
     """Algorithmic work of one launch of `name`: (bound, amount, unit).
 
@@ -62,7 +72,7 @@ def kernel_work(name, units, n, b, g, w, esize=2, symmetric=False, group=1):
     row = d * esize
     nk = min(n, b)
     flops = units * n * (n - 1) * d * (2 if symmetric else 1)
-    if name == "rkv_k2_compress":
+    if name in WHOLE_STEP:
         if group > 1:
             nbytes = units * (n * row + g * w * row + 4 * n)
         else:
@@ -102,6 +112,7 @@ def source_hash(files):
 
 _HEADERS = ["rkv_device.hpp", "rkv_problem.hpp", "rkv_launch.hpp"]
 KERNEL_SOURCES = {
+    "rkv_k2_resident": ["k2_resident.hip", "rkv_select.hpp", "rkv_stream.hpp"] + _HEADERS,
     "rkv_k2_compress": ["k2_wide.hip", "k2_redundancy.hip", "rkv_select.hpp", "rkv_stream.hpp"] + _HEADERS,
     "rkv_k2_redundancy": ["k2_redundancy.hip", "rkv_select.hpp"] + _HEADERS,
     "rkv_k2_long": ["k2_long.hip", "rkv_stream.hpp"] + _HEADERS,
@@ -204,7 +215,7 @@ def run_decode_loop(args, wl, c, rkv):
     wall = time.perf_counter() - t0
     times = rkv.timing_read()
     rkv.timing_enable(False)
-    launches, total_ms = times["rkv_k2_compress"]
+    launches, total_ms = times[whole_step_label(times)]
     kern_ms = total_ms / launches
     ev = sorted(a.elapsed_time(b) for a, b in ev_pairs)
     out = {
@@ -408,7 +419,17 @@ def main():
                      workspace=ws, select_group=group, **variant)
 
     step = call
+    graph_label = "graph_replay"
     if args.graph:
+        # the label of the one launch a single-unit-selection call makes on
+        # the dense bf16 path, from an eager call (replays carry no events)
+        rkv.timing_enable(True)
+        call()
+        torch.cuda.synchronize()
+        eager = rkv.timing_read()
+        rkv.timing_enable(False)
+        if len(eager) == 1 and whole_step_label(eager) is not None:
+            graph_label = whole_step_label(eager)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -442,10 +463,7 @@ def main():
     times = rkv.timing_read()
     rkv.timing_enable(False)
     if args.graph:
-        # the graph of a single-unit-selection call holds one launch
-        # (rkv_k2_compress) on the fused path; otherwise the replay is named
-        name = "rkv_k2_compress" if (group == 1 and c["dtype"] == "bf16") else "graph_replay"
-        times = {name: (len(evs), sum(a.elapsed_time(b_) for a, b_ in evs))}
+        times = {graph_label: (len(evs), sum(a.elapsed_time(b_) for a, b_ in evs))}
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = units / (ms_per_step * 1e-3)
@@ -469,7 +487,7 @@ def main():
             v["tflops"] = amt / (v["avg_ms"] * 1e-3) / 1e12
         elif kb == "hbm":
             v["gbs"] = amt / (v["avg_ms"] * 1e-3) / 1e9
-        if k == "rkv_k2_compress":   # the contraction it also carries
+        if k in WHOLE_STEP:   # the contraction it also carries
             pairs = n * (n - 1) * (2 if args.symmetric else 1)
             v["tflops"] = units * pairs * 128 / (v["avg_ms"] * 1e-3) / 1e12
             v["mfma_frac"] = v["tflops"] / MFMA_BF16_PEAK_TFLOPS

@@ -1,0 +1,687 @@
+// Dense bf16 caches with units of at most 1152 candidates: the whole
+// compression step of a unit in one 8-wave workgroup that reads every key
+// from memory once, persistent over units, one workgroup per CU.
+//
+// Same arithmetic as k1_importance.hip and k2_redundancy.hip (pages and
+// readings cited there): softmax of the window queries over the unit's keys
+// (query r sees keys j <= N-w+r), mean over a head's w queries, max over the
+// GQA group; R_j = max_{i<j} cos(k_i, k_j) on bf16 MFMA with fp32
+// accumulation and the norms applied in the epilogue; Z = lambda*I -
+// (1-lambda)*R; the window plus the top B-w by (Z desc, index asc),
+// ascending; the kept K/V rows gathered.
+//
+// Shape:
+//  * the unit's 128-row key tiles stream once, in order, through a ring of
+//    three LDS slots filled by direct global->LDS loads (two tiles in flight
+//    while one is consumed; the stream runs on into the next unit's first
+//    tiles while a unit finishes);
+//  * the keys stay: global row block b (32 rows) of tiles 0..nb-2 is held by
+//    wave b % 8 in registers, as 16x16x32 MFMA fragments (lane l holds row
+//    l % 16 of a 16-row half, 16-byte chunks (l / 16) + 4*ks), with the
+//    1/||k|| of the accumulator rows the lane will meet. Eight waves of four
+//    blocks hold 1024 rows; the unit's last tile is never needed as earlier
+//    rows of a later tile and stays in its LDS slot;
+//  * when tile t lands, its keys j are the columns: every wave forms the dot
+//    products of the rows it holds (i < j) with the tile's 128 keys and keeps,
+//    per column, the max of dot * (1/||k_i||); a column's max is the max over
+//    the lane's accumulator rows, then over the four lane quarters, then over
+//    the eight waves through LDS. R_j = that max * (1/||k_j||), the same
+//    products in the same order as a max of cosines;
+//  * the owners of tile t's rows form their logits against the window queries
+//    (online max and sum of exponentials per query) and their norms as they
+//    copy them into registers;
+//  * at the end of the unit the importance of every key is formed again from
+//    the held fragments (queries as MFMA rows, so a key's weights lie in one
+//    lane column and reduce in-lane and over two lane exchanges), then Z,
+//    the selection on Z in LDS, the kept K rows written from registers (the
+//    last tile's from LDS) and the kept V rows gathered.
+// Variants: without the causal window the statistics and weights mask only
+// padding keys; mean pooling sums the heads' window means and divides by G.
+// The symmetric R needs later keys as well and is served by k2_wide.hip.
+// Under head-shared selection the kernel stops after writing Z.
+#include "rkv_problem.hpp"
+#include "rkv_launch.hpp"
+#include "rkv_select.hpp"
+#include "rkv_stream.hpp"
+
+namespace rkv {
+namespace resident {
+
+using stream::wait_tiles;
+
+constexpr int kThreads = 512;
+constexpr int kRowBytes = 256;                  // bf16 row of 128
+constexpr int kTileBytes = 128 * kRowBytes;
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// acc += A * B over 32 k-values (16x16 tile): lane l gives row / column
+// l % 16 and k-values 8*(l/16).. of its operand; lane l receives
+// C[4*(l/16) + v][l % 16] in acc[v].
+__device__ __forceinline__ void mma16(f32x4_t& acc, u32x4_t a, u32x4_t b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                               __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+}
+
+// Fragment of 16 rows of a swizzled 128-row tile (or of the query block):
+// lane l takes row r0 + l % 16, chunk (l / 16) + 4*ks for k-step ks.
+__device__ __forceinline__ void load_frag(const char* base, int r0, int lane, u32x4_t (&f)[4]) {
+  const int row = r0 + (lane & 15), q = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) f[ks] = ld16(base + frag_offset<bf16_bits>(row, q + 4 * ks));
+}
+
+// Query fragments of the window: MFMA row m = 16*qs + l%16 is query row r of
+// head g with m = g * 2^rpg_shift + r; padding rows are zero.
+__device__ __forceinline__ void load_queries(const char* qlds, int lane, int W, int G, int rpg_shift,
+                                             u32x4_t (&qf)[2][4]) {
+  const int rpg_mask = (1 << rpg_shift) - 1;
+  const int q = lane >> 4;
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    const int m = qs * 16 + (lane & 15);
+    const int g = m >> rpg_shift, r = m & rpg_mask;
+    const bool ok = g < G && r < W;
+    const int n = ok ? g * W + r : 0;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qf[qs][ks] = ok ? ld16(qlds + frag_offset<bf16_bits>(n, q + 4 * ks)) : zero16();
+  }
+}
+
+// 1/||k|| of the 32 rows of a fragment pair, written to rn[key0 + row] (each
+// row's four quarters add their partial sums; rows past N are padding).
+__device__ __forceinline__ void row_norms(const u32x4_t (&f)[2][4], int key0, int lane, float* rn) {
+#pragma unroll
+  for (int rs = 0; rs < 2; ++rs) {
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) ss += sumsq_chunk<bf16_bits>(f[rs][ks]);
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    const int key = key0 + rs * 16 + (lane & 15);
+    if (lane < 16) rn[key] = ss > 0.f ? __frsqrt_rn(ss) : 0.f;
+  }
+}
+
+// Online softmax statistics of the window queries over 32 keys: lane l owns
+// query columns l % 16 and 16 + l % 16 (mrun/srun [qs]).
+__device__ __forceinline__ void stats_update(const u32x4_t (&kf)[2][4], const u32x4_t (&qf)[2][4],
+                                             int key0, int N, int W, int G, int rpg_shift,
+                                             bool causal, int lane, float (&mrun)[2],
+                                             float (&srun)[2]) {
+  asm volatile("" : "+v"(lane));   // per call: keeps lane-derived masks out of loop preheaders
+  const int rpg_mask = (1 << rpg_shift) - 1;
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int ksb = 0; ksb < 2; ++ksb)
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) mma16(acc[ksb][qs], kf[ksb][ks], qf[qs][ks]);   // C[key][query]
+  // the block holds padding or keys that some window query cannot see
+  const bool edge = key0 + 32 > (causal ? N - W : N);
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    const int m = qs * 16 + (lane & 15);
+    const int g = m >> rpg_shift, r = m & rpg_mask;
+    const bool qok = g < G && r < W;
+    const int last = causal ? N - W + r : N - 1;   // last key visible to window query r
+    float lg[8];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int ksb = 0; ksb < 2; ++ksb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int key = key0 + ksb * 16 + 4 * (lane >> 4) + v;
+        float x = acc[ksb][qs][v] * kLogitScaleLog2;
+        if (edge || !qok) x = (qok && key <= last) ? x : -INFINITY;
+        lg[ksb * 4 + v] = x;
+        mt = fmaxf(mt, x);
+      }
+    const float mn = fmaxf(mrun[qs], mt);
+    if (mn != -INFINITY) {
+      float s = (mrun[qs] != -INFINITY) ? srun[qs] * fast_exp2(mrun[qs] - mn) : 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += fast_exp2(lg[i] - mn);
+      srun[qs] = s;
+      mrun[qs] = mn;
+    }
+  }
+}
+
+// Column maxima of dot(k_i, k_j) * (1/||k_i||) for one 32-row block against
+// 32 columns: rows are the block's fragments `af` with the 1/||k|| of the
+// lane's accumulator rows in `rr`; `bf` are the columns. `diag`: rows and
+// columns are the same 32 keys, and only row < column counts.
+__device__ __forceinline__ void pair_max(const u32x4_t (&af)[2][4], const float* rnrow,
+                                         const u32x4_t (&bf)[2][4], bool diag, int lane,
+                                         float (&cm)[2]) {
+  f32x4_t rr[2];
+  for (int rs = 0; rs < 2; ++rs) rr[rs] = *reinterpret_cast<const f32x4_t*>(rnrow + rs * 16 + 4 * (lane >> 4));
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+      for (int cs = 0; cs < 2; ++cs) mma16(acc[rs][cs], af[rs][ks], bf[cs][ks]);   // C[row][col]
+  if (!diag) {
+#pragma unroll
+    for (int cs = 0; cs < 2; ++cs)
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) cm[cs] = fmaxf(cm[cs], acc[rs][cs][v] * rr[rs][v]);
+  } else {
+    int lane_v = lane;   // re-materialised: keeps the masks out of loop preheaders
+    asm volatile("" : "+v"(lane_v));
+    const int row0 = 4 * (lane_v >> 4), col = lane_v & 15;
+#pragma unroll
+    for (int cs = 0; cs < 2; ++cs)
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) {
+        if (rs > cs) continue;   // every row follows every column
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const bool before = rs < cs || row0 + v < col;
+          if (before) cm[cs] = fmaxf(cm[cs], acc[rs][cs][v] * rr[rs][v]);
+        }
+      }
+  }
+}
+
+// As pair_max for 16 columns (column half cs of a 32-key block), with the
+// row norms read from rnrow.
+__device__ __forceinline__ void pair_max16(const u32x4_t (&af)[2][4], const float* rnrow,
+                                           const u32x4_t (&bf)[4], int cs, bool diag, int lane,
+                                           float& cm) {
+  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs) mma16(acc[rs], af[rs][ks], bf[ks]);
+  int lane_v = lane;   // re-materialised: keeps the masks out of loop preheaders
+  asm volatile("" : "+v"(lane_v));
+  const int row0 = 4 * (lane_v >> 4), col = lane_v & 15;
+#pragma unroll
+  for (int rs = 0; rs < 2; ++rs) {
+    if (diag && rs > cs) continue;   // every row follows every column
+    const f32x4_t rr = *reinterpret_cast<const f32x4_t*>(rnrow + rs * 16 + row0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const bool before = !diag || rs < cs || row0 + v < col;
+      if (before) cm = fmaxf(cm, acc[rs][v] * rr[v]);
+    }
+  }
+}
+
+// Max over the four lane quarters: lanes 0..15 end with the column maxima.
+__device__ __forceinline__ void publish_cols(float (&cm)[2], float* dst, int lane) {
+#pragma unroll
+  for (int cs = 0; cs < 2; ++cs) {
+    float x = fmaxf(cm[cs], __shfl_xor(cm[cs], 16, 64));
+    x = fmaxf(x, __shfl_xor(x, 32, 64));
+    if (lane < 16) dst[cs * 16 + lane] = x;
+  }
+}
+
+// Importance of 16 keys key0 + l%16 from their fragments (lane l's key is
+// l % 16 in every quarter): weights of the window queries as MFMA rows
+// (queries 16*qs + 4*(l/16) + v in acc[qs][v]), summed over a head's rows
+// and pooled over heads by in-lane steps and two lane exchanges, then
+// scaled by inv_pool (1/w; 1/(w*G) under mean pooling).
+__device__ __forceinline__ float key_importance16(const u32x4_t (&kf)[4], const u32x4_t (&qf)[2][4],
+                                                  const float (&smax)[2][4],
+                                                  const float (&sinv)[2][4], int key0, int N,
+                                                  int W, int rpg_shift, bool causal, bool mean,
+                                                  float inv_pool, int lane) {
+  asm volatile("" : "+v"(lane));   // per call: keeps lane-derived masks out of loop preheaders
+  const int rpg_mask = (1 << rpg_shift) - 1;
+  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) mma16(acc[qs], qf[qs][ks], kf[ks]);   // C[query][key]
+  const int key = key0 + (lane & 15);
+  const int q = lane >> 4;
+  // bit b of the query index m = 16 qs + 4 q + v: summed within a head
+  // (b < rpg_shift) or under mean pooling, else max over heads
+  auto comb = [&](float a, float b, int bit) {
+    return (mean || bit < rpg_shift) ? a + b : fmaxf(a, b);
+  };
+  float x[2];
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    float w[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = qs * 16 + 4 * q + v;
+      const float pr = fast_exp2(acc[qs][v] * kLogitScaleLog2 - smax[qs][v]) * sinv[qs][v];
+      const bool vis = !causal || key <= N - W + (m & rpg_mask);
+      w[v] = vis ? pr : 0.f;
+    }
+    x[qs] = comb(comb(w[0], w[1], 0), comb(w[2], w[3], 0), 1);
+    x[qs] = comb(x[qs], __shfl_xor(x[qs], 16, 64), 2);
+    x[qs] = comb(x[qs], __shfl_xor(x[qs], 32, 64), 3);
+  }
+  return comb(x[0], x[1], 4) * inv_pool;
+}
+
+template <int kHeld>
+__global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
+    DenseProblem<bf16_bits> p, float* __restrict__ Zdbg, float* __restrict__ Rdbg,
+    float* __restrict__ Idbg, float lam, float oml, float inv_pool, int rpg_shift,
+    int32_t* __restrict__ kept_all, bf16_bits* __restrict__ K_out, bf16_bits* __restrict__ V_out,
+    int64_t out_stride, int score_only, ResidentPlan L) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int S = L.slots;
+  const int N = p.N, W = p.W, G = p.G, gw = G * W, B = p.B;
+  const int nb = (N + 127) / 128;
+  const int nh = nb - 1;                        // tiles held in registers
+  const bool causal = p.causal();
+  const bool mean = p.pool_mean();
+  u32x2_t* const stats = reinterpret_cast<u32x2_t*>(lds + L.stats);   // (max, 1/sum) bits
+  float* const sred_m = reinterpret_cast<float*>(lds + L.sred);      // [8][32]
+  float* const sred_s = sred_m + 8 * 32;
+  float* const rn = reinterpret_cast<float*>(lds + L.rn);            // [nb*128] 1/||k||
+  int32_t* const pos = reinterpret_cast<int32_t*>(lds + L.rn);       // after scoring: output row
+  float* const zs = reinterpret_cast<float*>(lds + L.zs);            // [nb*128] R, then Z
+  int32_t* const ks = reinterpret_cast<int32_t*>(lds + L.ks);        // [B] kept
+  float* const part = reinterpret_cast<float*>(lds + L.part);        // [2][8][128]
+  float* const dpart = reinterpret_cast<float*>(lds + L.dpart);      // [4][128]
+  SelectScratch& ssh = *reinterpret_cast<SelectScratch*>(lds + L.sel);
+
+
+  // ---- loader: every unit's tiles once, in order, into the ring ----
+  int ld_u = blockIdx.x, ld_par = 0, ld_k = 0;
+  int issued = 0, issue_slot = 0;
+  // The loader runs at most one unit ahead of the consumer: the window
+  // queries of two units share the two query slots.
+  int ld_limit = blockIdx.x + 2 * gridDim.x;
+  auto issue_next = [&]() -> bool {
+    if (ld_u >= p.num_units || ld_u >= ld_limit) return false;
+    int lane_v = lane;   // per call: keeps lane-derived values out of the callers' loops
+    asm volatile("" : "+v"(lane_v));
+    // Tile load q (0..3) of wave w fills KiB 4w + q of a slot: tile row
+    // 16w + 4q + lane/16 at chunk position lane % 16, fetching chunk
+    // (lane % 16) ^ (row & 15) of that row.
+    int lofs[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r16 = (4 * q + lane_v / 16) & 15;
+      lofs[q] = (lane_v / 16) * kRowBytes + (((lane_v % 16) ^ r16) << 4);
+    }
+    if (ld_k == 0) {   // the unit's window queries, ahead of its first tile
+      const char* qsrc = reinterpret_cast<const char*>(p.q(ld_u));
+      const int qkb = L.qbytes / 1024;
+      char* qdst = lds + L.q + ld_par * L.qbytes;
+      for (int kb = wave; kb < qkb; kb += 8) {
+        const int n = kb * 4 + lane_v / 16;
+        const int c = (lane_v % 16) ^ (n & 15);
+        load16_to_lds(qsrc + min(n, gw - 1) * kRowBytes + c * 16, qdst + kb * 1024);
+      }
+    }
+    const int t = ld_k;
+    char* slot = lds + issue_slot * kTileBytes;
+    const int row0 = t * 128 + wave * 16;   // first tile row this wave loads
+    if ((t + 1) * 128 <= N) {
+      const char* src = reinterpret_cast<const char*>(p.krow(ld_u, row0));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) load16_to_lds(src + q * 1024 + lofs[q], slot + wave * 4096 + q * 1024);
+    } else {   // last tile of the unit: rows past N repeat row N-1
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = min(row0 + 4 * q + lane_v / 16, N - 1);
+        const int chunk_ofs = lofs[q] - (lane_v / 16) * kRowBytes;
+        load16_to_lds(reinterpret_cast<const char*>(p.krow(ld_u, r)) + chunk_ofs,
+                      slot + wave * 4096 + q * 1024);
+      }
+    }
+    ++issued;
+    issue_slot = issue_slot + 1 == S ? 0 : issue_slot + 1;
+    if (++ld_k == nb) {
+      ld_k = 0;
+      ld_u += gridDim.x;
+      ld_par ^= 1;
+    }
+    return true;
+  };
+  // c = the tile in use; its slot and those of the tiles after it are taken
+  auto refill = [&](int c) {
+    while (issued - c < S && issue_next()) {
+    }
+  };
+  auto ensure_issued = [&](int c) {
+    if (issued < c + 1) {
+      lds_barrier();
+      refill(c);
+    }
+  };
+
+  // R of the keys of tile tt from the column maxima (threads 0..127);
+  // with_diag: the last tile, whose own rows left theirs in dpart
+  auto finalize = [&](int tt, bool with_diag, int tid_f) {
+    const int j = tt * 128 + tid_f;
+    if (j < N) {
+      const float* pp = part + (tt & 1) * 1024 + tid_f;
+      float m = pp[0];
+#pragma unroll
+      for (int w = 1; w < 8; ++w) m = fmaxf(m, pp[w * 128]);
+      if (with_diag)
+        for (int r = 0; r <= (tid_f >> 5); ++r) m = fmaxf(m, dpart[r * 128 + tid_f]);
+      zs[j] = j == 0 ? 0.f : m * rn[j];
+    }
+  };
+
+  int c = 0, cons_slot = 0;
+  refill(0);
+
+  int par = 0;
+  for (int u = blockIdx.x; u < p.num_units; u += gridDim.x, par ^= 1) {
+    // per unit: keeps lane-derived values from living across units
+    int lane_u = lane, tid_u = tid;
+    asm volatile("" : "+v"(lane_u), "+v"(tid_u));
+    ld_limit = u + 2 * gridDim.x;
+    const int64_t so = p.score_off(u);
+    const char* qlds = lds + L.q + par * L.qbytes;
+    float mrun[2] = {-INFINITY, -INFINITY}, srun[2] = {0.f, 0.f};
+    // (declared per unit: nothing held lives on into the next unit)
+    u32x4_t A[kHeld][2][4];   // held row blocks: slot s = row block 8s + wave
+
+    // ---------------- the tile stream: statistics, norms, R ----------------
+    for (int t = 0; t < nb; ++t) {
+      ensure_issued(c);
+      wait_tiles(issued - (c + 1));
+      lds_barrier();
+      refill(c);
+      const char* slot = lds + cons_slot * kTileBytes;
+      if (t > 0 && tid_u < 128) finalize(t - 1, false, tid_u);
+
+      // the owner of each of tile t's row blocks copies it into registers
+      // (tiles before the last) with its norms; the logits of a held block
+      // against the window queries follow one step later, when its owner is
+      // not copying, so each step carries half of both
+      if (t < nh && (wave >> 2) == (t & 1)) {
+        const int key0 = t * 128 + (wave & 3) * 32;
+#pragma unroll
+        for (int s = 0; s < kHeld; ++s) {
+          if (s != (t >> 1)) continue;
+          load_frag(slot, (wave & 3) * 32, lane_u, A[s][0]);
+          load_frag(slot, (wave & 3) * 32 + 16, lane_u, A[s][1]);
+          row_norms(A[s], key0, lane_u, rn);
+        }
+      }
+
+      // columns: the tile's keys against every held row before them
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        u32x4_t bf[2][4];
+        load_frag(slot, cb * 32, lane_u, bf[0]);
+        load_frag(slot, cb * 32 + 16, lane_u, bf[1]);
+        float cm[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+        for (int s = 0; s < kHeld; ++s) {
+          const int gb = 8 * s + wave;
+          if (gb >= 4 * nh || gb > 4 * t + 3) continue;
+          const bool diag = (gb >> 2) == t;
+          if (diag && (gb & 3) > cb) continue;
+          pair_max(A[s], rn + gb * 32, bf, diag && (gb & 3) == cb, lane_u, cm);
+        }
+        publish_cols(cm, part + (t & 1) * 1024 + wave * 128 + cb * 32, lane_u);
+      }
+      // statistics of the block this wave copied at step t-1
+      if (t >= 1 && t - 1 < nh && (wave >> 2) == ((t - 1) & 1)) {
+        const int key0 = (t - 1) * 128 + (wave & 3) * 32;
+#pragma unroll
+        for (int s = 0; s < kHeld; ++s) {
+          if (s != ((t - 1) >> 1)) continue;
+          u32x4_t qf[2][4];
+          load_queries(qlds, lane_u, W, G, rpg_shift, qf);
+          stats_update(A[s], qf, key0, N, W, G, rpg_shift, causal, lane_u, mrun, srun);
+        }
+      }
+      if (t < nh) {
+        ++c;
+        cons_slot = cons_slot + 1 == S ? 0 : cons_slot + 1;
+      }
+    }
+
+    // ---------------- the last tile's own rows ----------------
+    const int tl = nb - 1;
+    const char* lslot = lds + cons_slot * kTileBytes;
+    if ((wave >> 2) == (tl & 1)) {
+      const int r = wave & 3;
+      const int key0 = tl * 128 + r * 32;
+      u32x4_t af[2][4];
+      load_frag(lslot, r * 32, lane_u, af[0]);
+      load_frag(lslot, r * 32 + 16, lane_u, af[1]);
+      row_norms(af, key0, lane_u, rn);
+      f32x4_t rr[2];
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs)
+        rr[rs] = *reinterpret_cast<const f32x4_t*>(rn + key0 + rs * 16 + 4 * (lane_u >> 4));
+      {
+        u32x4_t qf[2][4];
+        load_queries(qlds, lane_u, W, G, rpg_shift, qf);
+        stats_update(af, qf, key0, N, W, G, rpg_shift, causal, lane_u, mrun, srun);
+      }
+      // rows past N (a copy of row N-1) only meet columns before them, which
+      // the diagonal mask drops, or columns past N, which are never read
+      for (int cb = r; cb < 4; ++cb) {
+        float cm[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+        for (int cs = 0; cs < 2; ++cs) {
+          u32x4_t bf[4];
+          load_frag(lslot, cb * 32 + cs * 16, lane_u, bf);
+          pair_max16(af, rn + key0, bf, cs, cb == r, lane_u, cm[cs]);
+        }
+        publish_cols(cm, dpart + r * 128 + cb * 32, lane_u);
+      }
+    }
+    // statistics of the wave: merge the four lane_u quarters
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      float m = mrun[qs], s = srun[qs];
+#pragma unroll
+      for (int sh = 16; sh <= 32; sh <<= 1) {
+        const float m2 = __shfl_xor(m, sh, 64), s2 = __shfl_xor(s, sh, 64);
+        const float mm = fmaxf(m, m2);
+        float st = 0.f;
+        if (mm != -INFINITY)
+          st = (m != -INFINITY ? s * fast_exp2(m - mm) : 0.f) +
+               (m2 != -INFINITY ? s2 * fast_exp2(m2 - mm) : 0.f);
+        m = mm;
+        s = st;
+      }
+      if (lane_u < 16) {
+        sred_m[wave * 32 + qs * 16 + lane_u] = m;
+        sred_s[wave * 32 + qs * 16 + lane_u] = s;
+      }
+    }
+    lds_barrier();
+    if (tid_u < 128) {
+      finalize(tl, true, tid_u);
+    } else if (tid_u < 160) {
+      const int m = tid_u - 128;
+      float mm = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) mm = fmaxf(mm, sred_m[w * 32 + m]);
+      float st = 0.f;
+      if (mm != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const float em = sred_m[w * 32 + m], es = sred_s[w * 32 + m];
+          if (em != -INFINITY) st += es * fast_exp2(em - mm);
+        }
+      }
+      const bool seen = mm != -INFINITY && st > 0.f;
+      stats[m] = u32x2_t{__float_as_uint(seen ? mm : 0.f), __float_as_uint(seen ? 1.0f / st : 0.f)};
+    }
+    lds_barrier();
+
+    // ---------------- importance and Z ----------------
+    {
+      u32x4_t qf[2][4];
+      load_queries(qlds, lane_u, W, G, rpg_shift, qf);
+      float smax[2][4], sinv[2][4];
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const u32x2_t st = stats[qs * 16 + 4 * (lane_u >> 4) + v];
+          smax[qs][v] = __uint_as_float(st.x);
+          sinv[qs][v] = __uint_as_float(st.y);
+        }
+      // importance of every key the wave holds first (independent chains),
+      // then Z over R in place
+      float Ih[kHeld][2], Il[2] = {0.f, 0.f};
+      const bool lown = (wave >> 2) == (tl & 1);   // owns a row block of the last tile
+      const int lkey0 = tl * 128 + (wave & 3) * 32;
+#pragma unroll
+      for (int s = 0; s < kHeld; ++s) {
+        const int gb = 8 * s + wave;
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs)
+          Ih[s][rs] = gb < 4 * nh ? key_importance16(A[s][rs], qf, smax, sinv, gb * 32 + rs * 16,
+                                                     N, W, rpg_shift, causal, mean, inv_pool,
+                                                     lane_u)
+                                  : 0.f;
+      }
+      if (lown) {
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs) {
+          u32x4_t kf[4];
+          load_frag(lslot, (wave & 3) * 32 + rs * 16, lane_u, kf);
+          Il[rs] = key_importance16(kf, qf, smax, sinv, lkey0 + rs * 16, N, W, rpg_shift, causal,
+                                    mean, inv_pool, lane_u);
+        }
+      }
+      auto put = [&](float I, int key0) {
+        const int key = key0 + (lane_u & 15);
+        if (lane_u < 16 && key < N) {
+          const float R = zs[key];
+          const float z = lam * I - oml * R + 0.0f;   // + 0 folds -0 onto +0
+          zs[key] = z;
+          if (Zdbg != nullptr) Zdbg[so + key] = z;
+          if (Rdbg != nullptr) Rdbg[so + key] = R;
+          if (Idbg != nullptr) Idbg[so + key] = I;
+        }
+      };
+#pragma unroll
+      for (int s = 0; s < kHeld; ++s) {
+        const int gb = 8 * s + wave;
+        if (gb >= 4 * nh) continue;
+        put(Ih[s][0], gb * 32);
+        put(Ih[s][1], gb * 32 + 16);
+      }
+      if (lown) {
+        put(Il[0], lkey0);
+        put(Il[1], lkey0 + 16);
+      }
+    }
+
+    // ---------------- selection and gather ----------------
+    // (score_only: Z went to Zdbg; a later launch selects for groups of units)
+    if (!score_only) {
+      __syncthreads();
+      int32_t* kept = kept_all + p.kept_off(u);
+      select_block<kThreads>(zs, N, B, W, kept, ssh, ks);
+      __syncthreads();
+      // output row of every candidate (-1: dropped), in the norms' place
+      for (int i = tid_u; i < N; i += kThreads) pos[i] = -1;
+      __syncthreads();
+      for (int r = tid_u; r < B; r += kThreads) pos[ks[r]] = r;
+      __syncthreads();
+      bf16_bits* Ko = K_out + (int64_t)u * out_stride;
+      // kept rows held in registers: lane_u quarter q writes chunks q + 4*ks,
+      // so the four quarters of a row fill 64 contiguous bytes per store
+#pragma unroll
+      for (int s = 0; s < kHeld; ++s) {
+        const int gb = 8 * s + wave;
+        if (gb >= 4 * nh) continue;
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs) {
+          const int o = pos[gb * 32 + rs * 16 + (lane_u & 15)];
+          if (o >= 0) {
+            char* dst = reinterpret_cast<char*>(Ko + (int64_t)o * kD) + (lane_u >> 4) * 16;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) st16(dst + k * 64, A[s][rs][k]);
+          }
+        }
+      }
+      // kept rows of the last tile, from its slot: four threads per row
+      {
+        const int x = tid_u >> 2, qq = tid_u & 3;
+        const int i = tl * 128 + x;
+        const int o = i < N ? pos[i] : -1;
+        if (o >= 0) {
+          char* dst = reinterpret_cast<char*>(Ko + (int64_t)o * kD);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int ch = qq * 4 + k;
+            st16(dst + ch * 16, ld16(lslot + frag_offset<bf16_bits>(x, ch)));
+          }
+        }
+      }
+      gather_rows_block<bf16_bits, kThreads>(ks, B, [&](int r) { return p.vrow(u, r); },
+                                             V_out + (int64_t)u * out_stride);
+    }
+    // release the last tile's slot (the next unit's first barrier orders it)
+    ++c;
+    cons_slot = cons_slot + 1 == S ? 0 : cons_slot + 1;
+  }
+}
+
+template <int kHeld>
+static hipError_t run_t(const DenseProblem<bf16_bits>& p, float* dbg_Z, float* dbg_R, float* dbg_I,
+                        float lam, int rpg_shift, int32_t* kept, bf16_bits* K_out,
+                        bf16_bits* V_out, int64_t out_stride, int score_only,
+                        const ResidentPlan& L, hipStream_t st) {
+  auto kern = k2r_kernel<kHeld>;
+  const void* fn = reinterpret_cast<const void*>(kern);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
+  int dev = 0, cus = 0;
+  if (e == hipSuccess) e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int grid = min(cus, p.num_units);   // one workgroup per CU, whole units each
+  // 1 - lambda and the pooling scale as arguments: uniform values that stay in
+  // scalar registers
+  const float oml = 1.0f - lam;
+  const float inv_pool = p.pool_mean() ? 1.0f / (float)(p.W * p.G) : 1.0f / (float)p.W;
+  return launch("rkv_k2_resident", kern, dim3(grid), dim3(kThreads), L.total, st, p, dbg_Z, dbg_R,
+                dbg_I, lam, oml, inv_pool, rpg_shift, kept, K_out, V_out, out_stride, score_only,
+                L);
+}
+
+}  // namespace resident
+
+bool k2_resident_fits(const DenseProblem<bf16_bits>& p, int nqb) {
+  const int nb = (p.N + 127) / 128;
+  return nqb == 1 && !p.symmetric() && nb - 1 <= 2 * kResidentHeld &&
+         resident_plan(p.N, p.B, p.G * p.W).total > 0;
+}
+
+hipError_t run_k2_resident(const DenseProblem<bf16_bits>& p, int nqb, float* dbg_Z, float* dbg_R,
+                           float* dbg_I, float lam, int rpg_shift, int32_t* kept,
+                           bf16_bits* K_out, bf16_bits* V_out, int64_t out_stride, int score_only,
+                           hipStream_t st) {
+  if (!k2_resident_fits(p, nqb) || (score_only && dbg_Z == nullptr)) return hipErrorInvalidValue;
+  const ResidentPlan L = resident_plan(p.N, p.B, p.G * p.W);
+  return resident::run_t<kResidentHeld>(p, dbg_Z, dbg_R, dbg_I, lam, rpg_shift, kept, K_out, V_out,
+                                        out_stride, score_only, L, st);
+}
+
+}  // namespace rkv

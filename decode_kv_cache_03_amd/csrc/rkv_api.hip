@@ -235,7 +235,14 @@ int dense_run(const rkv_dense_desc* d, const void* K, const void* V, const void*
     float* z = dbg_Z ? dbg_Z : L.z;
     bool scored = false;
     if constexpr (sizeof(T) == 2) {
-      if (rkv::fused_plan_choose(p.N, p.B, p.G * p.W, nqb).total > 0) {
+      if (rkv::k2_resident_fits(p, nqb)) {
+        // every key read once, the first N-128 held in registers
+        e = rkv::run_k2_resident(p, nqb, shared ? z : dbg_Z, dbg_R, dbg_I, d->mix_lambda,
+                                 rpg_shift, kept, static_cast<T*>(K_out), static_cast<T*>(V_out),
+                                 out_stride, shared ? 1 : 0, st);
+        if (e != hipSuccess) return hip_fail(e, "compression launch");
+        scored = true;
+      } else if (rkv::fused_plan_choose(p.N, p.B, p.G * p.W, nqb).total > 0) {
         e = rkv::run_k2_fused(p, nqb, shared ? z : dbg_Z, dbg_R, dbg_I, d->mix_lambda, rpg_shift,
                               kept, static_cast<T*>(K_out), static_cast<T*>(V_out), out_stride,
                               shared ? 1 : 0, st);

@@ -52,6 +52,16 @@ hipError_t run_k2_fused(const DenseProblem<bf16_bits>& p, int nqb, float* dbg_Z,
                         float* dbg_I, float lam, int rpg_shift, int32_t* kept, bf16_bits* K_out,
                         bf16_bits* V_out, int64_t out_stride, int score_only, hipStream_t st);
 
+// Dense bf16 caches with at most 1024 + 128 candidates per unit, one window
+// query block and the causal-order R (k2_resident_fits): the whole step in
+// one launch that reads every key once (k2_resident.hip). Arguments as
+// run_k2_fused.
+bool k2_resident_fits(const DenseProblem<bf16_bits>& p, int nqb);
+hipError_t run_k2_resident(const DenseProblem<bf16_bits>& p, int nqb, float* dbg_Z, float* dbg_R,
+                           float* dbg_I, float lam, int rpg_shift, int32_t* kept,
+                           bf16_bits* K_out, bf16_bits* V_out, int64_t out_stride, int score_only,
+                           hipStream_t st);
+
 // Long units (bf16): Z (R, I when requested) of every unit, one 512-row
 // block per work item (k2_long.hip); `count` = p.long_count(). Needs the
 // norms `rinv` and normalisers `fin` of run_k1; rows are read from

@@ -85,6 +85,39 @@ __host__ __device__ inline FusedPlan fused_plan_choose(int N, int B, int gw, int
   return none;
 }
 
+// LDS plan of the register-resident dense bf16 kernel (k2_resident.hip): a
+// ring of `slots` 128-row bf16 tiles, two slots of window queries, the
+// softmax normalisers and their per-wave partials, 1/||k|| (later the output
+// row of each candidate) and R then Z over the unit's padded tiles, the kept
+// indices, two rounds of per-wave column maxima, the last tile's own column
+// maxima, and selection scratch.
+struct ResidentPlan {
+  int slots, q, qbytes, stats, sred, rn, zs, ks, part, dpart, sel, total;
+};
+
+// Row blocks of 32 keys each wave holds in registers: 8 waves x 4 x 32 =
+// 1024 rows, so units of up to 1024 + 128 candidates.
+constexpr int kResidentHeld = 4;
+
+__host__ __device__ inline ResidentPlan resident_plan(int N, int B, int gw) {
+  ResidentPlan L;
+  const int nb = (N + 127) / 128;
+  L.slots = 3;
+  L.q = L.slots * 128 * 256;
+  L.qbytes = (gw * 256 + 1023) / 1024 * 1024;
+  L.stats = L.q + 2 * L.qbytes;
+  L.sred = L.stats + 32 * 8;
+  L.rn = L.sred + 2 * 8 * 32 * 4;
+  L.zs = L.rn + nb * 128 * 4;
+  L.ks = L.zs + nb * 128 * 4;
+  L.part = L.ks + round16((int64_t)B * 4);
+  L.dpart = L.part + 2 * 8 * 128 * 4;
+  L.sel = L.dpart + 4 * 128 * 4;
+  L.total = L.sel + round16(sizeof(SelectScratch));
+  if (L.total > kLdsBytesPerCU) L.total = 0;
+  return L;
+}
+
 // Reading variants of a call (bits as in rkv.h): the defaults are R over
 // earlier candidates, the causal window and max pooling over the GQA heads.
 constexpr uint32_t kVariantSymmetric = 1u;   // R_i over every j != i

@@ -186,4 +186,47 @@ __device__ __forceinline__ void gather_rows_block(const int32_t* __restrict__ ke
   }
 }
 
+// One row source: rows kept[0..nkeep) into consecutive output rows, in rounds
+// of U 16-byte chunks per thread, two rounds in flight, streaming loads and
+// stores, branch-free tails (as gather_rows_block).
+template <typename T, int NT, class Src>
+__device__ __forceinline__ void gather_rows_block(const int32_t* __restrict__ kept, int nkeep,
+                                                  Src src, T* __restrict__ out) {
+  constexpr int RC = Elem<T>::kRowChunks;
+  constexpr int U = 8;
+  constexpr int kRound = NT * U;   // chunks per round
+  const int total = nkeep * RC;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));   // keeps thread-derived values from being hoisted into callers' loops
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(out, 0, total * 16, kBufferWord3);
+  auto load_round = [&](int q0, u32x4_t (&vv)[U]) {
+    int row[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int q = q0 + j * NT + tid;
+      row[j] = kept[q < total ? q / RC : 0];
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int c = (q0 + j * NT + tid) % RC;
+      vv[j] = ld16_stream(reinterpret_cast<const char*>(src(row[j])) + 16 * c);
+    }
+  };
+  auto store_round = [&](int q0, const u32x4_t (&vv)[U]) {
+    const int ofs = (q0 + tid) * 16;
+#pragma unroll
+    for (int j = 0; j < U; ++j)
+      __builtin_amdgcn_raw_buffer_store_b128(vv[j], ro, ofs, j * NT * 16, kCachePolicyStream);
+  };
+  u32x4_t a[U], b[U];
+  if (total > 0) load_round(0, a);
+  for (int q0 = 0; q0 < total; q0 += 2 * kRound) {
+    if (q0 + kRound < total) load_round(q0 + kRound, b);
+    store_round(q0, a);
+    if (q0 + kRound >= total) break;
+    if (q0 + 2 * kRound < total) load_round(q0 + 2 * kRound, a);
+    store_round(q0 + kRound, b);
+  }
+}
+
 }  // namespace rkv
