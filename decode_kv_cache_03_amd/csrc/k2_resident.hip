@@ -47,13 +47,36 @@
 namespace rkv {
 namespace resident {
 
-using stream::wait_tiles;
+using stream::vm_imm;
 
 constexpr int kThreads = 512;
 constexpr int kRowBytes = 256;                  // bf16 row of 128
 constexpr int kTileBytes = 128 * kRowBytes;
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Wait until at most n vector-memory instructions of this wave are in
+// flight (n rounded down to a multiple of 4: never a shorter wait).
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n <= 0 ? 0 : (n >= 60 ? 15 : n >> 2)) {
+    case 0: __builtin_amdgcn_s_waitcnt(vm_imm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vm_imm(4)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vm_imm(8)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vm_imm(12)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(vm_imm(16)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(vm_imm(20)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(vm_imm(24)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(vm_imm(28)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(vm_imm(32)); break;
+    case 9: __builtin_amdgcn_s_waitcnt(vm_imm(36)); break;
+    case 10: __builtin_amdgcn_s_waitcnt(vm_imm(40)); break;
+    case 11: __builtin_amdgcn_s_waitcnt(vm_imm(44)); break;
+    case 12: __builtin_amdgcn_s_waitcnt(vm_imm(48)); break;
+    case 13: __builtin_amdgcn_s_waitcnt(vm_imm(52)); break;
+    case 14: __builtin_amdgcn_s_waitcnt(vm_imm(56)); break;
+    default: __builtin_amdgcn_s_waitcnt(vm_imm(60)); break;
+  }
+}
 
 // acc += A * B over 32 k-values (16x16 tile): lane l gives row / column
 // l % 16 and k-values 8*(l/16).. of its operand; lane l receives
@@ -290,6 +313,8 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
   const int N = p.N, W = p.W, G = p.G, gw = G * W, B = p.B;
   const int nb = (N + 127) / 128;
   const int nh = nb - 1;                        // tiles held in registers
+  const int kv_total = (16 * B + kThreads - 1) / kThreads;   // V chunks per thread per unit
+  const int kps = (kv_total + nb - 1) / nb;                  // ... per tile step (at most 4)
   const bool causal = p.causal();
   const bool mean = p.pool_mean();
   u32x2_t* const stats = reinterpret_cast<u32x2_t*>(lds + L.stats);   // (max, 1/sum) bits
@@ -301,8 +326,17 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
   int32_t* const ks = reinterpret_cast<int32_t*>(lds + L.ks);        // [B] kept
   float* const part = reinterpret_cast<float*>(lds + L.part);        // [2][8][128]
   float* const dpart = reinterpret_cast<float*>(lds + L.dpart);      // [4][128]
+  char* const vstage = lds + L.vstage;                               // [8 waves][4][1 KiB]
   SelectScratch& ssh = *reinterpret_cast<SelectScratch*>(lds + L.sel);
 
+
+  // Vector-memory instructions this wave has issued (vm), and the count just
+  // after each ring slot's tile: waiting for a tile allows exactly the
+  // instructions issued after it to stay in flight. Every instruction
+  // counted here is issued unconditionally by the whole wave (stores of
+  // dropped rows go past the end of their buffer, which discards them);
+  // uncounted ones only lengthen a wait.
+  int vm = 0, mark0 = 0, mark1 = 0;
 
   // ---- loader: every unit's tiles once, in order, into the ring ----
   int ld_u = blockIdx.x, ld_par = 0, ld_k = 0;
@@ -331,6 +365,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
         const int n = kb * 4 + lane_v / 16;
         const int c = (lane_v % 16) ^ (n & 15);
         load16_to_lds(qsrc + min(n, gw - 1) * kRowBytes + c * 16, qdst + kb * 1024);
+        ++vm;
       }
     }
     const int t = ld_k;
@@ -349,6 +384,11 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
                       slot + wave * 4096 + q * 1024);
       }
     }
+    vm += 4;
+    if (issue_slot == 0)
+      mark0 = vm;
+    else
+      mark1 = vm;
     ++issued;
     issue_slot = issue_slot + 1 == S ? 0 : issue_slot + 1;
     if (++ld_k == nb) {
@@ -386,6 +426,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
   };
 
   int c = 0, cons_slot = 0;
+  int last_u = -1;   // the last unit whose kept V rows are still to move
   refill(0);
 
   int par = 0;
@@ -397,16 +438,32 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
     const int64_t so = p.score_off(u);
     const char* qlds = lds + L.q + par * L.qbytes;
     float mrun[2] = {-INFINITY, -INFINITY}, srun[2] = {0.f, 0.f};
+    // the kept V rows of this workgroup's previous unit move during this
+    // unit's tile steps, kps 16-byte chunks per thread per step
+    const int pu = u - (int)gridDim.x;
+    const bool vg = !score_only && pu >= (int)blockIdx.x;
     // (declared per unit: nothing held lives on into the next unit)
     u32x4_t A[kHeld][2][4];   // held row blocks: slot s = row block 8s + wave
 
     // ---------------- the tile stream: statistics, norms, R ----------------
     for (int t = 0; t < nb; ++t) {
       ensure_issued(c);
-      wait_tiles(issued - (c + 1));
+      wait_vm(vm - (cons_slot == 0 ? mark0 : mark1));
       lds_barrier();
       refill(c);
       const char* slot = lds + cons_slot * kTileBytes;
+      // a slice of the previous unit's kept V rows, into this wave's staging
+      // (lane order); stored at the end of the step
+      const int nv = vg ? max(0, min(kps, kv_total - t * kps)) : 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j >= nv) continue;
+        const int q = (t * kps + j) * kThreads + tid_u;
+        const int r = min(q >> 4, B - 1);   // chunks past the end re-read a kept row
+        load16_to_lds(reinterpret_cast<const char*>(p.vrow(pu, ks[r])) + (q & 15) * 16,
+                      vstage + (wave * 4 + j) * 1024);
+      }
+      vm += nv;
       if (t > 0 && tid_u < 128) finalize(t - 1, false, tid_u);
 
       // the owner of each of tile t's row blocks copies it into registers
@@ -452,6 +509,20 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
           stats_update(A[s], qf, key0, N, W, G, rpg_shift, causal, lane_u, mrun, srun);
         }
       }
+      if (nv > 0) {
+        __builtin_amdgcn_s_waitcnt(vm_imm(0));   // the wave's V chunks have landed
+        asm volatile("" ::: "memory");
+        const __amdgpu_buffer_rsrc_t vo = __builtin_amdgcn_make_buffer_rsrc(
+            V_out + (int64_t)pu * out_stride, 0, B * kRowBytes, kBufferWord3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (j >= nv) continue;
+          const int q = (t * kps + j) * kThreads + tid_u;   // chunks past B rows: dropped
+          __builtin_amdgcn_raw_buffer_store_b128(ld16(vstage + (wave * 4 + j) * 1024 + lane_u * 16),
+                                                 vo, q * 16, 0, kCachePolicyStream);
+        }
+        vm += nv;
+      }
       if (t < nh) {
         ++c;
         cons_slot = cons_slot + 1 == S ? 0 : cons_slot + 1;
@@ -479,7 +550,9 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
       }
       // rows past N (a copy of row N-1) only meet columns before them, which
       // the diagonal mask drops, or columns past N, which are never read
-      for (int cb = r; cb < 4; ++cb) {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        if (cb < r) continue;
         float cm[2] = {-INFINITY, -INFINITY};
 #pragma unroll
         for (int cs = 0; cs < 2; ++cs) {
@@ -604,9 +677,12 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
       __syncthreads();
       for (int r = tid_u; r < B; r += kThreads) pos[ks[r]] = r;
       __syncthreads();
-      bf16_bits* Ko = K_out + (int64_t)u * out_stride;
-      // kept rows held in registers: lane_u quarter q writes chunks q + 4*ks,
-      // so the four quarters of a row fill 64 contiguous bytes per store
+      // kept K rows held in registers: lane quarter q writes chunks q + 4*ks,
+      // so the four quarters of a row fill 64 contiguous bytes per store;
+      // rows that are dropped store past the end of the buffer
+      const __amdgpu_buffer_rsrc_t ko = __builtin_amdgcn_make_buffer_rsrc(
+          K_out + (int64_t)u * out_stride, 0, B * kRowBytes, kBufferWord3);
+      const int past = B * kRowBytes;
 #pragma unroll
       for (int s = 0; s < kHeld; ++s) {
         const int gb = 8 * s + wave;
@@ -614,34 +690,37 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
 #pragma unroll
         for (int rs = 0; rs < 2; ++rs) {
           const int o = pos[gb * 32 + rs * 16 + (lane_u & 15)];
-          if (o >= 0) {
-            char* dst = reinterpret_cast<char*>(Ko + (int64_t)o * kD) + (lane_u >> 4) * 16;
+          const int ofs = o >= 0 ? o * kRowBytes + (lane_u >> 4) * 16 : past;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) st16(dst + k * 64, A[s][rs][k]);
-          }
+          for (int k = 0; k < 4; ++k)
+            __builtin_amdgcn_raw_buffer_store_b128(A[s][rs][k], ko, ofs, k * 64, kCachePolicyStream);
         }
+        vm += 8;
       }
       // kept rows of the last tile, from its slot: four threads per row
       {
         const int x = tid_u >> 2, qq = tid_u & 3;
         const int i = tl * 128 + x;
         const int o = i < N ? pos[i] : -1;
-        if (o >= 0) {
-          char* dst = reinterpret_cast<char*>(Ko + (int64_t)o * kD);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int ch = qq * 4 + k;
-            st16(dst + ch * 16, ld16(lslot + frag_offset<bf16_bits>(x, ch)));
-          }
+        for (int k = 0; k < 4; ++k) {
+          const int ch = qq * 4 + k;
+          __builtin_amdgcn_raw_buffer_store_b128(ld16(lslot + frag_offset<bf16_bits>(x, ch)), ko,
+                                                 o >= 0 ? o * kRowBytes + ch * 16 : past, 0,
+                                                 kCachePolicyStream);
         }
+        vm += 4;
       }
-      gather_rows_block<bf16_bits, kThreads>(ks, B, [&](int r) { return p.vrow(u, r); },
-                                             V_out + (int64_t)u * out_stride);
+      last_u = u;
     }
     // release the last tile's slot (the next unit's first barrier orders it)
     ++c;
     cons_slot = cons_slot + 1 == S ? 0 : cons_slot + 1;
   }
+  // the last unit's kept V rows: no later unit carries them
+  if (last_u >= 0)
+    gather_rows_block<bf16_bits, kThreads>(ks, B, [&](int r) { return p.vrow(last_u, r); },
+                                           V_out + (int64_t)last_u * out_stride);
 }
 
 template <int kHeld>

@@ -86,13 +86,14 @@ __host__ __device__ inline FusedPlan fused_plan_choose(int N, int B, int gw, int
 }
 
 // LDS plan of the register-resident dense bf16 kernel (k2_resident.hip): a
-// ring of `slots` 128-row bf16 tiles, two slots of window queries, the
+// ring of `slots` 128-row bf16 tiles, 32 KiB of staging for the previous
+// unit's V rows (up to 4 KiB per wave), two slots of window queries, the
 // softmax normalisers and their per-wave partials, 1/||k|| (later the output
 // row of each candidate) and R then Z over the unit's padded tiles, the kept
 // indices, two rounds of per-wave column maxima, the last tile's own column
 // maxima, and selection scratch.
 struct ResidentPlan {
-  int slots, q, qbytes, stats, sred, rn, zs, ks, part, dpart, sel, total;
+  int slots, vstage, q, qbytes, stats, sred, rn, zs, ks, part, dpart, sel, total;
 };
 
 // Row blocks of 32 keys each wave holds in registers: 8 waves x 4 x 32 =
@@ -102,8 +103,9 @@ constexpr int kResidentHeld = 4;
 __host__ __device__ inline ResidentPlan resident_plan(int N, int B, int gw) {
   ResidentPlan L;
   const int nb = (N + 127) / 128;
-  L.slots = 3;
-  L.q = L.slots * 128 * 256;
+  L.slots = 2;
+  L.vstage = L.slots * 128 * 256;
+  L.q = L.vstage + 32 * 1024;
   L.qbytes = (gw * 256 + 1023) / 1024 * 1024;
   L.stats = L.q + 2 * L.qbytes;
   L.sred = L.stats + 32 * 8;
