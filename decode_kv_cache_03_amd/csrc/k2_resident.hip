@@ -52,8 +52,36 @@ using stream::vm_imm;
 constexpr int kThreads = 512;
 constexpr int kRowBytes = 256;                  // bf16 row of 128
 constexpr int kTileBytes = 128 * kRowBytes;
+// Cache policy of the K'/V' stores: the default (write-back through L2)
+// measured faster here than streaming stores.
+constexpr int kOutPolicy = 0;
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// The value of lane l and of lane l ^ 16 (or l ^ 32), the lower lane's first,
+// from one VALU lane swap (gfx950): a butterfly step is op(lo, hi), the same
+// operands in the same order in both lanes.
+struct LanePair {
+  float lo, hi;
+};
+__device__ __forceinline__ LanePair pair16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ LanePair pair32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float sum_quarters(float x) {   // over lanes l, l^16, l^32, l^48
+  const LanePair a = pair16(x);
+  const LanePair b = pair32(a.lo + a.hi);
+  return b.lo + b.hi;
+}
+__device__ __forceinline__ float max_quarters(float x) {
+  const LanePair a = pair16(x);
+  const LanePair b = pair32(fmaxf(a.lo, a.hi));
+  return fmaxf(b.lo, b.hi);
+}
 
 // Wait until at most n vector-memory instructions of this wave are in
 // flight (n rounded down to a multiple of 4: never a shorter wait).
@@ -112,52 +140,53 @@ __device__ __forceinline__ void load_queries(const char* qlds, int lane, int W, 
   }
 }
 
-// 1/||k|| of the 32 rows of a fragment pair, written to rn[key0 + row] (each
-// row's four quarters add their partial sums; rows past N are padding).
-__device__ __forceinline__ void row_norms(const u32x4_t (&f)[2][4], int key0, int lane, float* rn) {
+// 1/||k|| of the 16*NK rows of NK fragments, written to rn[key0 + row]
+// (each row's four quarters add their partial sums; rows past N are padding).
+template <int NK>
+__device__ __forceinline__ void row_norms(const u32x4_t (&f)[NK][4], int key0, int lane, float* rn) {
 #pragma unroll
-  for (int rs = 0; rs < 2; ++rs) {
+  for (int rs = 0; rs < NK; ++rs) {
     float ss = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) ss += sumsq_chunk<bf16_bits>(f[rs][ks]);
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
+    ss = sum_quarters(ss);
     const int key = key0 + rs * 16 + (lane & 15);
     if (lane < 16) rn[key] = ss > 0.f ? __frsqrt_rn(ss) : 0.f;
   }
 }
 
-// Online softmax statistics of the window queries over 32 keys: lane l owns
-// query columns l % 16 and 16 + l % 16 (mrun/srun [qs]).
-__device__ __forceinline__ void stats_update(const u32x4_t (&kf)[2][4], const u32x4_t (&qf)[2][4],
+// Online softmax statistics of the window queries over 16*NK keys: lane l
+// owns query columns l % 16 and 16 + l % 16 (mrun/srun [qs]).
+template <int NK>
+__device__ __forceinline__ void stats_update(const u32x4_t (&kf)[NK][4], const u32x4_t (&qf)[2][4],
                                              int key0, int N, int W, int G, int rpg_shift,
                                              bool causal, int lane, float (&mrun)[2],
                                              float (&srun)[2]) {
   asm volatile("" : "+v"(lane));   // per call: keeps lane-derived masks out of loop preheaders
   const int rpg_mask = (1 << rpg_shift) - 1;
-  f32x4_t acc[2][2];
+  f32x4_t acc[NK][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < NK; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int ksb = 0; ksb < 2; ++ksb)
+    for (int ksb = 0; ksb < NK; ++ksb)
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) mma16(acc[ksb][qs], kf[ksb][ks], qf[qs][ks]);   // C[key][query]
   // the block holds padding or keys that some window query cannot see
-  const bool edge = key0 + 32 > (causal ? N - W : N);
+  const bool edge = key0 + 16 * NK > (causal ? N - W : N);
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
     const int m = qs * 16 + (lane & 15);
     const int g = m >> rpg_shift, r = m & rpg_mask;
     const bool qok = g < G && r < W;
     const int last = causal ? N - W + r : N - 1;   // last key visible to window query r
-    float lg[8];
+    float lg[4 * NK];
     float mt = -INFINITY;
 #pragma unroll
-    for (int ksb = 0; ksb < 2; ++ksb)
+    for (int ksb = 0; ksb < NK; ++ksb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int key = key0 + ksb * 16 + 4 * (lane >> 4) + v;
@@ -170,7 +199,7 @@ __device__ __forceinline__ void stats_update(const u32x4_t (&kf)[2][4], const u3
     if (mn != -INFINITY) {
       float s = (mrun[qs] != -INFINITY) ? srun[qs] * fast_exp2(mrun[qs] - mn) : 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s += fast_exp2(lg[i] - mn);
+      for (int i = 0; i < 4 * NK; ++i) s += fast_exp2(lg[i] - mn);
       srun[qs] = s;
       mrun[qs] = mn;
     }
@@ -251,8 +280,7 @@ __device__ __forceinline__ void pair_max16(const u32x4_t (&af)[2][4], const floa
 __device__ __forceinline__ void publish_cols(float (&cm)[2], float* dst, int lane) {
 #pragma unroll
   for (int cs = 0; cs < 2; ++cs) {
-    float x = fmaxf(cm[cs], __shfl_xor(cm[cs], 16, 64));
-    x = fmaxf(x, __shfl_xor(x, 32, 64));
+    const float x = max_quarters(cm[cs]);
     if (lane < 16) dst[cs * 16 + lane] = x;
   }
 }
@@ -293,8 +321,9 @@ __device__ __forceinline__ float key_importance16(const u32x4_t (&kf)[4], const 
       w[v] = vis ? pr : 0.f;
     }
     x[qs] = comb(comb(w[0], w[1], 0), comb(w[2], w[3], 0), 1);
-    x[qs] = comb(x[qs], __shfl_xor(x[qs], 16, 64), 2);
-    x[qs] = comb(x[qs], __shfl_xor(x[qs], 32, 64), 3);
+    const LanePair a = pair16(x[qs]);
+    const LanePair b = pair32(comb(a.lo, a.hi, 2));
+    x[qs] = comb(b.lo, b.hi, 3);
   }
   return comb(x[0], x[1], 4) * inv_pool;
 }
@@ -519,7 +548,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
           if (j >= nv) continue;
           const int q = (t * kps + j) * kThreads + tid_u;   // chunks past B rows: dropped
           __builtin_amdgcn_raw_buffer_store_b128(ld16(vstage + (wave * 4 + j) * 1024 + lane_u * 16),
-                                                 vo, q * 16, 0, kCachePolicyStream);
+                                                 vo, q * 16, 0, kOutPolicy);
         }
         vm += nv;
       }
@@ -530,64 +559,65 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
     }
 
     // ---------------- the last tile's own rows ----------------
+    // (lane ids re-materialised: offsets of the step loop do not live on)
+    int lane_p = lane_u, tid_p = tid_u;
+    asm volatile("" : "+v"(lane_p), "+v"(tid_p));
     const int tl = nb - 1;
     const char* lslot = lds + cons_slot * kTileBytes;
-    if ((wave >> 2) == (tl & 1)) {
-      const int r = wave & 3;
-      const int key0 = tl * 128 + r * 32;
-      u32x4_t af[2][4];
-      load_frag(lslot, r * 32, lane_u, af[0]);
-      load_frag(lslot, r * 32 + 16, lane_u, af[1]);
-      row_norms(af, key0, lane_u, rn);
-      f32x4_t rr[2];
-#pragma unroll
-      for (int rs = 0; rs < 2; ++rs)
-        rr[rs] = *reinterpret_cast<const f32x4_t*>(rn + key0 + rs * 16 + 4 * (lane_u >> 4));
-      {
-        u32x4_t qf[2][4];
-        load_queries(qlds, lane_u, W, G, rpg_shift, qf);
-        stats_update(af, qf, key0, N, W, G, rpg_shift, causal, lane_u, mrun, srun);
-      }
-      // rows past N (a copy of row N-1) only meet columns before them, which
-      // the diagonal mask drops, or columns past N, which are never read
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        if (cb < r) continue;
-        float cm[2] = {-INFINITY, -INFINITY};
-#pragma unroll
-        for (int cs = 0; cs < 2; ++cs) {
-          u32x4_t bf[4];
-          load_frag(lslot, cb * 32 + cs * 16, lane_u, bf);
-          pair_max16(af, rn + key0, bf, cs, cb == r, lane_u, cm[cs]);
-        }
-        publish_cols(cm, dpart + r * 128 + cb * 32, lane_u);
-      }
+    // norms and logits: wave w takes rows 16w.. of the tile
+    {
+      u32x4_t kf[1][4];
+      load_frag(lslot, wave * 16, lane_p, kf[0]);
+      row_norms(kf, tl * 128 + wave * 16, lane_p, rn);
+      u32x4_t qf[2][4];
+      load_queries(qlds, lane_p, W, G, rpg_shift, qf);
+      stats_update(kf, qf, tl * 128 + wave * 16, N, W, G, rpg_shift, causal, lane_p, mrun, srun);
     }
-    // statistics of the wave: merge the four lane_u quarters
+    lds_barrier();
+    // the tile's own pairs: row block r against column half (cb, cs) for
+    // r <= cb, 20 items dealt round-robin to the 8 waves; rows past N (a copy
+    // of row N-1) only meet columns before them, which the diagonal mask
+    // drops, or columns past N, which are never read
+    for (int it = wave; it < 20; it += 8) {
+      // item -> (r, cb, cs): pairs (r, cb) in the order (0,0..3), (1,1..3), ...
+      const int pr = it >> 1, cs = it & 1;
+      const int r = pr < 4 ? 0 : (pr < 7 ? 1 : (pr < 9 ? 2 : 3));
+      const int cb = r + pr - (r == 0 ? 0 : (r == 1 ? 4 : (r == 2 ? 7 : 9)));
+      u32x4_t af[2][4], bf[4];
+      load_frag(lslot, r * 32, lane_p, af[0]);
+      load_frag(lslot, r * 32 + 16, lane_p, af[1]);
+      load_frag(lslot, cb * 32 + cs * 16, lane_p, bf);
+      float cm = -INFINITY;
+      pair_max16(af, rn + tl * 128 + r * 32, bf, cs, cb == r, lane_p, cm);
+      const float x = max_quarters(cm);
+      if (lane_p < 16) dpart[r * 128 + cb * 32 + cs * 16 + lane_p] = x;
+    }
+    // statistics of the wave: merge the four lane quarters
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       float m = mrun[qs], s = srun[qs];
 #pragma unroll
       for (int sh = 16; sh <= 32; sh <<= 1) {
-        const float m2 = __shfl_xor(m, sh, 64), s2 = __shfl_xor(s, sh, 64);
-        const float mm = fmaxf(m, m2);
+        const LanePair mp = sh == 16 ? pair16(m) : pair32(m);
+        const LanePair sp = sh == 16 ? pair16(s) : pair32(s);
+        const float mm = fmaxf(mp.lo, mp.hi);
         float st = 0.f;
         if (mm != -INFINITY)
-          st = (m != -INFINITY ? s * fast_exp2(m - mm) : 0.f) +
-               (m2 != -INFINITY ? s2 * fast_exp2(m2 - mm) : 0.f);
+          st = (mp.lo != -INFINITY ? sp.lo * fast_exp2(mp.lo - mm) : 0.f) +
+               (mp.hi != -INFINITY ? sp.hi * fast_exp2(mp.hi - mm) : 0.f);
         m = mm;
         s = st;
       }
-      if (lane_u < 16) {
-        sred_m[wave * 32 + qs * 16 + lane_u] = m;
-        sred_s[wave * 32 + qs * 16 + lane_u] = s;
+      if (lane_p < 16) {
+        sred_m[wave * 32 + qs * 16 + lane_p] = m;
+        sred_s[wave * 32 + qs * 16 + lane_p] = s;
       }
     }
     lds_barrier();
-    if (tid_u < 128) {
-      finalize(tl, true, tid_u);
-    } else if (tid_u < 160) {
-      const int m = tid_u - 128;
+    if (tid_p < 128) {
+      finalize(tl, true, tid_p);
+    } else if (tid_p < 160) {
+      const int m = tid_p - 128;
       float mm = -INFINITY;
 #pragma unroll
       for (int w = 0; w < 8; ++w) mm = fmaxf(mm, sred_m[w * 32 + m]);
@@ -607,13 +637,13 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
     // ---------------- importance and Z ----------------
     {
       u32x4_t qf[2][4];
-      load_queries(qlds, lane_u, W, G, rpg_shift, qf);
+      load_queries(qlds, lane_p, W, G, rpg_shift, qf);
       float smax[2][4], sinv[2][4];
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const u32x2_t st = stats[qs * 16 + 4 * (lane_u >> 4) + v];
+          const u32x2_t st = stats[qs * 16 + 4 * (lane_p >> 4) + v];
           smax[qs][v] = __uint_as_float(st.x);
           sinv[qs][v] = __uint_as_float(st.y);
         }
@@ -629,21 +659,21 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
         for (int rs = 0; rs < 2; ++rs)
           Ih[s][rs] = gb < 4 * nh ? key_importance16(A[s][rs], qf, smax, sinv, gb * 32 + rs * 16,
                                                      N, W, rpg_shift, causal, mean, inv_pool,
-                                                     lane_u)
+                                                     lane_p)
                                   : 0.f;
       }
       if (lown) {
 #pragma unroll
         for (int rs = 0; rs < 2; ++rs) {
           u32x4_t kf[4];
-          load_frag(lslot, (wave & 3) * 32 + rs * 16, lane_u, kf);
+          load_frag(lslot, (wave & 3) * 32 + rs * 16, lane_p, kf);
           Il[rs] = key_importance16(kf, qf, smax, sinv, lkey0 + rs * 16, N, W, rpg_shift, causal,
-                                    mean, inv_pool, lane_u);
+                                    mean, inv_pool, lane_p);
         }
       }
       auto put = [&](float I, int key0) {
-        const int key = key0 + (lane_u & 15);
-        if (lane_u < 16 && key < N) {
+        const int key = key0 + (lane_p & 15);
+        if (lane_p < 16 && key < N) {
           const float R = zs[key];
           const float z = lam * I - oml * R + 0.0f;   // + 0 folds -0 onto +0
           zs[key] = z;
@@ -693,7 +723,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
           const int ofs = o >= 0 ? o * kRowBytes + (lane_u >> 4) * 16 : past;
 #pragma unroll
           for (int k = 0; k < 4; ++k)
-            __builtin_amdgcn_raw_buffer_store_b128(A[s][rs][k], ko, ofs, k * 64, kCachePolicyStream);
+            __builtin_amdgcn_raw_buffer_store_b128(A[s][rs][k], ko, ofs, k * 64, kOutPolicy);
         }
         vm += 8;
       }
@@ -707,7 +737,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
           const int ch = qq * 4 + k;
           __builtin_amdgcn_raw_buffer_store_b128(ld16(lslot + frag_offset<bf16_bits>(x, ch)), ko,
                                                  o >= 0 ? o * kRowBytes + ch * 16 : past, 0,
-                                                 kCachePolicyStream);
+                                                 kOutPolicy);
         }
         vm += 4;
       }
