@@ -39,6 +39,8 @@
 // padding keys; mean pooling sums the heads' window means and divides by G.
 // The symmetric R needs later keys as well and is served by k2_wide.hip.
 // Under head-shared selection the kernel stops after writing Z.
+#include <type_traits>
+
 #include "rkv_problem.hpp"
 #include "rkv_launch.hpp"
 #include "rkv_select.hpp"
@@ -334,6 +336,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
     float* __restrict__ Idbg, float lam, float oml, float inv_pool, int rpg_shift,
     int32_t* __restrict__ kept_all, bf16_bits* __restrict__ K_out, bf16_bits* __restrict__ V_out,
     int64_t out_stride, int score_only, ResidentPlan L) {
+  static_assert(kHeld == 4, "the runs of held blocks below are written out for four");
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -510,20 +513,38 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
         }
       }
 
-      // columns: the tile's keys against every held row before them
+      // columns: the tile's keys against every held row before them. The
+      // blocks wholly before tile t are slots 0..nfull-1, dealt as one
+      // straight-line run so that one block's epilogue overlaps the next
+      // block's products; the wave's own block of tile t (slot t/2) follows
+      // with the diagonal mask.
+      const int nfull = min(kHeld, max(0, (4 * t - wave + 7) >> 3));
+      const bool has_diag = t < nh && (wave >> 2) == (t & 1);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         u32x4_t bf[2][4];
         load_frag(slot, cb * 32, lane_u, bf[0]);
         load_frag(slot, cb * 32 + 16, lane_u, bf[1]);
         float cm[2] = {-INFINITY, -INFINITY};
+        auto full = [&](auto sc) {
+          constexpr int s = decltype(sc)::value;
+          pair_max(A[s], rn + (8 * s + wave) * 32, bf, false, lane_u, cm);
+        };
+        switch (nfull) {
+          case 4: full(std::integral_constant<int, 0>{}); full(std::integral_constant<int, 1>{});
+                  full(std::integral_constant<int, 2>{}); full(std::integral_constant<int, 3>{}); break;
+          case 3: full(std::integral_constant<int, 0>{}); full(std::integral_constant<int, 1>{});
+                  full(std::integral_constant<int, 2>{}); break;
+          case 2: full(std::integral_constant<int, 0>{}); full(std::integral_constant<int, 1>{}); break;
+          case 1: full(std::integral_constant<int, 0>{}); break;
+          default: break;
+        }
+        if (has_diag && (wave & 3) <= cb) {
 #pragma unroll
-        for (int s = 0; s < kHeld; ++s) {
-          const int gb = 8 * s + wave;
-          if (gb >= 4 * nh || gb > 4 * t + 3) continue;
-          const bool diag = (gb >> 2) == t;
-          if (diag && (gb & 3) > cb) continue;
-          pair_max(A[s], rn + gb * 32, bf, diag && (gb & 3) == cb, lane_u, cm);
+          for (int s = 0; s < kHeld; ++s) {
+            if (s != (t >> 1)) continue;
+            pair_max(A[s], rn + (8 * s + wave) * 32, bf, (wave & 3) == cb, lane_u, cm);
+          }
         }
         publish_cols(cm, part + (t & 1) * 1024 + wave * 128 + cb * 32, lane_u);
       }
@@ -652,15 +673,23 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
       float Ih[kHeld][2], Il[2] = {0.f, 0.f};
       const bool lown = (wave >> 2) == (tl & 1);   // owns a row block of the last tile
       const int lkey0 = tl * 128 + (wave & 3) * 32;
-#pragma unroll
-      for (int s = 0; s < kHeld; ++s) {
-        const int gb = 8 * s + wave;
+      // held slots 0..nheld-1, as one straight-line run
+      const int nheld = min(kHeld, max(0, (4 * nh - wave + 7) >> 3));
+      auto imp = [&](auto sc) {
+        constexpr int s = decltype(sc)::value;
 #pragma unroll
         for (int rs = 0; rs < 2; ++rs)
-          Ih[s][rs] = gb < 4 * nh ? key_importance16(A[s][rs], qf, smax, sinv, gb * 32 + rs * 16,
-                                                     N, W, rpg_shift, causal, mean, inv_pool,
-                                                     lane_p)
-                                  : 0.f;
+          Ih[s][rs] = key_importance16(A[s][rs], qf, smax, sinv, (8 * s + wave) * 32 + rs * 16, N, W,
+                                       rpg_shift, causal, mean, inv_pool, lane_p);
+      };
+      switch (nheld) {
+        case 4: imp(std::integral_constant<int, 0>{}); imp(std::integral_constant<int, 1>{});
+                imp(std::integral_constant<int, 2>{}); imp(std::integral_constant<int, 3>{}); break;
+        case 3: imp(std::integral_constant<int, 0>{}); imp(std::integral_constant<int, 1>{});
+                imp(std::integral_constant<int, 2>{}); break;
+        case 2: imp(std::integral_constant<int, 0>{}); imp(std::integral_constant<int, 1>{}); break;
+        case 1: imp(std::integral_constant<int, 0>{}); break;
+        default: break;
       }
       if (lown) {
 #pragma unroll
