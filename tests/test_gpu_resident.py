@@ -123,3 +123,37 @@ def test_resident_units_beyond_grid(rkv):
         par.assert_tau_valid(kept[u], ref["Z"], case.n, case.budget, case.window, f"unit {u}")
         assert np.array_equal(Ko[u], case.K[u][kept[u].astype(np.int64)]), f"unit {u} rows"
     torch.cuda.synchronize()
+
+
+TIE_CASES = [
+    # (name, N, B, w, lambda): keys drawn from few distinct rows, so many
+    # candidates share the same Z exactly and the index order decides
+    ("one-row", 1152, 1024, 8, 0.0),
+    ("one-row-lam", 1152, 1024, 8, 0.1),
+    ("three-rows", 1100, 700, 8, 0.0),
+    ("two-rows-small", 300, 150, 8, 0.0),
+]
+
+
+@pytest.mark.parametrize("case_", TIE_CASES, ids=[c[0] for c in TIE_CASES])
+def test_resident_selection_ties(rkv, case_):
+    """Exact ties: the kept set must be the selection of the device's own Z
+    with ties to the smaller index (the oracle's select on those values)."""
+    name, n, b, w, lam = case_
+    rows = 1 if name.startswith("one") else (3 if name.startswith("three") else 2)
+    case = dense_case_host(505 + n + rows, 1, 1, 4, 4, n, b, w, lam, "bf16", 0.0, 0.02)
+    rng = np.random.default_rng(505 + rows)
+    for h in range(case.num_heads):
+        pick = rng.integers(0, rows, size=n)
+        base = case.K[h, :rows].copy()
+        case.K[h] = base[pick]
+    res, labels = _run(rkv, case)
+    assert list(labels) == ["rkv_k2_resident"]
+    kept = res.kept_idx.cpu().numpy()
+    Z = res.Z.cpu().numpy()
+    Ko = par.to_host_f32(res.K_out)
+    for h in range(case.num_heads):
+        z = Z[h].astype(np.float64)
+        assert len(np.unique(z[: n - w])) < n // 4, f"{name}: expected many tied scores"
+        assert np.array_equal(kept[h], orc.select(z, n, b, w)), f"{name} head {h}: kept set"
+        assert np.array_equal(Ko[h], case.K[h][kept[h].astype(np.int64)]), f"{name} head {h}: rows"
