@@ -112,10 +112,10 @@ def source_hash(files):
 
 _HEADERS = ["rkv_device.hpp", "rkv_problem.hpp", "rkv_launch.hpp"]
 KERNEL_SOURCES = {
-    "rkv_k2_resident": ["k2_resident.hip", "rkv_select.hpp", "rkv_stream.hpp"] + _HEADERS,
+    "rkv_k2_resident": ["k2_resident.hip", "rkv_frag16.hpp", "rkv_select.hpp", "rkv_stream.hpp"] + _HEADERS,
     "rkv_k2_compress": ["k2_wide.hip", "k2_redundancy.hip", "rkv_select.hpp", "rkv_stream.hpp"] + _HEADERS,
     "rkv_k2_redundancy": ["k2_redundancy.hip", "rkv_select.hpp"] + _HEADERS,
-    "rkv_k2_long": ["k2_long.hip", "rkv_stream.hpp"] + _HEADERS,
+    "rkv_k2_long": ["k2_long.hip", "rkv_frag16.hpp", "rkv_stream.hpp"] + _HEADERS,
     "rkv_k1_stats": ["k1_importance.hip"] + _HEADERS,
     "rkv_k1_combine": ["k1_importance.hip"] + _HEADERS,
     "rkv_k4_select": ["k4_select.hip", "rkv_select.hpp"] + _HEADERS,

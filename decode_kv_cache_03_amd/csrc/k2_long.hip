@@ -37,6 +37,8 @@
 #include "rkv_problem.hpp"
 #include "rkv_launch.hpp"
 #include "rkv_stream.hpp"
+#include "rkv_frag16.hpp"
+#include <type_traits>
 
 namespace rkv {
 namespace longu {
@@ -396,12 +398,375 @@ static hipError_t run_sym(const P& p, int count, const float* rinv, const float*
 
 }  // namespace longu
 
+// ---- 1024-row items held in registers (one window-query block, causal R) ----
+//
+// An item's rows are held the way k2_resident.hip holds a unit's keys: row
+// block b (32 rows) of the item by wave b % 8, slot b / 8, as 16x16x32 MFMA
+// fragments (rkv_frag16.hpp), so each 32 KiB tile fetched feeds 1024 rows
+// (1024 flop per byte). Own tiles come first, descending: when own tile d
+// lands its owners copy their blocks and take the rows' norms (staged with
+// the tile) and importance, and every block of tiles d.. meets its columns
+// (the block of tile d under the diagonal mask). Tiles 0..t0-1 follow. A lane
+// keeps, for each of its accumulator rows, the max over the columns it met of
+// dot * (1/||k_j||); the max over the 16 column lanes and * (1/||k_i||) give R
+// at the end of the item.
+namespace longr {
+
+using namespace frag16;
+using stream::kLoadsPerTile;
+using stream::wait_tiles;
+
+constexpr int kThreads = 512;
+constexpr int kRowBytes = 256;
+constexpr int kTileBytes = 128 * kRowBytes;
+constexpr int kPer = kLoadsPerTile + 1;   // loads per wave per tile: 4 of keys, 1 of norms
+
+// Tile order of an item of up to 8 own tiles: own tiles descending, then
+// tiles 0..t0-1.
+struct Geo {
+  int t0, nt, nb;
+  __device__ int len() const { return nt + t0; }
+  __device__ int tile(int k) const { return k < nt ? t0 + nt - 1 - k : k - nt; }
+};
+__device__ __forceinline__ Geo geo_of(int n, int blk) {
+  Geo g;
+  g.nb = (n + 127) / 128;
+  g.t0 = 8 * blk;
+  g.nt = min(8, g.nb - g.t0);
+  return g;
+}
+
+template <class P>
+__global__ __launch_bounds__(kThreads, 1) void k2lr_kernel(P p, const float* __restrict__ rinv,
+                                                          const float* __restrict__ fin,
+                                                          float* __restrict__ Z,
+                                                          float* __restrict__ Rdbg,
+                                                          float* __restrict__ Idbg, float lam,
+                                                          float oml, float inv_pool, int rpg_shift,
+                                                          LongPlanR L) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int S = L.slots;
+  const int W = p.W, G = p.G, gw = G * W;
+  const bool causal = p.causal(), mean = p.pool_mean();
+  const int count = p.long_count();
+  const int grid = gridDim.x, bid = blockIdx.x;
+  const bf16_bits* rows = p.long_rows();
+  constexpr int kStatsBytes = 32 * 8;
+  float* const rrn = reinterpret_cast<float*>(lds + L.rrn);   // [1024] 1/||k|| of the item's rows
+  float* const rim = reinterpret_cast<float*>(lds + L.rim);   // [1024] importance
+
+  // ---- loader: this workgroup's items, tile by tile, into the ring ----
+  auto fetch = [&](int r, LongItem& it, Geo& g) -> bool {
+    const int k = r * grid + ((r & 1) ? grid - 1 - bid : bid);   // snake over rounds
+    if (k >= count) return false;
+    it = p.long_item(k);
+    it.u = __builtin_amdgcn_readfirstlane(it.u);
+    it.blk = __builtin_amdgcn_readfirstlane(it.blk);
+    it.n = __builtin_amdgcn_readfirstlane(it.n);
+    g = geo_of(it.n, it.blk);
+    return true;
+  };
+  int ld_r = 0, ld_par = 0, ld_k = 0;
+  LongItem ld_it;
+  Geo ld_g;
+  bool ld_valid = fetch(0, ld_it, ld_g);
+  int issued = 0, issue_slot = 0;
+  // The loader runs at most one item ahead of the consumer: the queries and
+  // normalisers of two items share the two parity buffers.
+  int ld_limit = 2;
+  auto issue_next = [&]() -> bool {
+    if (!ld_valid || ld_r >= ld_limit) return false;
+    int lane_v = lane;   // per call: keeps lane-derived values out of the callers' loops
+    asm volatile("" : "+v"(lane_v));
+    if (ld_k == 0) {   // the item's window queries and normalisers, ahead of its first tile
+      const char* q = reinterpret_cast<const char*>(p.q(ld_it.u));
+      const int qkb = L.qbytes / 1024;
+      char* qdst = lds + L.q + ld_par * L.qbytes;
+      for (int kb = wave; kb < qkb; kb += 8) {
+        const int n = kb * 4 + lane_v / 16;
+        const int c = (lane_v % 16) ^ (n & 15);
+        load16_to_lds(q + min(n, gw - 1) * kRowBytes + c * 16, qdst + kb * 1024);
+      }
+      if (wave == 0 && lane_v < 16)
+        load16_to_lds(reinterpret_cast<const char*>(fin) + ((int64_t)ld_it.u * 32) * 8 + lane_v * 16,
+                      lds + L.stats + ld_par * kStatsBytes);
+    }
+    const int t = ld_g.tile(ld_k);
+    char* slot = lds + issue_slot * kTileBytes;
+    const bf16_bits* urows = rows + ld_it.row_base;
+    // 1/||k|| of tile rows 16w.. (rows past n repeat row n-1), 16 lanes x 4 bytes
+    if (lane_v < 16) {
+      const int rr = min(t * 128 + wave * 16 + lane_v, ld_it.n - 1);
+      __builtin_amdgcn_global_load_lds(rinv + ld_it.score_off + rr,
+                                       (__attribute__((address_space(3))) void*)(lds + L.rn + issue_slot * 512 + wave * 64),
+                                       4, 0, 0);
+    }
+    // Tile load q (0..3) of wave w fills KiB 4w + q of a slot: tile row
+    // 16w + 4q + lane/16 at chunk position lane % 16, fetching chunk
+    // (lane % 16) ^ (row & 15) of that row.
+    const int row0 = t * 128 + wave * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rt = row0 + 4 * q + lane_v / 16;
+      const int r = min(rt, ld_it.n - 1);   // rows past n repeat row n-1
+      const int c = (lane_v % 16) ^ (rt & 15);
+      load16_to_lds(reinterpret_cast<const char*>(urows + (int64_t)r * kD) + c * 16,
+                    slot + wave * 4096 + q * 1024);
+    }
+    ++issued;
+    issue_slot = issue_slot + 1 == S ? 0 : issue_slot + 1;
+    if (++ld_k == ld_g.len()) {
+      ld_k = 0;
+      ++ld_r;
+      ld_par ^= 1;
+      ld_valid = fetch(ld_r, ld_it, ld_g);
+    }
+    return true;
+  };
+  auto refill = [&](int c) {
+    while (issued - c < S && issue_next()) {
+    }
+  };
+  auto ensure_issued = [&](int c) {
+    if (issued < c + 1) {
+      lds_barrier();
+      refill(c);
+    }
+  };
+
+  int c = 0, cons_slot = 0;   // tiles consumed, c % S
+  refill(0);
+
+  int par = 0;
+  for (int r = 0;; ++r, par ^= 1) {
+    LongItem it;
+    Geo g;
+    if (!fetch(r, it, g)) break;
+    ld_limit = r + 2;
+    int lane_u = lane;   // per item: keeps lane-derived values from living across items
+    asm volatile("" : "+v"(lane_u));
+    const int n = it.n;
+    const int base = g.t0 * 128;
+    const char* qlds = lds + L.q + par * L.qbytes;
+    const u32x2_t* st = reinterpret_cast<const u32x2_t*>(lds + L.stats + par * kStatsBytes);
+    // held slots of this wave: row blocks 8s + wave < 4 nt
+    const int nheld = min(4, max(0, (4 * g.nt - wave + 7) >> 3));
+
+    u32x4_t A[4][2][4];
+    f32x4_t mx[4][2];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) mx[s][rs] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+
+    // rows of held slot s (16-row half rs) against the 16 columns of bf:
+    // mask 0 = every column counts; 1 = the same tile, column < row counts
+    auto block = [&](auto sc, const u32x4_t (&bf)[4], float rc, int col_in_tile, int mask) {
+      constexpr int s = decltype(sc)::value;
+      f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs) mma16(acc[rs], A[s][rs][ks], bf[ks]);   // C[row][col]
+      if (mask == 0) {
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) mx[s][rs][v] = vmax(mx[s][rs][v], acc[rs][v] * rc);
+      } else {
+        int lane_m = lane_u;   // re-materialised: keeps the masks out of loop preheaders
+        asm volatile("" : "+v"(lane_m));
+        const int row0 = ((8 * s + wave) & 3) * 32 + 4 * (lane_m >> 4);   // row within the tile
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (col_in_tile < row0 + rs * 16 + v) mx[s][rs][v] = vmax(mx[s][rs][v], acc[rs][v] * rc);
+      }
+    };
+    // as block, unmasked, for two column sub-blocks at once: each running
+    // max takes both products in one three-way max
+    auto block2 = [&](auto sc, const u32x4_t (&bf)[2][4], float rc0, float rc1) {
+      constexpr int s = decltype(sc)::value;
+      f32x4_t acc[2][2];
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) acc[rs][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) mma16(acc[rs][h], A[s][rs][ks], bf[h][ks]);
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          mx[s][rs][v] = vmax(mx[s][rs][v], vmax(acc[rs][0][v] * rc0, acc[rs][1][v] * rc1));
+    };
+
+    const int len = g.len();
+    for (int k = 0; k < len; ++k) {
+      ensure_issued(c);
+      wait_tiles<kPer>(issued - (c + 1));
+      lds_barrier();
+      refill(c);
+      const char* slot = lds + cons_slot * kTileBytes;
+      const float* rns = reinterpret_cast<const float*>(lds + L.rn + cons_slot * 512);
+      const bool own = k < g.nt;
+      const int d = g.nt - 1 - k;   // own tile, relative (own steps)
+      if (own && (wave >> 2) == (d & 1)) {
+        // this wave's block of own tile d: registers, norms, importance
+        int lane_o = lane_u;
+        asm volatile("" : "+v"(lane_o));
+        const int rb = wave & 3;                // block within the tile
+        const int rel = (4 * d + rb) * 32;      // first row within the item
+        u32x4_t qf[2][4];
+        load_queries(qlds, lane_o, W, G, rpg_shift, qf);
+        float smax[2][4], sinv[2][4];
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const u32x2_t sv = st[qs * 16 + 4 * (lane_o >> 4) + v];
+            smax[qs][v] = __uint_as_float(sv.x);
+            sinv[qs][v] = __uint_as_float(sv.y);
+          }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if (s != (d >> 1)) continue;
+#pragma unroll
+          for (int rs = 0; rs < 2; ++rs) {
+            load_frag(slot, rb * 32 + rs * 16, lane_o, A[s][rs]);
+            const float I = key_importance16(A[s][rs], qf, smax, sinv, base + rel + rs * 16, n, W,
+                                             rpg_shift, causal, mean, inv_pool, lane_o);
+            if (lane_o < 16) {
+              rrn[rel + rs * 16 + lane_o] = rns[rb * 32 + rs * 16 + lane_o];
+              rim[rel + rs * 16 + lane_o] = I;
+            }
+          }
+        }
+      }
+      // which held slots meet this tile: own tile d, blocks of tiles d..
+      // (slots s_lo..), the block of tile d itself under the mask; other
+      // tiles, every held slot
+      const int s_lo = own ? max(0, (4 * d - wave + 7) >> 3) : 0;
+      const int s_diag = own && (wave >> 2) == (d & 1) ? (d >> 1) : -1;
+      if (s_lo == 0 && nheld == 4 && s_diag < 0) {
+        // every held slot, no mask: straight-line runs over column pairs
+#pragma unroll 1
+        for (int cs = 0; cs < 8; cs += 2) {
+          u32x4_t bf[2][4];
+          load_frag(slot, cs * 16, lane_u, bf[0]);
+          load_frag(slot, cs * 16 + 16, lane_u, bf[1]);
+          const float rc0 = rns[cs * 16 + (lane_u & 15)];
+          const float rc1 = rns[cs * 16 + 16 + (lane_u & 15)];
+          block2(std::integral_constant<int, 0>{}, bf, rc0, rc1);
+          block2(std::integral_constant<int, 1>{}, bf, rc0, rc1);
+          block2(std::integral_constant<int, 2>{}, bf, rc0, rc1);
+          block2(std::integral_constant<int, 3>{}, bf, rc0, rc1);
+        }
+      } else {
+#pragma unroll 1
+        for (int cs = 0; cs < 8; ++cs) {
+          u32x4_t bf[4];
+          load_frag(slot, cs * 16, lane_u, bf);
+          const float rc = rns[cs * 16 + (lane_u & 15)];
+          const int col = cs * 16 + (lane_u & 15);   // column within the tile
+          auto one = [&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            if (s < s_lo || s >= nheld) return;
+            if (s == s_diag) {
+              // block rb of tile d: columns of the block's own rows or earlier
+              if (cs * 16 < ((wave & 3) + 1) * 32) block(sc, bf, rc, col, 1);
+            } else {
+              block(sc, bf, rc, col, 0);
+            }
+          };
+          one(std::integral_constant<int, 0>{});
+          one(std::integral_constant<int, 1>{});
+          one(std::integral_constant<int, 2>{});
+          one(std::integral_constant<int, 3>{});
+        }
+      }
+      ++c;
+      cons_slot = cons_slot + 1 == S ? 0 : cons_slot + 1;
+    }
+
+    // row maxima over the 16 column lanes of each quarter, then R, I, Z
+    lds_barrier();   // the owners' norms and importance are in
+    int lane_e = lane_u;
+    asm volatile("" : "+v"(lane_e));
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s >= nheld) continue;
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) {
+        float x[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float m = mx[s][rs][v];
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+          x[v] = m;
+        }
+        const int v = lane_e & 15;   // lanes 0..3 of each quarter write one row each
+        if (v < 4) {
+          const float m = v == 0 ? x[0] : (v == 1 ? x[1] : (v == 2 ? x[2] : x[3]));
+          const int rel = (8 * s + wave) * 32 + rs * 16 + 4 * (lane_e >> 4) + v;
+          const int row = base + rel;
+          if (row < n) {
+            const float R = row == 0 ? 0.f : m * rrn[rel];
+            const float I = rim[rel];
+            const float z = lam * I - oml * R + 0.0f;   // + 0 folds -0 onto +0
+            Z[it.score_off + row] = z;
+            if (Rdbg != nullptr) Rdbg[it.score_off + row] = R;
+            if (Idbg != nullptr) Idbg[it.score_off + row] = I;
+          }
+        }
+      }
+    }
+    // (rrn and rim are next written by the next item's own tiles, after the
+    // barrier of its first step)
+  }
+  // every load this workgroup issued was consumed: the ring is empty
+}
+
+template <class P>
+static hipError_t run_r(const P& p, int count, const float* rinv, const float* fin, float* Z,
+                        float* dbg_R, float* dbg_I, float lam, int rpg_shift, hipStream_t st) {
+  const LongPlanR L = long_plan_r(p.G * p.W);
+  if (L.total == 0) return hipErrorInvalidValue;
+  auto kern = k2lr_kernel<P>;
+  const void* fn = reinterpret_cast<const void*>(kern);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
+  int dev = 0, cus = 0;
+  if (e == hipSuccess) e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int grid = min(cus, count);
+  // 1 - lambda and the pooling scale as arguments: uniform values that stay in
+  // scalar registers
+  const float oml = 1.0f - lam;
+  const float inv_pool = p.pool_mean() ? 1.0f / (float)(p.W * p.G) : 1.0f / (float)p.W;
+  return launch("rkv_k2_long", kern, dim3(grid), dim3(kThreads), L.total, st, p, rinv, fin, Z, dbg_R,
+                dbg_I, lam, oml, inv_pool, rpg_shift, L);
+}
+
+}  // namespace longr
+
 template <class P>
 hipError_t run_k2_long(const P& p, int nqb, int count, const float* rinv, const float* fin, float* Z,
                        float* dbg_R, float* dbg_I, float lam, int rpg_shift, hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  if (long_block_rows(nqb, p.symmetric()) == 1024)
+    return longr::run_r(p, count, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, st);
   const LongPlan L = long_plan_choose(p.G * p.W, nqb);
   if (L.total == 0) return hipErrorInvalidValue;
-  if (count <= 0) return hipSuccess;
   switch (nqb) {
     case 1: return longu::run_sym<1>(p, count, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);
     case 2: return longu::run_sym<2>(p, count, rinv, fin, Z, dbg_R, dbg_I, lam, rpg_shift, L, st);

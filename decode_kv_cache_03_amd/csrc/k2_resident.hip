@@ -12,29 +12,28 @@
 //
 // Shape:
 //  * the unit's 128-row key tiles stream once, in order, through a ring of
-//    three LDS slots filled by direct global->LDS loads (two tiles in flight
-//    while one is consumed; the stream runs on into the next unit's first
-//    tiles while a unit finishes);
+//    two LDS slots filled by direct global->LDS loads (one tile in flight
+//    while one is consumed; the next unit's first tile loads while a unit
+//    finishes);
 //  * the keys stay: global row block b (32 rows) of tiles 0..nb-2 is held by
-//    wave b % 8 in registers, as 16x16x32 MFMA fragments (lane l holds row
-//    l % 16 of a 16-row half, 16-byte chunks (l / 16) + 4*ks), with the
-//    1/||k|| of the accumulator rows the lane will meet. Eight waves of four
-//    blocks hold 1024 rows; the unit's last tile is never needed as earlier
-//    rows of a later tile and stays in its LDS slot;
+//    wave b % 8 in registers as 16x16x32 MFMA fragments (rkv_frag16.hpp).
+//    Eight waves of four blocks hold 1024 rows; the unit's last tile is never
+//    needed as earlier rows of a later tile and stays in its LDS slot;
 //  * when tile t lands, its keys j are the columns: every wave forms the dot
 //    products of the rows it holds (i < j) with the tile's 128 keys and keeps,
 //    per column, the max of dot * (1/||k_i||); a column's max is the max over
 //    the lane's accumulator rows, then over the four lane quarters, then over
 //    the eight waves through LDS. R_j = that max * (1/||k_j||), the same
 //    products in the same order as a max of cosines;
-//  * the owners of tile t's rows form their logits against the window queries
-//    (online max and sum of exponentials per query) and their norms as they
-//    copy them into registers;
+//  * the owners of tile t's rows copy them into registers with their norms;
+//    the same waves form the rows' logits against the window queries (online
+//    max and sum of exponentials per query) one step later;
 //  * at the end of the unit the importance of every key is formed again from
 //    the held fragments (queries as MFMA rows, so a key's weights lie in one
 //    lane column and reduce in-lane and over two lane exchanges), then Z,
-//    the selection on Z in LDS, the kept K rows written from registers (the
-//    last tile's from LDS) and the kept V rows gathered.
+//    the selection on Z in LDS, and the kept K rows stored from registers
+//    (the last tile's from LDS); the kept V rows move during the next unit's
+//    tile steps, a slice per step through an LDS stage.
 // Variants: without the causal window the statistics and weights mask only
 // padding keys; mean pooling sums the heads' window means and divides by G.
 // The symmetric R needs later keys as well and is served by k2_wide.hip.
@@ -45,10 +44,12 @@
 #include "rkv_launch.hpp"
 #include "rkv_select.hpp"
 #include "rkv_stream.hpp"
+#include "rkv_frag16.hpp"
 
 namespace rkv {
 namespace resident {
 
+using namespace frag16;
 using stream::vm_imm;
 
 constexpr int kThreads = 512;
@@ -57,33 +58,6 @@ constexpr int kTileBytes = 128 * kRowBytes;
 // Cache policy of the K'/V' stores: the default (write-back through L2)
 // measured faster here than streaming stores.
 constexpr int kOutPolicy = 0;
-
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-// The value of lane l and of lane l ^ 16 (or l ^ 32), the lower lane's first,
-// from one VALU lane swap (gfx950): a butterfly step is op(lo, hi), the same
-// operands in the same order in both lanes.
-struct LanePair {
-  float lo, hi;
-};
-__device__ __forceinline__ LanePair pair16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
-}
-__device__ __forceinline__ LanePair pair32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
-}
-__device__ __forceinline__ float sum_quarters(float x) {   // over lanes l, l^16, l^32, l^48
-  const LanePair a = pair16(x);
-  const LanePair b = pair32(a.lo + a.hi);
-  return b.lo + b.hi;
-}
-__device__ __forceinline__ float max_quarters(float x) {
-  const LanePair a = pair16(x);
-  const LanePair b = pair32(fmaxf(a.lo, a.hi));
-  return fmaxf(b.lo, b.hi);
-}
 
 // Wait until at most n vector-memory instructions of this wave are in
 // flight (n rounded down to a multiple of 4: never a shorter wait).
@@ -105,40 +79,6 @@ __device__ __forceinline__ void wait_vm(int n) {
     case 13: __builtin_amdgcn_s_waitcnt(vm_imm(52)); break;
     case 14: __builtin_amdgcn_s_waitcnt(vm_imm(56)); break;
     default: __builtin_amdgcn_s_waitcnt(vm_imm(60)); break;
-  }
-}
-
-// acc += A * B over 32 k-values (16x16 tile): lane l gives row / column
-// l % 16 and k-values 8*(l/16).. of its operand; lane l receives
-// C[4*(l/16) + v][l % 16] in acc[v].
-__device__ __forceinline__ void mma16(f32x4_t& acc, u32x4_t a, u32x4_t b) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                               __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
-}
-
-// Fragment of 16 rows of a swizzled 128-row tile (or of the query block):
-// lane l takes row r0 + l % 16, chunk (l / 16) + 4*ks for k-step ks.
-__device__ __forceinline__ void load_frag(const char* base, int r0, int lane, u32x4_t (&f)[4]) {
-  const int row = r0 + (lane & 15), q = lane >> 4;
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) f[ks] = ld16(base + frag_offset<bf16_bits>(row, q + 4 * ks));
-}
-
-// Query fragments of the window: MFMA row m = 16*qs + l%16 is query row r of
-// head g with m = g * 2^rpg_shift + r; padding rows are zero.
-__device__ __forceinline__ void load_queries(const char* qlds, int lane, int W, int G, int rpg_shift,
-                                             u32x4_t (&qf)[2][4]) {
-  const int rpg_mask = (1 << rpg_shift) - 1;
-  const int q = lane >> 4;
-#pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
-    const int m = qs * 16 + (lane & 15);
-    const int g = m >> rpg_shift, r = m & rpg_mask;
-    const bool ok = g < G && r < W;
-    const int n = ok ? g * W + r : 0;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qf[qs][ks] = ok ? ld16(qlds + frag_offset<bf16_bits>(n, q + 4 * ks)) : zero16();
   }
 }
 
@@ -285,49 +225,6 @@ __device__ __forceinline__ void publish_cols(float (&cm)[2], float* dst, int lan
     const float x = max_quarters(cm[cs]);
     if (lane < 16) dst[cs * 16 + lane] = x;
   }
-}
-
-// Importance of 16 keys key0 + l%16 from their fragments (lane l's key is
-// l % 16 in every quarter): weights of the window queries as MFMA rows
-// (queries 16*qs + 4*(l/16) + v in acc[qs][v]), summed over a head's rows
-// and pooled over heads by in-lane steps and two lane exchanges, then
-// scaled by inv_pool (1/w; 1/(w*G) under mean pooling).
-__device__ __forceinline__ float key_importance16(const u32x4_t (&kf)[4], const u32x4_t (&qf)[2][4],
-                                                  const float (&smax)[2][4],
-                                                  const float (&sinv)[2][4], int key0, int N,
-                                                  int W, int rpg_shift, bool causal, bool mean,
-                                                  float inv_pool, int lane) {
-  asm volatile("" : "+v"(lane));   // per call: keeps lane-derived masks out of loop preheaders
-  const int rpg_mask = (1 << rpg_shift) - 1;
-  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) mma16(acc[qs], qf[qs][ks], kf[ks]);   // C[query][key]
-  const int key = key0 + (lane & 15);
-  const int q = lane >> 4;
-  // bit b of the query index m = 16 qs + 4 q + v: summed within a head
-  // (b < rpg_shift) or under mean pooling, else max over heads
-  auto comb = [&](float a, float b, int bit) {
-    return (mean || bit < rpg_shift) ? a + b : fmaxf(a, b);
-  };
-  float x[2];
-#pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
-    float w[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = qs * 16 + 4 * q + v;
-      const float pr = fast_exp2(acc[qs][v] * kLogitScaleLog2 - smax[qs][v]) * sinv[qs][v];
-      const bool vis = !causal || key <= N - W + (m & rpg_mask);
-      w[v] = vis ? pr : 0.f;
-    }
-    x[qs] = comb(comb(w[0], w[1], 0), comb(w[2], w[3], 0), 1);
-    const LanePair a = pair16(x[qs]);
-    const LanePair b = pair32(comb(a.lo, a.hi, 2));
-    x[qs] = comb(b.lo, b.hi, 3);
-  }
-  return comb(x[0], x[1], 4) * inv_pool;
 }
 
 template <int kHeld>

@@ -256,8 +256,10 @@ int dense_run(const rkv_dense_desc* d, const void* K, const void* V, const void*
                          rpg_shift, st);
       if (e != hipSuccess) return hip_fail(e, "importance launch");
       if constexpr (sizeof(T) == 2) {
-        // bf16: 512-row blocks by the long-unit kernel, then selection and gather
-        const int count = units * ((p.N + 511) / 512);
+        // bf16: row blocks by the long-unit kernel, then selection and gather
+        const int lb = rkv::long_block_rows(nqb, p.symmetric());
+        p.long_shift = lb == 1024 ? 10 : 9;
+        const int count = units * ((p.N + lb - 1) / lb);
         e = rkv::run_k2_long(p, nqb, count, L.rinv, L.fin, z, dbg_R, dbg_I, d->mix_lambda, rpg_shift,
                              st);
         if (e != hipSuccess) return hip_fail(e, "redundancy launch");
@@ -421,12 +423,15 @@ void paged_plan(const rkv_paged_desc* d, const int32_t* seq_len, const int32_t* 
         ch += nch;
         scored.push_back({u, (n + rkv::kK2Rows - 1) / rkv::kK2Rows, n});
         if (bf16) {
-          // long-unit kernel: contiguous copy of the unit's keys, 512-row items
+          // long-unit kernel: contiguous copy of the unit's keys, items of
+          // lb rows (tb tiles), costed by the tiles each streams
           P.kc_base[u] = P.kc_elems;
-          const int nb = (n + 127) / 128, nb5 = (n + 511) / 512;
-          for (int blk = 0; blk < nb5; ++blk) {
+          const int lb = rkv::long_block_rows(P.nqb, sym), tb = lb / 128;
+          const int nb = (n + 127) / 128, nbl = (n + lb - 1) / lb;
+          for (int blk = 0; blk < nbl; ++blk) {
             rkv::LongItem it{u, blk, n, 0, P.kc_elems, sc - (int64_t)H * n + (int64_t)hk * n};
-            const int64_t tiles = sym ? nb + std::min(4, nb - 4 * blk) - 1 : std::min(nb, 4 * blk + 4);
+            const int own = std::min(tb, nb - tb * blk);
+            const int64_t tiles = sym ? nb + own - 1 : (int64_t)tb * blk + own;
             litems.push_back({tiles, it});
           }
           P.kc_elems += (int64_t)n * 128;

@@ -170,6 +170,34 @@ __host__ __device__ inline LongPlan long_plan_choose(int gw, int nqb) {
   return none;
 }
 
+// LDS plan of the long-unit kernel's 1024-row form (k2_long.hip, one window
+// query block, causal-order R): a ring of `slots` tiles with the 1/||k|| of
+// their rows, per item parity the window queries and softmax normalisers, and
+// the 1/||k|| and importance of the item's 1024 rows.
+struct LongPlanR {
+  int slots, rn, q, qbytes, stats, rrn, rim, total;
+};
+
+__host__ __device__ inline LongPlanR long_plan_r(int gw) {
+  LongPlanR L;
+  L.slots = 3;
+  L.rn = L.slots * 128 * 256;
+  L.q = L.rn + L.slots * 128 * 4;
+  L.qbytes = (gw * 256 + 1023) / 1024 * 1024;
+  L.stats = L.q + 2 * L.qbytes;
+  L.rrn = L.stats + 2 * 32 * 8;
+  L.rim = L.rrn + 1024 * 4;
+  L.total = L.rim + 1024 * 4;
+  if (L.total > kLdsBytesPerCU) L.total = 0;
+  return L;
+}
+
+// Rows per work item of the long-unit kernel: 1024 (keys held in registers)
+// for one window-query block and the causal-order R, else 512.
+__host__ __device__ inline int long_block_rows(int nqb, bool symmetric) {
+  return (nqb == 1 && !symmetric) ? 1024 : 512;
+}
+
 template <typename T>
 struct Finish {
   int32_t* queue;      // [8] items claimed per XCD; cleared by the statistics pass
@@ -230,11 +258,13 @@ struct DenseProblem : VariantBits {
     return u < num_units;
   }
 
-  // long-unit kernel items, in order of decreasing work: block index
-  // descending (a block sweeps its own tiles and every tile left of it)
-  __device__ int long_count() const { return num_units * ((N + 511) / 512); }
+  // long-unit kernel items of 1 << long_shift rows, in order of decreasing
+  // work: block index descending (a block sweeps its own tiles and every tile
+  // left of it)
+  int long_shift = 9;
+  __device__ int long_count() const { return num_units * ((N + (1 << long_shift) - 1) >> long_shift); }
   __device__ LongItem long_item(int k) const {
-    const int nb5 = (N + 511) / 512;
+    const int nb5 = (N + (1 << long_shift) - 1) >> long_shift;
     LongItem it;
     it.blk = nb5 - 1 - k / num_units;
     it.u = k - (k / num_units) * num_units;
