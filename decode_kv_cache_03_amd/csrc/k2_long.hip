@@ -1,6 +1,9 @@
-// Long units (bf16): redundancy, importance and Z of one 512-row block per
-// work item, by an 8-wave workgroup per CU that streams the unit's key tiles
-// through an LDS ring.
+// Long units (bf16): redundancy, importance and Z of one row block per work
+// item, by an 8-wave workgroup per CU that streams the unit's key tiles
+// through an LDS ring. Two kernels: items of 1024 rows held in registers as
+// 16x16 fragments (namespace longr, below: the causal R with one window-query
+// block), and items of 512 rows as 32x32 fragments (namespace longu: the
+// symmetric R and groups of more than one query block).
 //
 // Same arithmetic as the other scoring kernels (pages and readings cited in
 // k2_redundancy.hip): R_i = max_{j<i} cos(k_i, k_j) (every j != i for the
@@ -587,26 +590,22 @@ __global__ __launch_bounds__(kThreads, 1) void k2lr_kernel(P p, const float* __r
             if (col_in_tile < row0 + rs * 16 + v) mx[s][rs][v] = vmax(mx[s][rs][v], acc[rs][v] * rc);
       }
     };
-    // as block, unmasked, for two column sub-blocks at once: each running
-    // max takes both products in one three-way max
-    auto block2 = [&](auto sc, const u32x4_t (&bf)[2][4], float rc0, float rc1) {
-      constexpr int s = decltype(sc)::value;
-      f32x4_t acc[2][2];
-#pragma unroll
-      for (int rs = 0; rs < 2; ++rs)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) acc[rs][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // unmasked rows of half-block u = 2s + rs of the held slots against two
+    // column sub-blocks: the products (half_mma), then the running maxima,
+    // each taking both products in one three-way max (half_max)
+    auto half_mma = [&](auto uc, const u32x4_t (&bf)[2][4], f32x4_t (&acc)[2]) {
+      constexpr int s = decltype(uc)::value >> 1, rs = decltype(uc)::value & 1;
+      acc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      acc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int rs = 0; rs < 2; ++rs)
+        for (int h = 0; h < 2; ++h) mma16(acc[h], A[s][rs][ks], bf[h][ks]);
+    };
+    auto half_max = [&](auto uc, const f32x4_t (&acc)[2], float rc0, float rc1) {
+      constexpr int s = decltype(uc)::value >> 1, rs = decltype(uc)::value & 1;
 #pragma unroll
-          for (int h = 0; h < 2; ++h) mma16(acc[rs][h], A[s][rs][ks], bf[h][ks]);
-#pragma unroll
-      for (int rs = 0; rs < 2; ++rs)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          mx[s][rs][v] = vmax(mx[s][rs][v], vmax(acc[rs][0][v] * rc0, acc[rs][1][v] * rc1));
+      for (int v = 0; v < 4; ++v) mx[s][rs][v] = vmax(mx[s][rs][v], vmax(acc[0][v] * rc0, acc[1][v] * rc1));
     };
 
     const int len = g.len();
@@ -665,10 +664,24 @@ __global__ __launch_bounds__(kThreads, 1) void k2lr_kernel(P p, const float* __r
           load_frag(slot, cs * 16 + 16, lane_u, bf[1]);
           const float rc0 = rns[cs * 16 + (lane_u & 15)];
           const float rc1 = rns[cs * 16 + 16 + (lane_u & 15)];
-          block2(std::integral_constant<int, 0>{}, bf, rc0, rc1);
-          block2(std::integral_constant<int, 1>{}, bf, rc0, rc1);
-          block2(std::integral_constant<int, 2>{}, bf, rc0, rc1);
-          block2(std::integral_constant<int, 3>{}, bf, rc0, rc1);
+          // a software pipeline over the eight half-blocks: the maxima of
+          // u - 1 are taken between the products of u
+          f32x4_t acc[2][2];
+          auto stage = [&](auto uc) {
+            constexpr int u = decltype(uc)::value;
+            half_mma(uc, bf, acc[u & 1]);
+            half_max(std::integral_constant<int, u - 1>{}, acc[(u - 1) & 1], rc0, rc1);
+            interleave_8mfma_12valu();
+          };
+          half_mma(std::integral_constant<int, 0>{}, bf, acc[0]);
+          stage(std::integral_constant<int, 1>{});
+          stage(std::integral_constant<int, 2>{});
+          stage(std::integral_constant<int, 3>{});
+          stage(std::integral_constant<int, 4>{});
+          stage(std::integral_constant<int, 5>{});
+          stage(std::integral_constant<int, 6>{});
+          stage(std::integral_constant<int, 7>{});
+          half_max(std::integral_constant<int, 7>{}, acc[1], rc0, rc1);
         }
       } else {
 #pragma unroll 1

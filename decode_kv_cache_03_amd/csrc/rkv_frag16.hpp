@@ -55,6 +55,19 @@ __device__ __forceinline__ float max_quarters(float x) {
 // hold no NaN, where the two agree up to the sign of a zero.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
+// Scheduling hint for one pipeline stage of 8 MFMA and 12 VALU instructions
+// (products of one row half-block, maxima of the previous one): two MFMA,
+// then six times two VALU and one MFMA, so the VALU work sits between the
+// matrix instructions instead of after all of them.
+__device__ __forceinline__ void interleave_8mfma_12valu() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+}
+
 // acc += A * B over 32 k-values (16x16 tile): lane l gives row / column
 // l % 16 and k-values 8*(l/16).. of its operand; lane l receives
 // C[4*(l/16) + v][l % 16] in acc[v].
