@@ -379,19 +379,18 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
       ensure_issued(c);
       wait_vm(vm - (cons_slot == 0 ? mark0 : mark1));
       lds_barrier();
-      refill(c);
       const char* slot = lds + cons_slot * kTileBytes;
       // a slice of the previous unit's kept V rows, into this wave's staging
-      // (lane order); stored at the end of the step
+      // (lane order), one chunk per column block of the pair loop below so
+      // the loads enter the memory pipeline between the matrix work; stored
+      // at the end of the step
       const int nv = vg ? max(0, min(kps, kv_total - t * kps)) : 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (j >= nv) continue;
+      auto v_chunk = [&](int j) {
         const int q = (t * kps + j) * kThreads + tid_u;
         const int r = min(q >> 4, B - 1);   // chunks past the end re-read a kept row
         load16_to_lds(reinterpret_cast<const char*>(p.vrow(pu, ks[r])) + (q & 15) * 16,
                       vstage + (wave * 4 + j) * 1024);
-      }
+      };
       vm += nv;
       if (t > 0 && tid_u < 128) finalize(t - 1, false, tid_u);
 
@@ -419,6 +418,11 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
       const bool has_diag = t < nh && (wave >> 2) == (t & 1);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
+        // the next tile's loads, after one column block of matrix work (the
+        // slot freed at this step's barrier), so the step does not open with
+        // every wave queueing memory instructions
+        if (cb == 1) refill(c);
+        if (cb < nv) v_chunk(cb);
         u32x4_t bf[2][4];
         load_frag(slot, cb * 32, lane_u, bf[0]);
         load_frag(slot, cb * 32 + 16, lane_u, bf[1]);

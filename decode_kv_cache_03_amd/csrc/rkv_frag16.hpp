@@ -126,18 +126,44 @@ __device__ __forceinline__ float key_importance16(const u32x4_t (&kf)[4], const 
   auto comb = [&](float a, float b, int bit) {
     return (mean || bit < rpg_shift) ? a + b : fmaxf(a, b);
   };
+  // probabilities; keys before the window are seen by every window query
+  // (a block-uniform test), so only later keys take the causal mask
+  float w[2][4];
+  const bool all_seen = !causal || key0 + 15 <= N - W;
+  if (all_seen) {
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        w[qs][v] = fast_exp2(acc[qs][v] * kLogitScaleLog2 - smax[qs][v]) * sinv[qs][v];
+  } else {
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = qs * 16 + 4 * q + v;
+        const float pr = fast_exp2(acc[qs][v] * kLogitScaleLog2 - smax[qs][v]) * sinv[qs][v];
+        w[qs][v] = key <= N - W + (m & rpg_mask) ? pr : 0.f;
+      }
+  }
+  if (!mean && rpg_shift == 3) {
+    // 8 rows per head (windows of 5..8 queries), max over heads: bits 0..2
+    // of the query index are summed, bits 3 and 4 maxed
+    float x[2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      x[qs] = (w[qs][0] + w[qs][1]) + (w[qs][2] + w[qs][3]);
+      const LanePair a = pair16(x[qs]);
+      x[qs] = a.lo + a.hi;
+      const LanePair b = pair32(x[qs]);
+      x[qs] = fmaxf(b.lo, b.hi);
+    }
+    return fmaxf(x[0], x[1]) * inv_pool;
+  }
   float x[2];
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
-    float w[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = qs * 16 + 4 * q + v;
-      const float pr = fast_exp2(acc[qs][v] * kLogitScaleLog2 - smax[qs][v]) * sinv[qs][v];
-      const bool vis = !causal || key <= N - W + (m & rpg_mask);
-      w[v] = vis ? pr : 0.f;
-    }
-    x[qs] = comb(comb(w[0], w[1], 0), comb(w[2], w[3], 0), 1);
+    x[qs] = comb(comb(w[qs][0], w[qs][1], 0), comb(w[qs][2], w[qs][3], 0), 1);
     const LanePair a = pair16(x[qs]);
     const LanePair b = pair32(comb(a.lo, a.hi, 2));
     x[qs] = comb(b.lo, b.hi, 3);
