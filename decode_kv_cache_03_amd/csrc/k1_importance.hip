@@ -18,7 +18,11 @@
 //                the A operand, so each lane owns one query column and its
 //                running max / sum of exp stay in registers; also writes
 //                1/||k|| for every key, and for paged bf16 units copies the
-//                keys to contiguous rows for the long-unit kernel.
+//                keys to contiguous rows for the long-unit kernel. bf16 key
+//                rows reach LDS by direct loads of whole rows per
+//                instruction; fragments and the copy read them from there
+//                (loads of one row per lane touch 64 cache lines per
+//                instruction, 16 bytes of each).
 //   k1_combine   per unit: merges the chunks' (max, sum) per query row into
 //                (max, 1/sum).
 // A query row's normaliser needs every key before any weight can be formed,
@@ -72,19 +76,53 @@ __global__ __launch_bounds__(256) void k1_stats_kernel(P p, float* __restrict__ 
 
   float mloc[NQB], sloc[NQB];
   float lg[2][NQB][16];
+  // bf16: the wave's 64 key rows come into LDS by direct loads, 16 lanes per
+  // row (whole rows per instruction), position q of row r holding chunk
+  // q ^ (r & 15); fragments and the paged key copy read them from there
+  __shared__ __attribute__((aligned(16))) char kst[sizeof(T) == 2 ? 4 * 64 * 256 : 16];
+  char* const ws = kst + (sizeof(T) == 2 ? wave * 64 * 256 : 0);
+  const int rbase = chunk * kK1Keys + wave * 64;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rr = 4 * i + (lane >> 4);
+      const int key = min(rbase + rr, N - 1);   // rows past N repeat row N-1
+      load16_to_lds(reinterpret_cast<const char*>(p.krow(u, key)) + (((lane & 15) ^ (rr & 15)) << 4),
+                    ws + i * 1024);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's rows are in
+    // paged units scored by the long-unit kernel: their keys to contiguous
+    // rows, a whole row per 16 lanes
+    if (p.copy_dst(u, 0) != nullptr) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rr = 4 * i + (lane >> 4);
+        const int key = rbase + rr;
+        if (key < N)
+          st16(reinterpret_cast<char*>(p.copy_dst(u, key)) + (((lane & 15) ^ (rr & 15)) << 4),
+               ld16(ws + i * 1024 + lane * 16));
+      }
+    }
+  }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const int kbase = chunk * kK1Keys + wave * 64 + kb * 32;
+    const int kbase = rbase + kb * 32;
     const int key = kbase + (lane & 31);
     const bool kvalid = key < N;
     u32x4_t kf[NCH];
-    load_half_row<T>(kf, kvalid ? p.krow(u, key) : p.krow(u, 0), half, kvalid);
-    // paged units scored by the long-unit kernel: their keys to contiguous rows
-    if (kvalid) {
-      T* dst = p.copy_dst(u, key);
-      if (dst != nullptr) {
+    if constexpr (sizeof(T) == 2) {
+      const int rr = kb * 32 + (lane & 31);
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) st16(reinterpret_cast<char*>(dst) + half * (NCH * 16) + 16 * c, kf[c]);
+      for (int c = 0; c < NCH; ++c) kf[c] = kvalid ? ld16(ws + frag_offset<T>(rr, half * NCH + c)) : zero16();
+    } else {
+      load_half_row<T>(kf, kvalid ? p.krow(u, key) : p.krow(u, 0), half, kvalid);
+      // paged units scored by the long-unit kernel: their keys to contiguous rows
+      if (kvalid) {
+        T* dst = p.copy_dst(u, key);
+        if (dst != nullptr) {
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) st16(reinterpret_cast<char*>(dst) + half * (NCH * 16) + 16 * c, kf[c]);
+        }
       }
     }
     float ss = 0.f;
