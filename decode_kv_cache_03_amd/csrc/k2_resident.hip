@@ -33,7 +33,11 @@
 //    lane column and reduce in-lane and over two lane exchanges), then Z,
 //    the selection on Z in LDS, and the kept K rows stored from registers
 //    (the last tile's from LDS); the kept V rows move during the next unit's
-//    tile steps, a slice per step through an LDS stage.
+//    tile steps, a slice per step through an LDS stage;
+//  * a step's memory instructions are spread over its column loop (one V
+//    chunk per column block, the next tile's loads after the first block):
+//    issued together right after the step barrier, the eight waves' loads
+//    queue at the CU's vector-memory path and hold back the matrix work.
 // Variants: without the causal window the statistics and weights mask only
 // padding keys; mean pooling sums the heads' window means and divides by G.
 // The symmetric R needs later keys as well and is served by k2_wide.hip.
