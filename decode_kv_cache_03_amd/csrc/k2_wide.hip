@@ -489,9 +489,17 @@ __global__ __launch_bounds__(kThreads, 1) void k2f_kernel(
       int32_t* kept = kept_all + p.kept_off(u);
       select_block<kThreads>(zs, N, B, W, kept, ssh, ks);
       __syncthreads();
-      gather_rows_block<T, kThreads>(ks, B, [&](int r) { return p.krow(u, r); },
-                                     [&](int r) { return p.vrow(u, r); },
-                                     K_out + (int64_t)u * out_stride, V_out + (int64_t)u * out_stride);
+      auto srck = [&](int r) { return p.krow(u, r); };
+      auto srcv = [&](int r) { return p.vrow(u, r); };
+      // the phase R registers are free here: 12 chunks of each tensor per
+      // round for budgets of 2048 or more (qwen-14b: 4% faster per event),
+      // 8 below (at B = 1024 the longer rounds measured 3% slower)
+      if (B >= 2048)
+        gather_rows_block<T, kThreads, decltype(srck), decltype(srcv), 12>(
+            ks, B, srck, srcv, K_out + (int64_t)u * out_stride, V_out + (int64_t)u * out_stride);
+      else
+        gather_rows_block<T, kThreads, decltype(srck), decltype(srcv), 8>(
+            ks, B, srck, srcv, K_out + (int64_t)u * out_stride, V_out + (int64_t)u * out_stride);
     }
     // ks is next written by the next unit's selection, after the barriers of
     // its statistics and redundancy phases

@@ -131,7 +131,9 @@ __device__ __forceinline__ void stage_scores(const float* __restrict__ z, int n,
 }
 
 // Copy rows kept[0..nkeep) of two row sources into consecutive output rows, as
-// 16-byte chunks, in rounds of U chunks of each tensor per thread. Rounds are
+// 16-byte chunks, in rounds of U chunks of each tensor per thread (a caller
+// whose registers are free at that point takes more per round: the copy is
+// bounded by the bytes a CU keeps in flight). Rounds are
 // software-pipelined two deep: the loads of round r+1 are in flight while
 // round r is stored. Output chunk q sits at byte 16q, so the stores are
 // buffer stores with one per-thread offset and a uniform per-chunk offset:
@@ -141,12 +143,11 @@ __device__ __forceinline__ void stage_scores(const float* __restrict__ z, int n,
 // keys; K rows are usually still cached from scoring and are read normally.
 // Branch-free tails: chunks past the end read row kept[0] again and their
 // stores fall outside the buffer range, which drops them.
-template <typename T, int NT, class SrcK, class SrcV>
+template <typename T, int NT, class SrcK, class SrcV, int U = 8>
 __device__ __forceinline__ void gather_rows_block(const int32_t* __restrict__ kept, int nkeep,
                                                   SrcK srck, SrcV srcv, T* __restrict__ K_out,
                                                   T* __restrict__ V_out) {
   constexpr int RC = Elem<T>::kRowChunks;
-  constexpr int U = 8;
   constexpr int kRound = NT * U;   // chunks per round
   const int total = nkeep * RC;
   int tid = threadIdx.x;
