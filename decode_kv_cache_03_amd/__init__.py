@@ -62,6 +62,30 @@ def _require_cuda(*ts):
     for t in ts:
         if t is not None and not t.is_cuda:
             raise ValueError("tensors must be on a GPU (the library has no CPU path)")
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors must share one GPU (got {sorted(str(d) for d in devs)})")
+
+
+def _check_rows_out(name, t, dtype, bh, rows):
+    """An output of [bh, >= rows, 128] rows of `dtype`, rows contiguous: the
+    library writes rows * 128 elements per unit at the tensor's unit stride."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype} (got {t.dtype})")
+    if t.dim() != 3 or t.shape[0] != bh or t.shape[1] < rows or t.shape[2] != HEAD_DIM:
+        raise ValueError(f"{name} must be [{bh}, >= {rows}, {HEAD_DIM}] (got {tuple(t.shape)})")
+
+
+def _check_index_out(name, t, numel, shape=None):
+    """A contiguous int32 index output of exactly `shape`, or (shape None)
+    holding at least `numel` entries."""
+    import torch
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)} (got {list(t.shape)})")
+    if t.numel() < numel:
+        raise ValueError(f"{name} must hold at least {numel} entries (got {t.numel()})")
 
 
 def variant_bits(symmetric: bool = False, causal: bool = True, pool: str = "max") -> int:
@@ -121,10 +145,15 @@ def compress(K, V, Q_win, kv_budget: int, window_size: int = 8, mix_lambda: floa
         K_out = torch.empty((bh, b, HEAD_DIM), dtype=K.dtype, device=dev)
     if V_out is None:
         V_out = torch.empty((bh, b, HEAD_DIM), dtype=K.dtype, device=dev)
-    if K_out.stride() != V_out.stride() or K_out.stride(2) != 1 or K_out.stride(1) != HEAD_DIM:
-        raise ValueError("K_out and V_out rows must be contiguous with equal strides")
     if kept_idx is None:
         kept_idx = torch.empty((bh, b), dtype=torch.int32, device=dev)
+    _require_cuda(K, K_out, V_out, kept_idx)
+    # the library writes min(N, B) rows per unit (kept indices: B per unit)
+    _check_rows_out("K_out", K_out, K.dtype, bh, min(n, b))
+    _check_rows_out("V_out", V_out, K.dtype, bh, min(n, b))
+    if K_out.stride() != V_out.stride() or K_out.stride(2) != 1 or K_out.stride(1) != HEAD_DIM:
+        raise ValueError("K_out and V_out rows must be contiguous with equal strides")
+    _check_index_out("kept_idx", kept_idx, bh * b, shape=(bh, b))
     dbg = [torch.empty((bh, n), dtype=torch.float32, device=dev) for _ in range(3)] if debug \
         else [None, None, None]
     d = dense_desc(bh, n, g, window_size, b, mix_lambda, _dtype_code(K),
@@ -168,7 +197,9 @@ def compress_paged(K_pages, V_pages, page_table, seq_len, budget, Q_win, free_li
     indices and the new free count.
     """
     import torch
-    _require_cuda(K_pages, V_pages, page_table, Q_win, free_list)
+    _require_cuda(K_pages, V_pages, page_table, Q_win, free_list, kept_idx)
+    if not (K_pages.dtype == V_pages.dtype == Q_win.dtype):
+        raise TypeError("K_pages, V_pages and Q_win must share a dtype")
     if K_pages.dim() != 4 or K_pages.shape[3] != HEAD_DIM or V_pages.shape != K_pages.shape \
             or K_pages.stride() != V_pages.stride() or K_pages.stride(3) != 1:
         raise ValueError("K_pages and V_pages must be [P, H, page_size, 128] with equal strides")
@@ -196,6 +227,7 @@ def compress_paged(K_pages, V_pages, page_table, seq_len, budget, Q_win, free_li
     total_kept = H * int(sum(min(int(a), int(b)) for a, b in zip(sl, bu)))
     if kept_idx is None:
         kept_idx = torch.empty(max(total_kept, 1), dtype=torch.int32, device=dev)
+    _check_index_out("kept_idx", kept_idx, total_kept)
     zbuf = torch.empty(max(H * int(sl.sum()), 1), dtype=torch.float32, device=dev) if debug else None
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -205,6 +237,35 @@ def compress_paged(K_pages, V_pages, page_table, seq_len, budget, Q_win, free_li
                                       int(free_list.numel()), ctypes.byref(cnt), _ptr(zbuf),
                                       _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
     return PagedResult(kept_idx, int(cnt.value), zbuf)
+
+
+class PagePlanResult(NamedTuple):
+    pages_now: object       # numpy int32 [S]
+    pages_peak: object      # -1 where compression is off
+    pages_after: object
+    pages_freed: object
+    steps_to_event: object  # -1 where compression is off
+    totals: dict            # sums over the sequences with compression on
+
+
+def page_plan(seq_len, budget, page_size: int = 16, divide_length: int = 128) -> PagePlanResult:
+    """Page accounting of a paged cache under periodic compression, for a
+    scheduler that admits requests on the compressed footprint (host only;
+    see rkv_paged_plan in rkv.h)."""
+    import numpy as np
+    sl, sl_p = _host_i32(seq_len)
+    bu, bu_p = _host_i32(budget)
+    if sl.shape != bu.shape or sl.ndim != 1:
+        raise ValueError("seq_len and budget need one entry per sequence")
+    S = int(sl.shape[0])
+    plan = (_lib.PagePlan * max(S, 1))()
+    tot = (ctypes.c_int64 * 4)()
+    _lib.check(_lib.load().rkv_paged_plan(S, sl_p, bu_p, int(page_size), int(divide_length), plan,
+                                          tot))
+    cols = {f: np.array([getattr(plan[i], f) for i in range(S)], dtype=np.int32)
+            for f, _ in _lib.PagePlan._fields_}
+    totals = dict(zip(("pages_now", "pages_peak", "pages_after", "pages_freed"), map(int, tot)))
+    return PagePlanResult(**cols, totals=totals)
 
 
 def timing_enable(on: bool = True) -> None:

@@ -24,7 +24,7 @@ STATUS_NAMES = {RKV_OK: "RKV_OK", RKV_EINVAL: "RKV_EINVAL", RKV_EWORKSPACE: "RKV
                 RKV_EHIP: "RKV_EHIP"}
 
 EXPORTS = ["rkv_workspace_size", "rkv_compress", "rkv_paged_workspace_size", "rkv_compress_paged",
-           "rkv_last_error", "rkv_timing_enable", "rkv_timing_read"]
+           "rkv_paged_plan", "rkv_last_error", "rkv_timing_enable", "rkv_timing_read"]
 
 
 class DenseDesc(ctypes.Structure):
@@ -44,6 +44,12 @@ class PagedDesc(ctypes.Structure):
                 ("mix_lambda", ctypes.c_float), ("dtype", ctypes.c_int32),
                 ("page_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
                 ("slot_stride", ctypes.c_int64), ("variant", ctypes.c_uint32)]
+
+
+class PagePlan(ctypes.Structure):
+    _fields_ = [("pages_now", ctypes.c_int32), ("pages_peak", ctypes.c_int32),
+                ("pages_after", ctypes.c_int32), ("pages_freed", ctypes.c_int32),
+                ("steps_to_event", ctypes.c_int32)]
 
 
 class RkvError(RuntimeError):
@@ -76,6 +82,9 @@ def load():
     lib.rkv_compress_paged.argtypes = [ctypes.POINTER(PagedDesc), vp, vp, vp, pi32, pi32, vp, vp, vp,
                                        i32, pi32, vp, vp, sz, vp]
     lib.rkv_compress_paged.restype = ctypes.c_int
+    lib.rkv_paged_plan.argtypes = [i32, pi32, pi32, i32, i32, ctypes.POINTER(PagePlan),
+                                   ctypes.POINTER(ctypes.c_int64)]
+    lib.rkv_paged_plan.restype = ctypes.c_int
     lib.rkv_last_error.argtypes = []
     lib.rkv_last_error.restype = ctypes.c_char_p
     lib.rkv_timing_enable.argtypes = [ctypes.c_int]

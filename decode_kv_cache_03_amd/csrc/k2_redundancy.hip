@@ -548,8 +548,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k2_items_kernel(
         }
         __syncthreads();
         const int uu = u;
-        gather_rows_block<T, 256>(staged ? ks : kept, Bu, [&](int r) { return p.krow(uu, r); },
-                             [&](int r) { return p.vrow(uu, r); }, fs.K_out + (int64_t)u * fs.out_stride,
+        gather_rows_block<T, 256>(staged ? ks : kept, Bu, [&](int r) { return p.krow(uu, clamp_row(r, N)); },
+                             [&](int r) { return p.vrow(uu, clamp_row(r, N)); }, fs.K_out + (int64_t)u * fs.out_stride,
                              fs.V_out + (int64_t)u * fs.out_stride);
         __syncthreads();   // the staging buffer is a tile buffer again
       }

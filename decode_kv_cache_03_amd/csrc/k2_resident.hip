@@ -392,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
       auto v_chunk = [&](int j) {
         const int q = (t * kps + j) * kThreads + tid_u;
         const int r = min(q >> 4, B - 1);   // chunks past the end re-read a kept row
-        load16_to_lds(reinterpret_cast<const char*>(p.vrow(pu, ks[r])) + (q & 15) * 16,
+        load16_to_lds(reinterpret_cast<const char*>(p.vrow(pu, clamp_row(ks[r], N))) + (q & 15) * 16,
                       vstage + (wave * 4 + j) * 1024);
       };
       vm += nv;
@@ -639,7 +639,10 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
       // output row of every candidate (-1: dropped), in the norms' place
       for (int i = tid_u; i < N; i += kThreads) pos[i] = -1;
       __syncthreads();
-      for (int r = tid_u; r < B; r += kThreads) pos[ks[r]] = r;
+      for (int r = tid_u; r < B; r += kThreads) {
+        const int kr = ks[r];
+        if ((unsigned)kr < (unsigned)N) pos[kr] = r;
+      }
       __syncthreads();
       // kept K rows held in registers: lane quarter q writes chunks q + 4*ks,
       // so the four quarters of a row fill 64 contiguous bytes per store;
@@ -683,7 +686,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
   }
   // the last unit's kept V rows: no later unit carries them
   if (last_u >= 0)
-    gather_rows_block<bf16_bits, kThreads>(ks, B, [&](int r) { return p.vrow(last_u, r); },
+    gather_rows_block<bf16_bits, kThreads>(ks, B, [&](int r) { return p.vrow(last_u, clamp_row(r, N)); },
                                            V_out + (int64_t)last_u * out_stride);
 }
 

@@ -489,8 +489,8 @@ __global__ __launch_bounds__(kThreads, 1) void k2f_kernel(
       int32_t* kept = kept_all + p.kept_off(u);
       select_block<kThreads>(zs, N, B, W, kept, ssh, ks);
       __syncthreads();
-      auto srck = [&](int r) { return p.krow(u, r); };
-      auto srcv = [&](int r) { return p.vrow(u, r); };
+      auto srck = [&](int r) { return p.krow(u, clamp_row(r, N)); };
+      auto srcv = [&](int r) { return p.vrow(u, clamp_row(r, N)); };
       // the phase R registers are free here: 12 chunks of each tensor per
       // round for budgets of 2048 or more (qwen-14b: 4% faster per event),
       // 8 below (at B = 1024 the longer rounds measured 3% slower)

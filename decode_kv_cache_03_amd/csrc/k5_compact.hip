@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void k5_gather_kernel(DenseProblem<T> p,
     const int q = i * 256 + tid;
     const int r = r0 + q / RC, c = q % RC;
     if (r < nkeep) {
-      const int src = kept[r];
+      const int src = clamp_row(kept[r], p.N);
       kv[i] = ld16(reinterpret_cast<const char*>(p.krow(u, src)) + 16 * c);
       vv[i] = ld16(reinterpret_cast<const char*>(p.vrow(u, src)) + 16 * c);
     }
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void k5_paged_kernel(PagedProblem<T> p, T* Kp,
     for (int i = 0; i < PER; ++i) {
       const int q = i * 256 + tid;
       const int r = c0 + q / RC, c = q % RC;
-      src[i] = (r < B) ? kept[r] : r;
+      src[i] = (r < B) ? clamp_row(kept[r], N) : r;
       if (src[i] != r) {
         kv[i] = ld16(reinterpret_cast<const char*>(p.krow(u, src[i])) + 16 * c);
         vv[i] = ld16(reinterpret_cast<const char*>(p.vrow(u, src[i])) + 16 * c);

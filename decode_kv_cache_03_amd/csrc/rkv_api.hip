@@ -645,6 +645,54 @@ extern "C" int rkv_compress_paged(const rkv_paged_desc* desc, void* K_pages, voi
   return rc;
 }
 
+// ---- page accounting for admission ---------------------------------------------
+extern "C" int rkv_paged_plan(int32_t num_seqs, const int32_t* seq_len_host,
+                              const int32_t* budget_host, int32_t page_size, int32_t divide_length,
+                              rkv_page_plan* plan_host, int64_t* totals_host) {
+  if (num_seqs < 0) return fail(RKV_EINVAL, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (page_size < 1 || page_size > 4096 || log2_exact(page_size) < 0)
+    return fail(RKV_EINVAL, "page_size must be a power of two in [1, 4096] (got %d)", page_size);
+  if (divide_length < 0) return fail(RKV_EINVAL, "divide_length must be >= 0 (got %d)", divide_length);
+  if (num_seqs > 0 && (!seq_len_host || !budget_host))
+    return fail(RKV_EINVAL, "seq_len_host and budget_host must be non-NULL");
+  for (int s = 0; s < num_seqs; ++s) {
+    const int32_t n = seq_len_host[s], b = budget_host[s];
+    if (n < 0) return fail(RKV_EINVAL, "seq_len[%d] = %d must be >= 0", s, n);
+    if (b < 0 || b % page_size)
+      return fail(RKV_EINVAL, "budget[%d] = %d must be 0 or a positive multiple of page_size %d", s,
+                  b, page_size);
+    if ((int64_t)b + divide_length > INT32_MAX)
+      return fail(RKV_EINVAL, "budget[%d] + divide_length overflows", s);
+  }
+  int64_t tot[4] = {0, 0, 0, 0};
+  auto pages = [&](int64_t tokens) { return (int32_t)((tokens + page_size - 1) / page_size); };
+  for (int s = 0; s < num_seqs; ++s) {
+    const int64_t n = seq_len_host[s], b = budget_host[s];
+    rkv_page_plan pl;
+    pl.pages_now = pages(n);
+    if (b == 0 || divide_length == 0) {   // compression off for this sequence
+      pl.pages_peak = -1;
+      pl.pages_after = pl.pages_now;
+      pl.pages_freed = 0;
+      pl.steps_to_event = -1;
+    } else {
+      const int64_t cap = b + divide_length;   // length at which the append compresses
+      pl.pages_peak = pages(std::max(n, cap));
+      pl.pages_after = (int32_t)(b / page_size);
+      pl.pages_freed = pl.pages_peak - pl.pages_after;
+      pl.steps_to_event = n >= cap ? 0 : (int32_t)(cap - n);
+      tot[0] += pl.pages_now;
+      tot[1] += pl.pages_peak;
+      tot[2] += pl.pages_after;
+      tot[3] += pl.pages_freed;
+    }
+    if (plan_host) plan_host[s] = pl;
+  }
+  if (totals_host)
+    for (int i = 0; i < 4; ++i) totals_host[i] = tot[i];
+  return RKV_OK;
+}
+
 // ---- errors and timing --------------------------------------------------------
 extern "C" const char* rkv_last_error(void) { return g_error.c_str(); }
 

@@ -59,6 +59,11 @@ constexpr int kCachePolicyStream = 2;
 __device__ __forceinline__ void st16(void* p, u32x4_t v) {
   *reinterpret_cast<u32x4_t*>(p) = v;
 }
+
+// A row index taken from a kept list, forced into [0, n): a kept list that is
+// stale or only partly written then reads rows of the right unit (a wrong
+// result a test reports) instead of memory outside the unit.
+__device__ __forceinline__ int clamp_row(int r, int n) { return min(max(r, 0), n - 1); }
 __device__ __forceinline__ u32x4_t zero16() {
   u32x4_t z = {0u, 0u, 0u, 0u};
   return z;

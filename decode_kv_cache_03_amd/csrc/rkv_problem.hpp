@@ -223,6 +223,8 @@ struct DenseProblem : VariantBits {
 
   __device__ int n(int) const { return N; }
   __device__ int budget(int) const { return B; }
+  // Row t of unit u, unchecked: tile loads pass rows bounded by construction;
+  // rows read from a kept list go through clamp_row first.
   __device__ const T* krow(int u, int t) const { return K + (int64_t)u * kv_stride + (int64_t)t * kD; }
   __device__ const T* vrow(int u, int t) const { return V + (int64_t)u * kv_stride + (int64_t)t * kD; }
   __device__ const T* q(int u) const { return Q + (int64_t)u * G * W * kD; }
@@ -313,9 +315,11 @@ struct PagedProblem : VariantBits {
   __device__ const T* row_in(const T* pool, int u, int t) const {
     const int s = u / H;
     const int hk = u - s * H;
-    int pg = page_table[(int64_t)s * maxp + (t >> ps_shift)];
-    // Out-of-range page ids are never dereferenced: the row reads as page 0's
-    // slot instead (results for such a table are undefined, memory stays safe).
+    // A row past the table reads its last column, and an out-of-range page
+    // id reads page 0's slot instead: results for such inputs are undefined,
+    // but memory outside the table and the pool is never touched.
+    const int col = min(max(t >> ps_shift, 0), maxp - 1);
+    int pg = page_table[(int64_t)s * maxp + col];
     pg = (pg >= 0 && pg < num_pages) ? pg : 0;
     return pool + (int64_t)pg * page_stride + (int64_t)hk * head_stride +
            (int64_t)(t & ((1 << ps_shift) - 1)) * slot_stride;

@@ -200,6 +200,54 @@ int rkv_compress_paged(const rkv_paged_desc* desc, void* K_pages, void* V_pages,
                        int32_t* free_list, int32_t free_capacity, int32_t* free_count_host,
                        float* dbg_Z, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Compression-aware admission: page accounting of a paged cache under
+ * periodic compression, on the host [P1 "What the redundancy scoring
+ * actually does at decode time": the serving port's scheduler admits
+ * requests on the compressed footprint, and compression returns freed blocks
+ * to the allocator; P3 "Approach": compression runs periodically during
+ * decoding with a fixed buffer].
+ *
+ * A sequence that holds L tokens, with budget B and buffer divide_length D,
+ * is compressed back to B tokens by the append that brings it to B + D
+ * tokens; a sequence already holding more than B + D tokens (e.g. after a
+ * long prompt) is compressed by the next call, at its current length. So it
+ * never holds more than max(L, B + D) tokens, and a scheduler that reserves
+ * that many pages per running sequence can admit new requests on the
+ * remainder. Per sequence s (a sequence occupies ceil(tokens / page_size)
+ * pages):
+ *   pages_now      ceil(L / page_size)
+ *   pages_peak     ceil(max(L, B + D) / page_size): the most it holds before
+ *                  its next compression completes
+ *   pages_after    B / page_size: held right after that compression
+ *   pages_freed    pages_peak - pages_after: returned to the free list by it
+ *                  (what rkv_compress_paged appends for s when called then)
+ *   steps_to_event tokens still to append before that compression: 0 when
+ *                  L >= B + D (due now), else B + D - L
+ * B = 0 or D = 0 switches compression off for the sequence (the pages' "0
+ * disables" convention): then pages_peak = -1 (unbounded), pages_after =
+ * pages_now, pages_freed = 0 and steps_to_event = -1. Nothing here touches a
+ * GPU. */
+typedef struct rkv_page_plan {
+  int32_t pages_now;
+  int32_t pages_peak;
+  int32_t pages_after;
+  int32_t pages_freed;
+  int32_t steps_to_event;
+} rkv_page_plan;
+
+/* Fills plan_host[s] for s < num_seqs from seq_len_host[s] (L >= 0) and
+ * budget_host[s] (B = 0, or B > 0 and a multiple of page_size), with
+ * page_size a power of two in [1, 4096] and divide_length >= 0. When
+ * totals_host is not NULL it receives four sums over the sequences with
+ * compression on: pages_now, pages_peak, pages_after and pages_freed; the
+ * pages still to be claimed before the next compressions is then
+ * totals[1] - totals[0]. All pointers are host memory; plan_host may be NULL
+ * when only totals are wanted. Returns RKV_OK, or RKV_EINVAL (nothing
+ * written) for a bad argument. */
+int rkv_paged_plan(int32_t num_seqs, const int32_t* seq_len_host, const int32_t* budget_host,
+                   int32_t page_size, int32_t divide_length, rkv_page_plan* plan_host,
+                   int64_t* totals_host);
+
 /* Message of the last failed call on this host thread ("" if none). The
  * pointer stays valid until the next call on this thread. */
 const char* rkv_last_error(void);

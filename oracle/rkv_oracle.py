@@ -235,6 +235,31 @@ def logical_rows(pages, page_table_row, n: int, head: int, page_size: int) -> np
     return np.asarray(pages)[page_table_row[t // page_size], head, t % page_size]
 
 
+def return_pages(page_table, seq_len, budget, free_list, page_size: int):
+    """Block return after compaction (reading R8) [P1 "What the redundancy
+    scoring actually does at decode time": freed blocks go back to the
+    allocator].
+
+    A compressed sequence (N_s > B_s) keeps B_s tokens in its first
+    B_s/page_size pages; each later page it held (up to ceil(N_s/page_size))
+    is appended to the free list, sequences in order and pages in order within
+    a sequence, and its table entry becomes -1. Returns (new table, new free
+    list); the inputs are not modified.
+    """
+    table = np.array(page_table, copy=True)
+    freed = [int(x) for x in free_list]
+    for s in range(table.shape[0]):
+        n = int(seq_len[s])
+        b = int(budget[s])
+        if n <= b:
+            continue
+        held = (n + page_size - 1) // page_size
+        for p in range(b // page_size, held):
+            freed.append(int(table[s, p]))
+            table[s, p] = -1
+    return table, np.asarray(freed, dtype=np.int64)
+
+
 def compress_paged(K_pages, V_pages, page_table, seq_len, budget, Q, free_list,
                    window: int, lam: float, page_size: int, **variant) -> dict:
     """Paged compression with page return (reading R8).
@@ -247,10 +272,8 @@ def compress_paged(K_pages, V_pages, page_table, seq_len, budget, Q, free_list,
     """
     Kp = np.array(K_pages, copy=True)
     Vp = np.array(V_pages, copy=True)
-    table = np.array(page_table, copy=True)
-    freed = [int(x) for x in free_list]
     kept_all = []
-    n_seq, heads = table.shape[0], Kp.shape[1]
+    n_seq, heads = np.shape(page_table)[0], Kp.shape[1]
     for s in range(n_seq):
         n = int(seq_len[s])
         b = int(budget[s])
@@ -269,9 +292,5 @@ def compress_paged(K_pages, V_pages, page_table, seq_len, budget, Q, free_list,
             Kp[page_table[s][r // page_size], h, r % page_size] = Kl[kept]
             Vp[page_table[s][r // page_size], h, r % page_size] = Vl[kept]
         kept_all.append(kept_s)
-        if n > b:
-            for p in range(b // page_size, (n + page_size - 1) // page_size):
-                freed.append(int(table[s, p]))
-                table[s, p] = -1
-    return dict(K_pages=Kp, V_pages=Vp, page_table=table,
-                free_list=np.asarray(freed, dtype=np.int64), kept=kept_all)
+    table, freed = return_pages(page_table, seq_len, budget, free_list, page_size)
+    return dict(K_pages=Kp, V_pages=Vp, page_table=table, free_list=freed, kept=kept_all)

@@ -19,8 +19,15 @@ Pinned facts and where they come from:
     identical query heads pool to the single-head importance;
   * a hand-worked 2-D example with keys at known angles;
   * structure: output size, window kept, ascending order, K'/V' = gather;
-  * paged: page table and free list follow in closed form from lengths and
-    budgets; live slots hold the kept rows; nothing else changes.
+  * paged page return, by invariants that do not restate the oracle's loop:
+    the live table entries and the free list are an exact partition of the
+    pool before and after; the free list only grows at its end, by the pages
+    a sequence no longer needs (ceil(N_s/ps) - ceil(min(N_s, B_s)/ps) each);
+    the pages a sequence keeps are its first ones, unchanged; the freed ids,
+    located in the old table, ascend by (sequence, page);
+  * paged data: live slots hold the kept rows; nothing else changes;
+  * redundancy of listed rows: equal to the brute force's R at those rows,
+    to 1 at planted exact copies and to 0 for orthogonal keys.
 
 Pins of the reading variants (symmetric redundancy, importance without the
 in-window causal mask, mean pooling over the GQA heads) and of head-shared
@@ -271,25 +278,75 @@ def check_structure(seed):
     assert np.array_equal(o["V_out"], V[kept])
 
 
+def check_page_return(table0, free0, table1, free1, seq_len, budget, ps, pool):
+    """Invariants of the page return, stated without its loop.
+
+    table0/free0: state before (live entries of the table plus the free list
+    must be an exact partition of the pool's page ids 0..pool-1); table1/free1:
+    after. A sequence of L tokens occupies ceil(L/ps) pages; after the call a
+    sequence holds min(N_s, B_s) tokens."""
+    table0 = np.asarray(table0)
+    table1 = np.asarray(table1)
+    free0 = [int(x) for x in free0]
+    free1 = [int(x) for x in free1]
+    S = len(seq_len)
+    held0 = [-(-int(n) // ps) for n in seq_len]
+    held1 = [-(-min(int(n), int(b)) // ps) for n, b in zip(seq_len, budget)]
+
+    def live(t):
+        return [int(x) for s in range(S) for x in t[s] if x >= 0]
+
+    assert sorted(live(table0) + free0) == list(range(pool)), "initial state is not a partition"
+    # the free list keeps its entries and grows at the end by the pages given up
+    assert free1[:len(free0)] == free0, "existing free-list entries changed"
+    assert len(free1) - len(free0) == sum(h0 - h1 for h0, h1 in zip(held0, held1)), \
+        "wrong number of pages returned"
+    # every page is either live in the table or free, exactly once
+    assert sorted(live(table1) + free1) == list(range(pool)), "pool not conserved"
+    for s in range(S):
+        # the pages kept are the sequence's first ones, unchanged; the ones
+        # after them no longer belong to it; the columns past its old length
+        # are untouched
+        assert np.array_equal(table1[s, :held1[s]], table0[s, :held1[s]]), f"seq {s}: kept pages moved"
+        assert np.all(table1[s, held1[s]:held0[s]] < 0), f"seq {s}: a returned page is still mapped"
+        assert np.array_equal(table1[s, held0[s]:], table0[s, held0[s]:]), f"seq {s}: columns past N_s"
+    # the freed ids, found in the old table, ascend by (sequence, page)
+    where = {int(table0[s, p]): (s, p) for s in range(S) for p in range(held0[s])}
+    at = [where[x] for x in free1[len(free0):]]
+    assert at == sorted(at), "freed pages out of (sequence, page) order"
+
+
 def check_paged(seed):
     from synth import paged_case_host
     ps = 16
-    lens = [40, 100, 16, 130]
-    fracs = [0.5, 0.3, 0.9, 0.4]
+    lens = [40, 100, 16, 130, 33]
+    fracs = [0.5, 0.3, 0.9, 0.4, 0.9]
     case = paged_case_host(seed, lens, fracs, kv_heads=2, gqa=2, window=4, lam=0.1,
                            dtype="f32", page_size=ps, spare_pages=5, d=8)
     out = orc.compress_paged(case.K_pages, case.V_pages, case.page_table, case.seq_len,
                              case.budget, case.Q, case.free_list, case.window, case.lam, ps)
-    table = case.page_table.copy()
-    free = list(case.free_list)
-    for s, n in enumerate(case.seq_len):
-        b = int(case.budget[s])
-        if n > b:
-            for p in range(b // ps, -(-int(n) // ps)):
-                free.append(int(table[s, p]))
-                table[s, p] = -1
-    assert np.array_equal(out["page_table"], table)
-    assert list(out["free_list"]) == free
+    check_page_return(case.page_table, case.free_list, out["page_table"], out["free_list"],
+                      case.seq_len, case.budget, ps, case.meta["pool"])
+    # the page return step alone, on random lengths and budgets (pages of 1,
+    # 4 and 16 tokens; some sequences compressed, some not)
+    rng = _rng(seed)
+    for ps_r in (1, 4, 16):
+        S = int(rng.integers(2, 7))
+        n = rng.integers(1, 12 * ps_r, size=S)
+        b = ps_r * rng.integers(1, 8, size=S)
+        held = -(-n // ps_r)
+        maxp = int(held.max()) + int(rng.integers(0, 3))
+        pool = int(held.sum()) + int(rng.integers(0, 5))
+        perm = rng.permutation(pool)
+        table = np.full((S, maxp), -1, dtype=np.int64)
+        off = 0
+        for s in range(S):
+            table[s, :held[s]] = perm[off:off + held[s]]
+            off += int(held[s])
+        free = perm[off:]
+        t1, f1 = orc.return_pages(table, n, b, free, ps_r)
+        check_page_return(table, free, t1, f1, n, b, ps_r, pool)
+        assert np.array_equal(table, np.asarray(table)), "inputs modified"
     live = np.zeros(case.K_pages.shape[:1] + case.K_pages.shape[1:3], dtype=bool)
     for s, n in enumerate(case.seq_len):
         n = int(n)
@@ -306,6 +363,32 @@ def check_paged(seed):
                 live[pg_dst, h, r % ps] = True
     assert np.array_equal(out["K_pages"][~live], case.K_pages[~live])
     assert np.array_equal(out["V_pages"][~live], case.V_pages[~live])
+
+
+def check_redundancy_rows(seed):
+    """R of listed rows: the brute force at those rows on tiny heads (both
+    readings); 1 at planted exact copies and 0 for orthogonal keys on a larger
+    head."""
+    rng = _rng(seed)
+    n = int(rng.integers(8, 30))
+    d = int(rng.integers(2, 10))
+    K = rng.standard_normal((n, d))
+    K[n - 1] = 0.5 * K[2]
+    K[n // 2] = K[1] + 0.01 * rng.standard_normal(d)
+    rows = np.concatenate([[0, n - 1], rng.choice(n, size=5, replace=False)])
+    for sym in (False, True):
+        ref = bf.redundancy_bf(K.tolist(), symmetric=sym)
+        _close(orc.redundancy_rows(K, rows, symmetric=sym), [ref[int(i)] for i in rows])
+    n, d = 600, 64
+    K = rng.standard_normal((n, d))
+    copies = sorted(rng.choice(np.arange(100, n), size=20, replace=False).tolist())
+    for t in copies:
+        K[t] = float(rng.choice([0.25, 2.0])) * K[int(rng.integers(0, 100))]
+    R = orc.redundancy_rows(K, copies + [0, 1, 50])
+    _close(R[:len(copies)], np.ones(len(copies)), 1e-12)
+    assert R[len(copies)] == 0.0 and R[len(copies) + 1] < 1.0 - 1e-6
+    basis = np.eye(d)[rng.permutation(d)[:40]] * rng.uniform(0.5, 3.0, size=(40, 1))
+    assert np.array_equal(orc.redundancy_rows(basis, np.arange(40)), np.zeros(40))
 
 
 VARIANTS = [dict(symmetric=True), dict(causal=False), dict(pool="mean"),
@@ -426,4 +509,5 @@ ALL_CHECKS = [check_bruteforce, check_select_ties, check_lambda_one, check_lambd
               check_duplicates, check_orthogonal, check_scale_invariance, check_zero_queries,
               check_softmax_rows, check_identical_heads, check_logit_scale, check_hand_example, check_structure,
               check_paged, check_bruteforce_variants, check_symmetric_closed_forms,
-              check_unmasked_closed_forms, check_pooling_closed_forms, check_shared]
+              check_unmasked_closed_forms, check_pooling_closed_forms, check_shared,
+              check_redundancy_rows]

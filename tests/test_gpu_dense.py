@@ -153,6 +153,28 @@ def test_repeat_calls_are_bit_identical(rkv):
     assert par.bits_equal(a.K_out, b.K_out) and par.bits_equal(a.V_out, b.V_out)
 
 
+def test_binding_rejects_bad_outputs(rkv):
+    """Output buffers of the wrong dtype, shape or index type are refused in
+    the binding, before anything is launched."""
+    import torch
+    K = torch.zeros((2, 300, 128), dtype=torch.bfloat16, device="cuda")
+    V = torch.zeros_like(K)
+    Q = torch.zeros((2, 4, 8, 128), dtype=torch.bfloat16, device="cuda")
+    dev = dict(device="cuda")
+    with pytest.raises(TypeError):
+        rkv.compress(K, V, Q, 200, K_out=torch.empty((2, 200, 128), dtype=torch.float32, **dev))
+    with pytest.raises(TypeError):
+        rkv.compress(K, V, Q, 200, V_out=torch.empty((2, 200, 128), dtype=torch.float16, **dev))
+    with pytest.raises(ValueError):
+        rkv.compress(K, V, Q, 200, K_out=torch.empty((2, 100, 128), dtype=torch.bfloat16, **dev))
+    with pytest.raises(ValueError):
+        rkv.compress(K, V, Q, 200, kept_idx=torch.empty((2, 200), dtype=torch.int64, **dev))
+    with pytest.raises(ValueError):
+        rkv.compress(K, V, Q, 200, kept_idx=torch.empty((2, 100), dtype=torch.int32, **dev))
+    with pytest.raises(TypeError):
+        rkv.compress(K, V.float(), Q, 200)
+
+
 def test_zero_units_is_a_noop(rkv):
     import torch
     K = torch.zeros((0, 100, 128), dtype=torch.bfloat16, device="cuda")
@@ -162,8 +184,19 @@ def test_zero_units_is_a_noop(rkv):
     assert res.kept_idx.shape == (0, 64)
 
 
+def assert_selection_matches_scores(kept, Z, n, b, w, what):
+    """For every unit: given the device's own scores, the kept set is unique
+    (the window plus the top B-w by (Z desc, index asc), ascending), so it is
+    compared exactly with the oracle's selection step on those scores."""
+    kept = kept.cpu().numpy()
+    Z = Z.cpu().numpy().astype(np.float64)
+    bad = [h for h in range(kept.shape[0]) if not np.array_equal(kept[h], orc.select(Z[h], n, b, w))]
+    assert not bad, f"{what}: {len(bad)} units select differently from their scores, first {bad[:5]}"
+
+
 def _device_case_checks(rkv, case, sample, what):
-    """Full-size device-generated case: oracle on sampled units, structure on all."""
+    """Full-size device-generated case: oracle on sampled units; structure,
+    gather and the selection given the device's scores on every unit."""
     import torch
     res = rkv.compress(case.K, case.V, case.Q, case.budget, case.window, case.lam, debug=True)
     torch.cuda.synchronize()
@@ -176,6 +209,7 @@ def _device_case_checks(rkv, case, sample, what):
     assert par.bits_equal(res.K_out, torch.gather(case.K, 1, idx))
     assert par.bits_equal(res.V_out, torch.gather(case.V, 1, idx))
     assert bool(torch.isfinite(res.Z).all())
+    assert_selection_matches_scores(kept, res.Z, n, b, w, what)
     for h in sample:
         Kh = par.to_host_f32(case.K[h])
         Vh = par.to_host_f32(case.V[h])

@@ -2,6 +2,7 @@
 import numpy as np
 import pytest
 
+import oracle_pins as pins
 import parity as par
 from oracle import rkv_oracle as orc
 from synth import CONFIGS, paged_case_device, paged_case_host
@@ -105,7 +106,37 @@ FRACS = [0.5, 0.3, 0.9, 0.4, 0.25, 0.1, 0.34, 0.2]
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_small_ragged(rkv, dtype):
     case = paged_case_host(21, LENS, FRACS, kv_heads=2, gqa=2, window=8, lam=0.1, dtype=dtype)
-    _check_host_case(case, *_run_host_case(rkv, case))
+    out = _run_host_case(rkv, case)
+    _check_host_case(case, *out)
+    # the host page accounting agrees with what the device call returned:
+    # with a buffer of 1 every sequence above its budget is due now
+    plan = rkv.page_plan(case.seq_len, case.budget, case.page_size, divide_length=1)
+    due = plan.steps_to_event == 0
+    assert out[0].free_count - len(case.free_list) == int(plan.pages_freed[due].sum())
+    table = out[4].cpu().numpy()
+    assert np.array_equal((table >= 0).sum(axis=1)[due], plan.pages_after[due])
+
+
+def test_binding_rejects_mismatched_pools(rkv):
+    """Checks in the binding that raise before anything is launched."""
+    import torch
+    case = paged_case_host(27, LENS[:3], FRACS[:3], kv_heads=2, gqa=2, window=8, lam=0.1)
+    Kp = par.to_device(case.K_pages, "bf16")
+    table = torch.from_numpy(case.page_table).cuda()
+    Q = par.to_device(case.Q, "bf16")
+    fl = torch.full((64,), -1, dtype=torch.int32, device="cuda")
+    args = (table, case.seq_len, case.budget)
+    with pytest.raises(TypeError):
+        rkv.compress_paged(Kp, Kp.float(), *args, Q, fl, 0, case.window, case.lam)
+    with pytest.raises(TypeError):
+        rkv.compress_paged(Kp, Kp.clone(), *args, Q.float(), fl, 0, case.window, case.lam)
+    with pytest.raises(ValueError):
+        rkv.compress_paged(Kp, Kp.clone(), *args, Q, fl, 0, case.window, case.lam,
+                           kept_idx=torch.empty(3, dtype=torch.int32, device="cuda"))
+    with pytest.raises(ValueError):
+        rkv.compress_paged(Kp, Kp.clone(), *args, Q, fl, 0, case.window, case.lam,
+                           kept_idx=torch.empty(4096, dtype=torch.int64, device="cuda"))
+    assert torch.equal(table, torch.from_numpy(case.page_table).cuda())
 
 
 def test_free_list_appends_after_existing_entries(rkv):
@@ -152,20 +183,32 @@ def test_paged_ragged_full_size(rkv):
     res = rkv.compress_paged(case.K_pages, case.V_pages, table, case.seq_len, case.budget, case.Q,
                              fl, len(case.free_list), case.window, case.lam, debug=True)
     torch.cuda.synchronize()
-    # page table and free list: closed form, exact
-    t_ref = case.page_table.copy()
-    f_ref = list(case.free_list)
-    for s, (n, b) in enumerate(zip(case.seq_len, case.budget)):
-        if n > b:
-            for p in range(int(b) // ps, -(-int(n) // ps)):
-                f_ref.append(int(t_ref[s, p]))
-                t_ref[s, p] = -1
-    assert res.free_count == cap
-    assert np.array_equal(table.cpu().numpy(), t_ref)
-    assert np.array_equal(fl.cpu().numpy(), np.asarray(f_ref, dtype=np.int32))
-    # every live slot of every (seq, head) is a bit-exact copy of its kept row
+    # page table and free list: exactly the oracle's page return, and its
+    # invariants (pool conserved, order, counts) checked on the device result
+    t_ref, f_ref = orc.return_pages(case.page_table, case.seq_len, case.budget, case.free_list, ps)
+    t_gpu, f_gpu = table.cpu().numpy(), fl.cpu().numpy()
+    assert res.free_count == cap == len(f_ref)
+    assert np.array_equal(t_gpu, t_ref)
+    assert np.array_equal(f_gpu, f_ref.astype(np.int32))
+    pins.check_page_return(case.page_table, case.free_list, t_gpu, f_gpu, case.seq_len,
+                           case.budget, ps, int(case.meta["pool"]))
     kept_all = res.kept_idx
+    # every compressed (seq, head): the selection is the unique one for the
+    # device's own scores
     off, zoff = _kept_offsets(case.seq_len, case.budget, H)
+    kh, zh = kept_all.cpu().numpy(), res.Z.cpu().numpy().astype(np.float64)
+    bad = []
+    for s, (n, b) in enumerate(zip(case.seq_len, case.budget)):
+        n, b = int(n), int(b)
+        if n <= b:
+            continue
+        for h in range(H):
+            k = kh[off[s] + h * b: off[s] + (h + 1) * b]
+            z = zh[zoff[s] + h * n: zoff[s] + (h + 1) * n]
+            if not np.array_equal(k, orc.select(z, n, b, case.window)):
+                bad.append((s, h))
+    assert not bad, f"{len(bad)} units select differently from their scores: {bad[:5]}"
+    # every live slot of every (seq, head) is a bit-exact copy of its kept row
     ptab = torch.from_numpy(case.page_table.astype(np.int64)).cuda()
     live = torch.zeros(case.K_pages.shape[:3], dtype=torch.bool, device="cuda")
     for s, (n, b) in enumerate(zip(case.seq_len, case.budget)):

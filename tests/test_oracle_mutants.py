@@ -17,6 +17,47 @@ _orig_probs = orc.attention_probs
 _orig_red = orc.redundancy
 _orig_imp = orc.importance
 _orig_select = orc.select
+_orig_rows = orc.redundancy_rows
+
+
+def _pages_variant(page_table, seq_len, budget, free_list, page_size, mode):
+    """Page return with one mistake."""
+    table = np.array(page_table, copy=True)
+    freed = [int(x) for x in free_list]
+    todo = []
+    for s in range(table.shape[0]):
+        n, b = int(seq_len[s]), int(budget[s])
+        if n <= b:
+            continue
+        first = b // page_size + (1 if mode == "first_page_late" else 0)
+        end = n // page_size if mode == "floor_of_length" else (n + page_size - 1) // page_size
+        ps_ = list(range(first, end))
+        if mode == "descending":
+            ps_ = ps_[::-1]
+        todo += [(s, p) for p in ps_]
+    if mode == "page_major":
+        todo.sort(key=lambda sp: (sp[1], sp[0]))
+    for s, p in todo:
+        freed.append(int(table[s, p]))
+        if mode == "freed_per_head":        # one append for each of two heads
+            freed.append(int(table[s, p]))
+        if mode != "entries_kept":
+            table[s, p] = -1
+    return table, np.asarray(freed, dtype=np.int64)
+
+
+def _rows_variant(K, rows, symmetric=False, mode="self"):
+    R = _orig_red(K, symmetric=symmetric)
+    if mode == "shifted":
+        return R[np.maximum(np.asarray(rows, dtype=np.int64) - 1, 0)]
+    K = np.asarray(K, dtype=np.float64)
+    nrm = np.sqrt((K * K).sum(1))
+    out = []
+    for i in rows:
+        i = int(i)
+        c = K[:i + 1] @ K[i] / (nrm[:i + 1] * nrm[i])
+        out.append(c.max())
+    return np.array(out)
 
 
 def _probs_variant(K, Q, window, mask_shift=0, scale_pow=0.5, causal=True, swap_r=False):
@@ -124,6 +165,18 @@ MUTANTS = {
     "shared_first_head": ("compress_shared", lambda *a, **kw: _shared_variant(*a, mode="first_head", **kw)),
     "shared_max_over_heads": ("compress_shared", lambda *a, **kw: _shared_variant(*a, mode="max_over_heads", **kw)),
     "shared_min_over_heads": ("compress_shared", lambda *a, **kw: _shared_variant(*a, mode="min_over_heads", **kw)),
+    # paged page return
+    "pages_first_page_late": ("return_pages", lambda *a: _pages_variant(*a, mode="first_page_late")),
+    "pages_floor_of_length": ("return_pages", lambda *a: _pages_variant(*a, mode="floor_of_length")),
+    "pages_descending": ("return_pages", lambda *a: _pages_variant(*a, mode="descending")),
+    "pages_page_major_order": ("return_pages", lambda *a: _pages_variant(*a, mode="page_major")),
+    "pages_freed_per_head": ("return_pages", lambda *a: _pages_variant(*a, mode="freed_per_head")),
+    "pages_entries_kept": ("return_pages", lambda *a: _pages_variant(*a, mode="entries_kept")),
+    # redundancy of listed rows
+    "rows_include_self": ("redundancy_rows", lambda K, rows, symmetric=False:
+                          _rows_variant(K, rows, symmetric, "self")),
+    "rows_shifted": ("redundancy_rows", lambda K, rows, symmetric=False:
+                     _rows_variant(K, rows, symmetric, "shifted")),
 }
 
 

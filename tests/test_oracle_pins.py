@@ -49,6 +49,11 @@ def test_paged_closed_form(seed):
     pins.check_paged(seed)
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_redundancy_rows(seed):
+    pins.check_redundancy_rows(seed)
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_bruteforce_variants(seed):
     pins.check_bruteforce_variants(seed)
