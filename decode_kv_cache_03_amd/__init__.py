@@ -171,6 +171,45 @@ def compress(K, V, Q_win, kv_budget: int, window_size: int = 8, mix_lambda: floa
     return CompressResult(kept_idx, K_out, V_out, *dbg)
 
 
+def compress_static(K, V, Q_win, kv_budget: int, window_size: int = 8, mix_lambda: float = 0.1,
+                    *, K_out, V_out, kept_idx, I=None, R=None, Z=None, stream=None,
+                    symmetric: bool = False, causal: bool = True, pool: str = "max",
+                    select_group: int = 1) -> CompressResult:
+    """:func:`compress` through rkv_compress_static: no workspace and no
+    allocation, neither here nor in the library, so every output (and any
+    debug score buffer, float32 [Bh, N]) is the caller's. The call must need
+    at most the library's static scratch (64 MiB per GPU); calls on one GPU
+    must not overlap."""
+    import torch
+    _require_cuda(K, V, Q_win, K_out, V_out, kept_idx, I, R, Z)
+    if K.dim() != 3 or V.shape != K.shape or K.shape[2] != HEAD_DIM:
+        raise ValueError(f"K and V must be [Bh, N, {HEAD_DIM}] with equal shapes")
+    if K.stride(2) != 1 or K.stride(1) != HEAD_DIM or V.stride() != K.stride():
+        raise ValueError("K and V rows must be contiguous with equal strides")
+    if Q_win.dim() != 4 or Q_win.shape[0] != K.shape[0] or Q_win.shape[2] != window_size \
+            or Q_win.shape[3] != HEAD_DIM or not Q_win.is_contiguous():
+        raise ValueError("Q_win must be a contiguous [Bh, G, window_size, 128] tensor")
+    if not (K.dtype == V.dtype == Q_win.dtype):
+        raise TypeError("K, V and Q_win must share a dtype")
+    bh, n, b = int(K.shape[0]), int(K.shape[1]), int(kv_budget)
+    _check_rows_out("K_out", K_out, K.dtype, bh, min(n, b))
+    _check_rows_out("V_out", V_out, K.dtype, bh, min(n, b))
+    if K_out.stride() != V_out.stride() or K_out.stride(2) != 1 or K_out.stride(1) != HEAD_DIM:
+        raise ValueError("K_out and V_out rows must be contiguous with equal strides")
+    _check_index_out("kept_idx", kept_idx, bh * b, shape=(bh, b))
+    for name, t in (("I", I), ("R", R), ("Z", Z)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (bh, n)
+                              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 [{bh}, {n}] tensor")
+    d = dense_desc(bh, n, int(Q_win.shape[1]), window_size, b, mix_lambda, _dtype_code(K),
+                   K.stride(0) if bh > 1 else 0, K_out.stride(0) if bh > 1 else 0,
+                   variant_bits(symmetric, causal, pool), int(select_group))
+    _lib.check(_lib.load().rkv_compress_static(ctypes.byref(d), _ptr(K), _ptr(V), _ptr(Q_win),
+                                               _ptr(kept_idx), _ptr(K_out), _ptr(V_out), _ptr(I),
+                                               _ptr(R), _ptr(Z), _stream_ptr(stream)))
+    return CompressResult(kept_idx, K_out, V_out, I, R, Z)
+
+
 def paged_desc(num_seqs, kv_heads, gqa, window, page_size, max_pages, num_pages, lam, dtype_code,
                page_stride=0, head_stride=0, slot_stride=0, variant=0):
     return _lib.PagedDesc(num_seqs, kv_heads, HEAD_DIM, gqa, window, page_size, max_pages, num_pages,

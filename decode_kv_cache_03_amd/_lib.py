@@ -23,8 +23,10 @@ STATUS_NAMES = {RKV_OK: "RKV_OK", RKV_EINVAL: "RKV_EINVAL", RKV_EWORKSPACE: "RKV
                 RKV_EFREELIST: "RKV_EFREELIST", RKV_EUNSUPPORTED: "RKV_EUNSUPPORTED",
                 RKV_EHIP: "RKV_EHIP"}
 
-EXPORTS = ["rkv_workspace_size", "rkv_compress", "rkv_paged_workspace_size", "rkv_compress_paged",
-           "rkv_paged_plan", "rkv_last_error", "rkv_timing_enable", "rkv_timing_read"]
+EXPORTS = ["rkv_workspace_size", "rkv_compress", "rkv_compress_static", "rkv_paged_workspace_size",
+           "rkv_compress_paged", "rkv_paged_plan", "rkv_last_error", "rkv_timing_enable",
+           "rkv_timing_read"]
+STATIC_SCRATCH_BYTES = 64 << 20      # RKV_STATIC_SCRATCH_BYTES
 
 
 class DenseDesc(ctypes.Structure):
@@ -77,6 +79,9 @@ def load():
     lib.rkv_compress.argtypes = [ctypes.POINTER(DenseDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                  sz, vp]
     lib.rkv_compress.restype = ctypes.c_int
+    lib.rkv_compress_static.argtypes = [ctypes.POINTER(DenseDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        vp]
+    lib.rkv_compress_static.restype = ctypes.c_int
     lib.rkv_paged_workspace_size.argtypes = [ctypes.POINTER(PagedDesc), pi32, pi32]
     lib.rkv_paged_workspace_size.restype = sz
     lib.rkv_compress_paged.argtypes = [ctypes.POINTER(PagedDesc), vp, vp, vp, pi32, pi32, vp, vp, vp,

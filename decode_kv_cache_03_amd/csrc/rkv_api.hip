@@ -303,21 +303,13 @@ extern "C" size_t rkv_workspace_size(const rkv_dense_desc* desc) {
   return dense_layout(desc, nullptr).bytes;
 }
 
-extern "C" int rkv_compress(const rkv_dense_desc* desc, const void* K, const void* V,
-                            const void* Q_win, int32_t* kept_idx, void* K_out, void* V_out,
-                            float* dbg_I, float* dbg_R, float* dbg_Z, void* workspace,
-                            size_t workspace_bytes, void* stream) {
-  int rc = check_dense_desc(desc);
-  if (rc) return rc;
-  const size_t need = dense_layout(desc, nullptr).bytes;
-  if (desc->num_heads == 0) return RKV_OK;
+namespace {
+
+// Checks of a dense call's buffers (the descriptor is valid and num_heads > 0).
+int check_dense_buffers(const rkv_dense_desc* desc, const void* K, const void* V, const void* Q_win,
+                        const int32_t* kept_idx, const void* K_out, const void* V_out) {
   if (!K || !V || !Q_win || !kept_idx || !K_out || !V_out)
     return fail(RKV_EINVAL, "K, V, Q_win, kept_idx, K_out and V_out must be non-NULL");
-  if (!workspace || workspace_bytes < need)
-    return fail(RKV_EWORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need, workspace_bytes,
-                workspace ? "" : ", NULL");
-  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
-    return fail(RKV_EWORKSPACE, "workspace must be 256-byte aligned");
   const size_t es = desc->dtype == RKV_BF16 ? 2 : 4;
   const int64_t in_stride = desc->kv_head_stride ? desc->kv_head_stride : (int64_t)desc->n_cand * 128;
   const int64_t out_stride = desc->out_head_stride ? desc->out_head_stride : (int64_t)desc->budget * 128;
@@ -328,7 +320,87 @@ extern "C" int rkv_compress(const rkv_dense_desc* desc, const void* K, const voi
       ranges_overlap(V_out, out_bytes, K, in_bytes) || ranges_overlap(V_out, out_bytes, V, in_bytes) ||
       ranges_overlap(K_out, out_bytes, V_out, out_bytes))
     return fail(RKV_EINVAL, "K_out and V_out must not overlap each other, K or V");
+  return RKV_OK;
+}
+
+}  // namespace
+
+extern "C" int rkv_compress(const rkv_dense_desc* desc, const void* K, const void* V,
+                            const void* Q_win, int32_t* kept_idx, void* K_out, void* V_out,
+                            float* dbg_I, float* dbg_R, float* dbg_Z, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  int rc = check_dense_desc(desc);
+  if (rc) return rc;
+  const size_t need = dense_layout(desc, nullptr).bytes;
+  if (desc->num_heads == 0) return RKV_OK;
+  rc = check_dense_buffers(desc, K, V, Q_win, kept_idx, K_out, V_out);
+  if (rc) return rc;
+  if (!workspace || workspace_bytes < need)
+    return fail(RKV_EWORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(RKV_EWORKSPACE, "workspace must be 256-byte aligned");
   const DenseLayout L = dense_layout(desc, static_cast<char*>(workspace));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  g_error.clear();
+  if (desc->dtype == RKV_BF16)
+    return dense_run<bf16_bits>(desc, K, V, Q_win, kept_idx, K_out, V_out, dbg_I, dbg_R, dbg_Z, L, st);
+  return dense_run<float>(desc, K, V, Q_win, kept_idx, K_out, V_out, dbg_I, dbg_R, dbg_Z, L, st);
+}
+
+// ---- dense compression without allocation ---------------------------------------
+// The workspace of rkv_compress_static: a device array of fixed size that
+// every GPU the library runs on holds from load to process exit. In host
+// code `scratch` names a host-side stand-in, never the device memory: the
+// device address comes from hipGetSymbolAddress, once per device with that
+// device current, and only that address is handed to kernels.
+static __device__ __align__(256) char scratch[RKV_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int device_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(RKV_EUNSUPPORTED, "device %d: at most %d devices are served", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || reinterpret_cast<uintptr_t>(p) % kAlign)
+      return fail(RKV_EHIP, "device scratch of device %d is not 256-byte aligned", dev);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RKV_OK;
+}
+
+}  // namespace
+
+extern "C" int rkv_compress_static(const rkv_dense_desc* desc, const void* K, const void* V,
+                                   const void* Q_win, int32_t* kept_idx, void* K_out, void* V_out,
+                                   float* dbg_I, float* dbg_R, float* dbg_Z, void* stream) {
+  int rc = check_dense_desc(desc);
+  if (rc) return rc;
+  const size_t need = dense_layout(desc, nullptr).bytes;
+  if (desc->num_heads == 0) return RKV_OK;
+  rc = check_dense_buffers(desc, K, V, Q_win, kept_idx, K_out, V_out);
+  if (rc) return rc;
+  if (need > RKV_STATIC_SCRATCH_BYTES)
+    return fail(RKV_EWORKSPACE,
+                "this call needs %zu bytes of workspace, above the %zu of the static scratch: "
+                "split the units over several calls or use rkv_compress",
+                need, (size_t)RKV_STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  rc = device_scratch(&ws);
+  if (rc) return rc;
+  const DenseLayout L = dense_layout(desc, static_cast<char*>(ws));
   hipStream_t st = static_cast<hipStream_t>(stream);
   g_error.clear();
   if (desc->dtype == RKV_BF16)

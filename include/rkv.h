@@ -140,6 +140,24 @@ int rkv_compress(const rkv_dense_desc* desc, const void* K, const void* V, const
                  int32_t* kept_idx, void* K_out, void* V_out, float* dbg_I, float* dbg_R,
                  float* dbg_Z, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the device scratch behind rkv_compress_static (per GPU). */
+#define RKV_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* rkv_compress without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). Same arguments,
+ * outputs and errors as rkv_compress, minus workspace; the workspace is a
+ * library-owned device array of RKV_STATIC_SCRATCH_BYTES that each GPU holds
+ * from library load until the process ends. A call whose
+ * rkv_workspace_size(desc) exceeds that returns RKV_EWORKSPACE (nothing
+ * done). The library makes no hipMalloc/hipFree or other allocating call
+ * here. Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (each call initialises what it reads): calls that overlap on one GPU
+ * (different streams or host threads without ordering) race, so order them. */
+int rkv_compress_static(const rkv_dense_desc* desc, const void* K, const void* V,
+                        const void* Q_win, int32_t* kept_idx, void* K_out, void* V_out,
+                        float* dbg_I, float* dbg_R, float* dbg_Z, void* stream);
+
 /* Paged layout: a pool of num_pages pages; token t of (sequence s, KV head
  * hk) is the 128-element row at
  *   pages + page_table[s][t / page_size] * page_stride + hk * head_stride

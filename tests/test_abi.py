@@ -223,3 +223,21 @@ def test_python_binding_refuses_cpu_tensors(lib):
     K = torch.zeros((1, 100, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         rkv.compress(K, K, torch.zeros((1, 4, 8, 128), dtype=torch.bfloat16), 64)
+
+
+def test_static_entry_point_rejects_before_any_gpu_call(lib):
+    """rkv_compress_static validates like rkv_compress and refuses a call whose
+    workspace would not fit its static scratch, all before touching a GPU."""
+    far = [ctypes.c_void_p(k << 44) for k in range(1, 5)]   # disjoint even for 33 GB inputs
+
+    def call(d, K=far[0]):
+        return lib.rkv_compress_static(ctypes.byref(d), K, far[1], FAKE, FAKE, far[2], far[3],
+                                       None, None, None, None)
+    assert call(dense(head_dim=64)) == _lib.RKV_EINVAL
+    assert call(dense(budget=8)) == _lib.RKV_EINVAL
+    assert call(dense(), K=None) == _lib.RKV_EINVAL
+    assert call(dense(num_heads=0)) == _lib.RKV_OK
+    big = dense(num_heads=16384, n_cand=8000, budget=6000)
+    assert lib.rkv_workspace_size(ctypes.byref(big)) > _lib.STATIC_SCRATCH_BYTES
+    assert call(big) == _lib.RKV_EWORKSPACE
+    assert b"static scratch" in lib.rkv_last_error()
