@@ -48,7 +48,7 @@ WORKLOADS = {
 
 # launch labels of the kernels that run the whole dense step in one launch
 # (register-resident keys for short units, the LDS tile ring otherwise)
-WHOLE_STEP = ("rkv_k2_resident", "rkv_k2_compress")
+WHOLE_STEP = ("rkv_k2_resident", "rkv_k2_resident2", "rkv_k2_compress")
 
 
 def whole_step_label(times):
@@ -122,7 +122,10 @@ def source_hash(files):
 
 _HEADERS = ["rkv_device.hpp", "rkv_problem.hpp", "rkv_launch.hpp"]
 KERNEL_SOURCES = {
-    "rkv_k2_resident": ["k2_resident.hip", "rkv_frag16.hpp", "rkv_select.hpp", "rkv_stream.hpp"] + _HEADERS,
+    "rkv_k2_resident": ["k2_resident.hip", "rkv_resident.hpp", "rkv_frag16.hpp", "rkv_select.hpp",
+                        "rkv_stream.hpp"] + _HEADERS,
+    "rkv_k2_resident2": ["k2_resident2.hip", "rkv_resident.hpp", "rkv_frag16.hpp", "rkv_select.hpp",
+                         "rkv_stream.hpp"] + _HEADERS,
     "rkv_k2_compress": ["k2_wide.hip", "k2_redundancy.hip", "rkv_select.hpp", "rkv_stream.hpp"] + _HEADERS,
     "rkv_k2_redundancy": ["k2_redundancy.hip", "rkv_select.hpp"] + _HEADERS,
     "rkv_k2_long": ["k2_long.hip", "rkv_frag16.hpp", "rkv_stream.hpp"] + _HEADERS,

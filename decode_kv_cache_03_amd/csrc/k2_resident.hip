@@ -44,192 +44,15 @@
 // Under head-shared selection the kernel stops after writing Z.
 #include <type_traits>
 
-#include "rkv_problem.hpp"
 #include "rkv_launch.hpp"
+#include "rkv_resident.hpp"
 #include "rkv_select.hpp"
-#include "rkv_stream.hpp"
-#include "rkv_frag16.hpp"
 
 namespace rkv {
 namespace resident {
 
 using namespace frag16;
 using stream::vm_imm;
-
-constexpr int kThreads = 512;
-constexpr int kRowBytes = 256;                  // bf16 row of 128
-constexpr int kTileBytes = 128 * kRowBytes;
-// Cache policy of the K'/V' stores: the default (write-back through L2)
-// measured faster here than streaming stores.
-constexpr int kOutPolicy = 0;
-
-// Wait until at most n vector-memory instructions of this wave are in
-// flight (n rounded down to a multiple of 4: never a shorter wait).
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n <= 0 ? 0 : (n >= 60 ? 15 : n >> 2)) {
-    case 0: __builtin_amdgcn_s_waitcnt(vm_imm(0)); break;
-    case 1: __builtin_amdgcn_s_waitcnt(vm_imm(4)); break;
-    case 2: __builtin_amdgcn_s_waitcnt(vm_imm(8)); break;
-    case 3: __builtin_amdgcn_s_waitcnt(vm_imm(12)); break;
-    case 4: __builtin_amdgcn_s_waitcnt(vm_imm(16)); break;
-    case 5: __builtin_amdgcn_s_waitcnt(vm_imm(20)); break;
-    case 6: __builtin_amdgcn_s_waitcnt(vm_imm(24)); break;
-    case 7: __builtin_amdgcn_s_waitcnt(vm_imm(28)); break;
-    case 8: __builtin_amdgcn_s_waitcnt(vm_imm(32)); break;
-    case 9: __builtin_amdgcn_s_waitcnt(vm_imm(36)); break;
-    case 10: __builtin_amdgcn_s_waitcnt(vm_imm(40)); break;
-    case 11: __builtin_amdgcn_s_waitcnt(vm_imm(44)); break;
-    case 12: __builtin_amdgcn_s_waitcnt(vm_imm(48)); break;
-    case 13: __builtin_amdgcn_s_waitcnt(vm_imm(52)); break;
-    case 14: __builtin_amdgcn_s_waitcnt(vm_imm(56)); break;
-    default: __builtin_amdgcn_s_waitcnt(vm_imm(60)); break;
-  }
-}
-
-// 1/||k|| of the 16*NK rows of NK fragments, written to rn[key0 + row]
-// (each row's four quarters add their partial sums; rows past N are padding).
-template <int NK>
-__device__ __forceinline__ void row_norms(const u32x4_t (&f)[NK][4], int key0, int lane, float* rn) {
-#pragma unroll
-  for (int rs = 0; rs < NK; ++rs) {
-    float ss = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) ss += sumsq_chunk<bf16_bits>(f[rs][ks]);
-    ss = sum_quarters(ss);
-    const int key = key0 + rs * 16 + (lane & 15);
-    if (lane < 16) rn[key] = ss > 0.f ? __frsqrt_rn(ss) : 0.f;
-  }
-}
-
-// Online softmax statistics of the window queries over 16*NK keys: lane l
-// owns query columns l % 16 and 16 + l % 16 (mrun/srun [qs]).
-template <int NK>
-__device__ __forceinline__ void stats_update(const u32x4_t (&kf)[NK][4], const u32x4_t (&qf)[2][4],
-                                             int key0, int N, int W, int G, int rpg_shift,
-                                             bool causal, int lane, float (&mrun)[2],
-                                             float (&srun)[2]) {
-  asm volatile("" : "+v"(lane));   // per call: keeps lane-derived masks out of loop preheaders
-  const int rpg_mask = (1 << rpg_shift) - 1;
-  f32x4_t acc[NK][2];
-#pragma unroll
-  for (int a = 0; a < NK; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-    for (int ksb = 0; ksb < NK; ++ksb)
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) mma16(acc[ksb][qs], kf[ksb][ks], qf[qs][ks]);   // C[key][query]
-  // the block holds padding or keys that some window query cannot see
-  const bool edge = key0 + 16 * NK > (causal ? N - W : N);
-#pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
-    const int m = qs * 16 + (lane & 15);
-    const int g = m >> rpg_shift, r = m & rpg_mask;
-    const bool qok = g < G && r < W;
-    const int last = causal ? N - W + r : N - 1;   // last key visible to window query r
-    float lg[4 * NK];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int ksb = 0; ksb < NK; ++ksb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int key = key0 + ksb * 16 + 4 * (lane >> 4) + v;
-        float x = acc[ksb][qs][v] * kLogitScaleLog2;
-        if (edge || !qok) x = (qok && key <= last) ? x : -INFINITY;
-        lg[ksb * 4 + v] = x;
-        mt = fmaxf(mt, x);
-      }
-    const float mn = fmaxf(mrun[qs], mt);
-    if (mn != -INFINITY) {
-      float s = (mrun[qs] != -INFINITY) ? srun[qs] * fast_exp2(mrun[qs] - mn) : 0.f;
-#pragma unroll
-      for (int i = 0; i < 4 * NK; ++i) s += fast_exp2(lg[i] - mn);
-      srun[qs] = s;
-      mrun[qs] = mn;
-    }
-  }
-}
-
-// Column maxima of dot(k_i, k_j) * (1/||k_i||) for one 32-row block against
-// 32 columns: rows are the block's fragments `af` with the 1/||k|| of the
-// lane's accumulator rows in `rr`; `bf` are the columns. `diag`: rows and
-// columns are the same 32 keys, and only row < column counts.
-__device__ __forceinline__ void pair_max(const u32x4_t (&af)[2][4], const float* rnrow,
-                                         const u32x4_t (&bf)[2][4], bool diag, int lane,
-                                         float (&cm)[2]) {
-  f32x4_t rr[2];
-  for (int rs = 0; rs < 2; ++rs) rr[rs] = *reinterpret_cast<const f32x4_t*>(rnrow + rs * 16 + 4 * (lane >> 4));
-  f32x4_t acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-    for (int rs = 0; rs < 2; ++rs)
-#pragma unroll
-      for (int cs = 0; cs < 2; ++cs) mma16(acc[rs][cs], af[rs][ks], bf[cs][ks]);   // C[row][col]
-  if (!diag) {
-#pragma unroll
-    for (int cs = 0; cs < 2; ++cs)
-#pragma unroll
-      for (int rs = 0; rs < 2; ++rs)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) cm[cs] = fmaxf(cm[cs], acc[rs][cs][v] * rr[rs][v]);
-  } else {
-    int lane_v = lane;   // re-materialised: keeps the masks out of loop preheaders
-    asm volatile("" : "+v"(lane_v));
-    const int row0 = 4 * (lane_v >> 4), col = lane_v & 15;
-#pragma unroll
-    for (int cs = 0; cs < 2; ++cs)
-#pragma unroll
-      for (int rs = 0; rs < 2; ++rs) {
-        if (rs > cs) continue;   // every row follows every column
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const bool before = rs < cs || row0 + v < col;
-          if (before) cm[cs] = fmaxf(cm[cs], acc[rs][cs][v] * rr[rs][v]);
-        }
-      }
-  }
-}
-
-// As pair_max for 16 columns (column half cs of a 32-key block), with the
-// row norms read from rnrow.
-__device__ __forceinline__ void pair_max16(const u32x4_t (&af)[2][4], const float* rnrow,
-                                           const u32x4_t (&bf)[4], int cs, bool diag, int lane,
-                                           float& cm) {
-  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-    for (int rs = 0; rs < 2; ++rs) mma16(acc[rs], af[rs][ks], bf[ks]);
-  int lane_v = lane;   // re-materialised: keeps the masks out of loop preheaders
-  asm volatile("" : "+v"(lane_v));
-  const int row0 = 4 * (lane_v >> 4), col = lane_v & 15;
-#pragma unroll
-  for (int rs = 0; rs < 2; ++rs) {
-    if (diag && rs > cs) continue;   // every row follows every column
-    const f32x4_t rr = *reinterpret_cast<const f32x4_t*>(rnrow + rs * 16 + row0);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const bool before = !diag || rs < cs || row0 + v < col;
-      if (before) cm = fmaxf(cm, acc[rs][v] * rr[v]);
-    }
-  }
-}
-
-// Max over the four lane quarters: lanes 0..15 end with the column maxima.
-__device__ __forceinline__ void publish_cols(float (&cm)[2], float* dst, int lane) {
-#pragma unroll
-  for (int cs = 0; cs < 2; ++cs) {
-    const float x = max_quarters(cm[cs]);
-    if (lane < 16) dst[cs * 16 + lane] = x;
-  }
-}
 
 template <int kHeld>
 __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(

@@ -242,6 +242,13 @@ int dense_run(const rkv_dense_desc* d, const void* K, const void* V, const void*
                                  out_stride, shared ? 1 : 0, st);
         if (e != hipSuccess) return hip_fail(e, "compression launch");
         scored = true;
+      } else if (rkv::k2_resident2_fits(p, rpg_shift)) {
+        // up to 2048 + 128 candidates: keys held in registers in two passes
+        e = rkv::run_k2_resident2(p, shared ? z : dbg_Z, dbg_R, dbg_I, d->mix_lambda, rpg_shift,
+                                  kept, static_cast<T*>(K_out), static_cast<T*>(V_out), out_stride,
+                                  shared ? 1 : 0, st);
+        if (e != hipSuccess) return hip_fail(e, "compression launch");
+        scored = true;
       } else if (rkv::fused_plan_choose(p.N, p.B, p.G * p.W, nqb).total > 0) {
         e = rkv::run_k2_fused(p, nqb, shared ? z : dbg_Z, dbg_R, dbg_I, d->mix_lambda, rpg_shift,
                               kept, static_cast<T*>(K_out), static_cast<T*>(V_out), out_stride,

@@ -62,6 +62,17 @@ hipError_t run_k2_resident(const DenseProblem<bf16_bits>& p, int nqb, float* dbg
                            bf16_bits* K_out, bf16_bits* V_out, int64_t out_stride, int score_only,
                            hipStream_t st);
 
+// Dense bf16 caches with 1152 < N <= 2176 candidates per unit, at most 48
+// window query rows, the causal-order R and a budget that is a multiple of
+// 32 (k2_resident2_fits): the whole step in one launch that holds each
+// unit's keys in registers in two passes of 1024 rows (k2_resident2.hip).
+// Arguments as run_k2_fused.
+bool k2_resident2_fits(const DenseProblem<bf16_bits>& p, int rpg_shift);
+hipError_t run_k2_resident2(const DenseProblem<bf16_bits>& p, float* dbg_Z, float* dbg_R,
+                            float* dbg_I, float lam, int rpg_shift, int32_t* kept,
+                            bf16_bits* K_out, bf16_bits* V_out, int64_t out_stride, int score_only,
+                            hipStream_t st);
+
 // Long units (bf16): Z (R, I when requested) of every unit, one 512-row
 // block per work item (k2_long.hip); `count` = p.long_count(). Needs the
 // norms `rinv` and normalisers `fin` of run_k1; rows are read from

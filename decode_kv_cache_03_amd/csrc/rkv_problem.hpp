@@ -120,6 +120,38 @@ __host__ __device__ inline ResidentPlan resident_plan(int N, int B, int gw) {
   return L;
 }
 
+// LDS plan of the two-pass register-resident kernel (k2_resident2.hip): as
+// ResidentPlan with nq = 16 * (query groups) window rows, plus one word for
+// the count of a unit's kept rows held in the first pass.
+struct Resident2Plan {
+  int slots, vstage, q, qbytes, stats, sred, rn, zs, ks, part, dpart, sel, nlow, total;
+};
+
+// Rows held in registers per pass, and tiles per pass.
+constexpr int kResident2PassRows = 1024;
+constexpr int kResident2PassTiles = 8;
+
+__host__ __device__ inline Resident2Plan resident2_plan(int N, int B, int gw, int nq) {
+  Resident2Plan L;
+  const int nb = (N + 127) / 128;
+  L.slots = 2;
+  L.vstage = L.slots * 128 * 256;
+  L.q = L.vstage + 32 * 1024;
+  L.qbytes = (gw * 256 + 1023) / 1024 * 1024;
+  L.stats = L.q + 2 * L.qbytes;
+  L.sred = L.stats + nq * 8;
+  L.rn = L.sred + 2 * 8 * nq * 4;
+  L.zs = L.rn + nb * 128 * 4;
+  L.ks = L.zs + nb * 128 * 4;
+  L.part = L.ks + round16((int64_t)B * 4);
+  L.dpart = L.part + 2 * 8 * 128 * 4;
+  L.sel = L.dpart + 4 * 128 * 4;
+  L.nlow = L.sel + round16(sizeof(SelectScratch));
+  L.total = L.nlow + 16;
+  if (L.total > kLdsBytesPerCU) L.total = 0;
+  return L;
+}
+
 // Reading variants of a call (bits as in rkv.h): the defaults are R over
 // earlier candidates, the causal window and max pooling over the GQA heads.
 constexpr uint32_t kVariantSymmetric = 1u;   // R_i over every j != i

@@ -81,6 +81,14 @@ SHAPES = [
     (5000, 4000, 8, 4, 0.1, "bf16", 1),    # fused kernel with a 2-slot tile ring
     (8000, 6000, 8, 4, 0.1, "bf16", 1),    # unit too long for one workgroup: long-unit kernel
     (7777, 6000, 8, 4, 0.1, "bf16", 2),    # long-unit kernel, ragged last tile and block
+    # two-pass register-resident kernel (1152 < N <= 2176, B a multiple of 32)
+    (2176, 2048, 8, 5, 0.1, "bf16", 3),    # the Qwen-14B event shape: 3 query groups
+    (1800, 1280, 8, 4, 0.1, "bf16", 2),    # 6 tiles held in the second pass, last tile of 8 rows
+    (1200, 640, 8, 4, 0.3, "bf16", 2),     # 1 tile held in the second pass
+    (1500, 1024, 8, 6, 0.1, "bf16", 2),    # 48 window rows (6 heads of 8)
+    (2000, 1504, 12, 3, 0.5, "bf16", 2),   # 16 rows per head, 3 groups
+    (2100, 1536, 8, 2, 0.0, "bf16", 2),    # 2 query groups, redundancy only
+    (2176, 2048, 8, 5, 1.0, "bf16", 2),    # importance only
 ]
 
 

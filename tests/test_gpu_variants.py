@@ -30,6 +30,7 @@ SHAPES = [
     (70, 40, 8, 4, 0.1, "bf16", 2),        # one partial tile
     (300, 200, 8, 2, 0.1, "f32", 2),       # team path (fp32)
     (8000, 6000, 8, 4, 0.1, "bf16", 1),    # team path (unit too long for the fused kernel)
+    (2176, 2048, 8, 5, 0.1, "bf16", 2),    # two-pass resident kernel (symmetric: fused kernel)
 ]
 
 
@@ -162,6 +163,7 @@ SHARED = [
     (700, 512, 8, 5, "bf16", 16, 4),       # several groups, ragged tile
     (300, 200, 8, 2, "f32", 4, 2),         # team path
     (8000, 6000, 8, 4, "bf16", 2, 2),      # team path, long units
+    (2176, 2048, 8, 5, "bf16", 4, 2),      # two-pass resident kernel, scores only
 ]
 
 
