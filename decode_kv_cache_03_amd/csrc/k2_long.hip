@@ -15,9 +15,11 @@
 // Why a separate kernel: a unit of N keys needs N^2/2 cosine pairs but only
 // N rows of keys, so for long units the contraction is MFMA-bound as long as
 // each key tile fetched from memory feeds enough rows. The item kernels of
-// k2_redundancy.hip feed 128 rows per 32 KiB tile; here a block holds 512
-// rows (wave w: rows 64w..64w+63, both 64-column halves of every tile), so a
-// tile carries 512 flop per byte fetched.
+// k2_redundancy.hip feed 128 rows per 32 KiB tile; here an item holds 1024
+// rows in the 16x16 form (longr: wave w holds row blocks of 32 with block
+// index = w mod 8) or 512 rows in the 32x32 form (longu: wave w rows
+// 64w..64w+63, both 64-column halves of every tile), so a tile carries 1024
+// or 512 flop per byte fetched.
 //
 // Shape:
 //  * tiles (128 rows, 32 KiB, XOR-swizzled chunks) stream through a ring of

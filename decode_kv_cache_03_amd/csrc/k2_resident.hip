@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
   float* const part = reinterpret_cast<float*>(lds + L.part);        // [2][8][128]
   float* const dpart = reinterpret_cast<float*>(lds + L.dpart);      // [4][128]
   char* const vstage = lds + L.vstage;                               // [8 waves][4][1 KiB]
-  SelectScratch& ssh = *reinterpret_cast<SelectScratch*>(lds + L.sel);
+  SelectLeanScratch& ssh = *reinterpret_cast<SelectLeanScratch*>(lds + L.sel);
 
 
   // Vector-memory instructions this wave has issued (vm), and the count just
@@ -456,17 +456,12 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
     // (score_only: Z went to Zdbg; a later launch selects for groups of units)
     if (!score_only) {
       __syncthreads();
+      // the kept list and every candidate's output row (-1: dropped), in the
+      // norms' place
+      select_block_lean<kThreads>(zs, N, B, W, ks, pos, ssh);
+      __syncthreads();
       int32_t* kept = kept_all + p.kept_off(u);
-      select_block<kThreads>(zs, N, B, W, kept, ssh, ks);
-      __syncthreads();
-      // output row of every candidate (-1: dropped), in the norms' place
-      for (int i = tid_u; i < N; i += kThreads) pos[i] = -1;
-      __syncthreads();
-      for (int r = tid_u; r < B; r += kThreads) {
-        const int kr = ks[r];
-        if ((unsigned)kr < (unsigned)N) pos[kr] = r;
-      }
-      __syncthreads();
+      for (int r = tid_u; r < B; r += kThreads) kept[r] = ks[r];
       // kept K rows held in registers: lane quarter q writes chunks q + 4*ks,
       // so the four quarters of a row fill 64 contiguous bytes per store;
       // rows that are dropped store past the end of the buffer

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r2_kernel(
   float* const dpart = reinterpret_cast<float*>(lds + L.dpart);      // [4][128]
   char* const vstage = lds + L.vstage;                               // [8 waves][4][1 KiB]
   int32_t* const nlow_lds = reinterpret_cast<int32_t*>(lds + L.nlow); // kept rows < 1024
-  SelectScratch& ssh = *reinterpret_cast<SelectScratch*>(lds + L.sel);
+  SelectLeanScratch& ssh = *reinterpret_cast<SelectLeanScratch*>(lds + L.sel);
 
   // Vector-memory instructions this wave has issued (vm), and the count just
   // after each ring slot's tile (as in k2_resident.hip): every counted
@@ -457,19 +457,18 @@ __global__ __launch_bounds__(kThreads, 1) void k2r2_kernel(
     // ---------------- selection and gather ----------------
     if (!score_only) {
       __syncthreads();
+      // the kept list and every candidate's output row (-1: dropped), in the
+      // norms' place
+      select_block_lean<kThreads>(zs, N, B, W, ks, pos, ssh);
+      __syncthreads();
       int32_t* kept = kept_all + p.kept_off(u);
-      select_block<kThreads>(zs, N, B, W, kept, ssh, ks);
-      __syncthreads();
-      for (int i = tid_u; i < N; i += kThreads) pos[i] = -1;
-      __syncthreads();
       for (int r = tid_u; r < B; r += kThreads) {
         const int kr = ks[r];
-        if ((unsigned)kr < (unsigned)N) pos[kr] = r;
-        // kept rows below 1024 (ascending): their count, written once
+        kept[r] = kr;
+        // the count of kept rows below 1024 (ascending; the window is above)
         if (kr < kPR && (r + 1 == B || ks[r + 1] >= kPR)) *nlow_lds = r + 1;
       }
       if (tid_u == 0 && ks[0] >= kPR) *nlow_lds = 0;
-      __syncthreads();
       // kept K rows of pass 1 from registers (dropped rows store past the end)
       const __amdgpu_buffer_rsrc_t ko = __builtin_amdgcn_make_buffer_rsrc(
           K_out + (int64_t)u * out_stride, 0, B * kRowBytes, kBufferWord3);

@@ -115,7 +115,7 @@ __host__ __device__ inline ResidentPlan resident_plan(int N, int B, int gw) {
   L.part = L.ks + round16((int64_t)B * 4);
   L.dpart = L.part + 2 * 8 * 128 * 4;
   L.sel = L.dpart + 4 * 128 * 4;
-  L.total = L.sel + round16(sizeof(SelectScratch));
+  L.total = L.sel + round16(sizeof(SelectLeanScratch));
   if (L.total > kLdsBytesPerCU) L.total = 0;
   return L;
 }
@@ -146,7 +146,7 @@ __host__ __device__ inline Resident2Plan resident2_plan(int N, int B, int gw, in
   L.part = L.ks + round16((int64_t)B * 4);
   L.dpart = L.part + 2 * 8 * 128 * 4;
   L.sel = L.dpart + 4 * 128 * 4;
-  L.nlow = L.sel + round16(sizeof(SelectScratch));
+  L.nlow = L.sel + round16(sizeof(SelectLeanScratch));
   L.total = L.nlow + 16;
   if (L.total > kLdsBytesPerCU) L.total = 0;
   return L;

@@ -85,7 +85,9 @@ __device__ __forceinline__ void select_block(const float* __restrict__ z, int N,
   }
   uint32_t tot;
   const uint32_t eq_before = block_inclusive_scan<NT>(eq, sh.scan, &tot) - eq;
-  const uint32_t take = (take_eq > eq_before) ? min(eq, take_eq - eq_before) : 0u;
+  // this thread's share of the equal keys taken (see select_block_lean on
+  // why there is no conditional subtraction)
+  const uint32_t take = min(eq, take_eq - min(eq_before, take_eq));
   const uint32_t cnt = gt + take;
   uint32_t pos = block_inclusive_scan<NT>(cnt, sh.scan, &tot) - cnt;
   uint32_t taken = 0;
@@ -105,6 +107,148 @@ __device__ __forceinline__ void select_block(const float* __restrict__ z, int N,
   for (int r = tid; r < W; r += NT) {
     kept[k + r] = cand + r;
     if (kept_copy != nullptr) kept_copy[k + r] = cand + r;
+  }
+}
+
+// Inclusive sum over the lanes 0..lane of one wave.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Shared scratch of select_block_lean: three rotating histograms and the
+// per-wave totals of the ordered pass's scan.
+struct SelectLeanScratch {
+  uint32_t hist[3][256];
+  uint32_t wsum[16];
+};
+
+// The selection of select_block (same keys, same threshold and tie rule,
+// same output) with one workgroup barrier per digit pass instead of six,
+// for units whose candidates fit 16-bit counts (N - W < 65536):
+//  * pass p adds its keys into histogram p % 3 (the lanes of a wave that
+//    share the first active lane's digit add with one atomic) and clears
+//    histogram (p + 1) % 3 for the next pass, which no wave has read since
+//    pass p - 2, before the barrier p; after it, EVERY wave reads the 256
+//    counts (lane l: digits 255-4l .. 252-4l), scans them over its lanes and
+//    finds the same digit and count above it, so nothing is broadcast;
+//  * the ordered pass gives thread t the candidates [t*per, t*per + per):
+//    one block scan of (keys above T) << 16 | (keys equal to T) yields both
+//    the thread's output position (above-T keys before it, plus the equal
+//    keys taken before it: the first take_eq in index order) and how many
+//    of its own equal keys it takes.
+// Writes ks[0..B) and pos[i] (output row of candidate i, or -1) for every
+// i < N, both in LDS; every index written is bounded ([0, B), [0, N)). The
+// caller's barrier after the call publishes them. All NT threads call it
+// with the same arguments; sh.hist[0] and [1] are cleared here (one barrier).
+// Requires N > B > W.
+template <int NT>
+__device__ __forceinline__ void select_block_lean(const float* __restrict__ z, int N, int B, int W,
+                                                  int32_t* __restrict__ ks, int32_t* __restrict__ pos,
+                                                  SelectLeanScratch& sh) {
+  static_assert(NT >= 256 && NT % 64 == 0 && NT / 64 <= 16, "256..1024 threads");
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));   // keeps thread-derived values from being hoisted into callers' loops
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wave0 = tid - lane;
+  const int cand = N - W;
+  const int k = B - W;
+  if (tid < 256) {
+    sh.hist[0][tid] = 0u;
+    sh.hist[1][tid] = 0u;
+  }
+  lds_barrier();
+  uint32_t prefix = 0, mask = 0, remaining = (uint32_t)k;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    uint32_t* const hc = sh.hist[pass % 3];
+    for (int i0 = wave0; i0 < cand; i0 += NT) {   // bounds uniform across the wave
+      const int i = i0 + lane;
+      const uint32_t key = i < cand ? order_key(z[i]) : 0u;
+      const bool in = i < cand && (key & mask) == prefix;
+      const uint32_t dig = (key >> shift) & 255u;
+      const uint64_t act = __ballot(in);
+      if (act != 0) {
+        const int lead = __builtin_amdgcn_readfirstlane(__ffsll((long long)act) - 1);
+        const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)dig, lead) & 255u;
+        const uint64_t same = __ballot(in && dig == d0);
+        if (lane == lead) atomicAdd(&hc[d0], (uint32_t)__popcll(same));
+        if (in && dig != d0) atomicAdd(&hc[dig], 1u);
+      }
+    }
+    if (pass >= 1 && pass < 3 && tid < 256) sh.hist[(pass + 1) % 3][tid] = 0u;
+    lds_barrier();
+    // every wave: the count of keys at or above each digit, from the top
+    const u32x4_t h = *reinterpret_cast<const u32x4_t*>(hc + 252 - 4 * lane);
+    const uint32_t c[4] = {h.w, h.z, h.y, h.x};
+    const uint32_t sum = c[0] + c[1] + c[2] + c[3];
+    const uint32_t incl = wave_inclusive_scan(sum, lane);
+    uint32_t cum = incl - sum, dsel = 0u, abv = 0u;
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (!found && cum + c[j] >= remaining) {
+        found = true;
+        dsel = (uint32_t)(255 - 4 * lane - j);
+        abv = cum;
+      }
+      cum += c[j];
+    }
+    found = found && incl - sum < remaining;
+    const uint64_t fb = __ballot(found);
+    const int fl = fb != 0 ? __builtin_amdgcn_readfirstlane(__ffsll((long long)fb) - 1) : 0;
+    const uint32_t digit = (uint32_t)__builtin_amdgcn_readlane((int)dsel, fl) & 255u;
+    const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)abv, fl);
+    prefix |= digit << shift;
+    mask |= 255u << shift;
+    remaining = remaining > above ? remaining - above : 0u;
+  }
+  const uint32_t T = prefix;
+  const uint32_t take_eq = remaining;   // keys equal to T to keep, smallest indices first
+  const int per = (cand + NT - 1) / NT;
+  const int lo = min(cand, tid * per), hi = min(cand, lo + per);
+  uint32_t gt = 0, eq = 0;
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t key = order_key(z[i]);
+    gt += key > T;
+    eq += key == T;
+  }
+  const uint32_t packed = (gt << 16) | eq;
+  const uint32_t incl = wave_inclusive_scan(packed, lane);
+  if (lane == 63) sh.wsum[wave] = incl;
+  lds_barrier();
+  uint32_t before = 0;
+  for (int w = 0; w < wave; ++w) before += sh.wsum[w];
+  const uint32_t excl = before + incl - packed;
+  // equal keys taken by the threads before this one (the first take_eq in
+  // index order), then this thread's share; take_eq - taken_before cannot
+  // wrap. (Written without a conditional subtraction: the optimizer turned
+  // `take_eq > eq_before ? take_eq - eq_before : 0` into an unconditional
+  // no-wrap subtraction and then dropped the min below as redundant.)
+  const uint32_t taken_before = min(excl & 0xffffu, take_eq);
+  uint32_t p = (excl >> 16) + taken_before;
+  const uint32_t take = min(eq, take_eq - taken_before);
+  uint32_t taken = 0;
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t key = order_key(z[i]);
+    bool keep = key > T;
+    if (key == T && taken < take) {
+      keep = true;
+      ++taken;
+    }
+    const bool ok = keep && p < (uint32_t)k;
+    if (ok) ks[p] = i;
+    pos[i] = ok ? (int)p : -1;
+    p += keep;
+  }
+  for (int r = tid; r < W; r += NT) {
+    ks[k + r] = cand + r;
+    pos[cand + r] = k + r;
   }
 }
 
