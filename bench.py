@@ -339,10 +339,11 @@ def run_decode_loop(args, wl, c, rkv):
 def run_paged(args, wl, c, rkv, variant):
     """The paged ragged workload: 128 sequences of 2K..32K tokens x 8 KV heads
     in 16-token shuffled pages, compressed in place with page return. The call
-    mutates the page table and free list, so both are restored from copies
-    before every step, outside the timed region; each step is timed with HIP
-    events on the call's stream (the host-side planning and the metadata
-    upload it enqueues are inside)."""
+    mutates the page pools, the page table and the free list, so all three
+    are restored from copies before every step, outside the timed region
+    (every step then does the same work); each step is timed with HIP events
+    on the call's stream (the host-side planning and the metadata upload it
+    enqueues are inside)."""
     import numpy as np
     import torch
     from synth import paged_case_device
@@ -352,6 +353,7 @@ def run_paged(args, wl, c, rkv, variant):
     H, ps, w = case.kv_heads, case.page_size, case.window
     table0 = torch.from_numpy(case.page_table).cuda()
     table = table0.clone()
+    K0, V0 = case.K_pages.clone(), case.V_pages.clone()
     freed = int(sum(-(-int(n) // ps) - int(b) // ps for n, b in zip(case.seq_len, case.budget)
                     if n > b))
     fl0 = torch.full((len(case.free_list) + freed,), -1, dtype=torch.int32, device="cuda")
@@ -366,16 +368,20 @@ def run_paged(args, wl, c, rkv, variant):
                                   case.Q, fl, len(case.free_list), w, case.lam, kept_idx=kept,
                                   **variant)
 
-    for _ in range(args.warmup):
+    def restore():
         table.copy_(table0)
         fl.copy_(fl0)
+        case.K_pages.copy_(K0)
+        case.V_pages.copy_(V0)
+
+    for _ in range(args.warmup):
+        restore()
         step()
     torch.cuda.synchronize()
     rkv.timing_enable(True)
     evs = []
     for _ in range(args.steps):
-        table.copy_(table0)
-        fl.copy_(fl0)
+        restore()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         step()
@@ -413,8 +419,8 @@ def run_paged(args, wl, c, rkv, variant):
             t = torch.arange(n, device="cuda")
             pg = table0[s_][t // ps].long()
             h = int(rng.integers(0, H))
-            sample.append((case.K_pages[pg, h, t % ps].float().cpu().numpy()[None],
-                           case.V_pages[pg, h, t % ps].float().cpu().numpy()[None],
+            sample.append((K0[pg, h, t % ps].float().cpu().numpy()[None],
+                           V0[pg, h, t % ps].float().cpu().numpy()[None],
                            case.Q[s_, h].float().cpu().numpy()[None]))
             budgets.append(int(case.budget[s_]))
         if sample:
@@ -438,7 +444,8 @@ def run_paged(args, wl, c, rkv, variant):
                    "head_dim": 128, "pool_pages": int(case.meta["pool"])},
         "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
         "step_ms": {"median": ms[len(ms) // 2], "min": ms[0], "max": ms[-1]},
-        "note": "page table and free list restored before every step, outside the timed region",
+        "note": "page pools, page table and free list restored before every step, outside the "
+                "timed region",
     }
     print(json.dumps(out))
 
