@@ -450,6 +450,41 @@ def run_paged(args, wl, c, rkv, variant):
     print(json.dumps(out))
 
 
+def memory_ceilings():
+    """What plain torch operations reach on this part, as a yardstick for the
+    kernels' rates: device copy (read + write), fill (write only) and a
+    random gather of 256-byte rows (read + write), at 0.5, 2 and 8 GiB, each
+    timed with HIP events over 10 calls after 3 untimed ones. One JSON line."""
+    import torch
+    out = []
+
+    def timed(fn, reps=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    for gib in (0.5, 2, 8):
+        n = int(gib * 2**30) // 2
+        a = torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_()
+        b = torch.empty_like(a)
+        idx = torch.randperm(n // 128, device="cuda")
+        rows_a, rows_b = a.view(-1, 128), b.view(-1, 128)
+        out.append({"gib": gib,
+                    "copy_tbs": 2 * n * 2 / timed(lambda: b.copy_(a)) / 1e12,
+                    "fill_tbs": n * 2 / timed(lambda: b.fill_(1.0)) / 1e12,
+                    "row_gather_tbs": 2 * n * 2 / timed(
+                        lambda: torch.index_select(rows_a, 0, idx, out=rows_b)) / 1e12})
+        del a, b, idx, rows_a, rows_b
+    print(json.dumps({"memory_ceilings": out, "unit": "TB/s (bytes read + written / time)"}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -467,6 +502,8 @@ def main():
                     help="head-shared selection over runs of this many consecutive units")
     ap.add_argument("--graph", action="store_true",
                     help="capture the compression call in a HIP graph and time its replays")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure plain copy, fill and random row-gather rates of this part")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy kernel three times, so "
                          "memory counters can be scaled against a known byte count")
@@ -480,6 +517,9 @@ def main():
     import decode_kv_cache_03_amd as rkv
     from synth import CONFIGS, dense_case_device
 
+    if args.ceilings:
+        memory_ceilings()
+        return
     if args.calibrate_copy:
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")   # 1 GiB
         dst = torch.empty_like(src)
