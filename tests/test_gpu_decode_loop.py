@@ -77,11 +77,12 @@ def test_zero_budget_or_buffer_disables_compression(rkv):
             loop.append(r, r, r[:, None])
 
 
-def test_full_decode_loop_sampled_events(rkv):
+def test_full_decode_loop_eight_chains(rkv):
     """The whole Llama3-8B-shaped decode loop (64 x 32 x 8 = 16384 units,
-    16384 steps, 120 events), as the loop benchmark runs it; three units are
-    checked against the oracle from snapshots at every 12th event and the
-    last one."""
+    16384 steps, 120 events), as the loop benchmark runs it; eight units
+    spread over sequences, layers and heads are checked against the oracle
+    from snapshots at every one of the 120 events, each event's input being
+    the cache the previous events compacted."""
     import torch
     from decode_kv_cache_03_amd.decode_loop import DecodeLoop
     from synth import CONFIGS
@@ -91,26 +92,24 @@ def test_full_decode_loop_sampled_events(rkv):
                           coverage=c["coverage"], sigma=c["sigma"], max_back=B)
     loop = DecodeLoop(stream.units, c["gqa"], kv_budget=B, window_size=w, divide_length=dl,
                       mix_lambda=lam)
-    units = [0, stream.units // 2 + 3, stream.units - 1]
-    checked = set(range(0, 120, 12)) | {119}
+    units = [0, 1, 2059, 4607, 8190, 9999, 12345, stream.units - 1]
     snap = {}
 
     def on_event(lp):
-        if lp.events in checked:
-            q = lp.window_queries()
-            snap["data"] = [(par.to_host_f32(lp.K[u]), par.to_host_f32(lp.V[u]), par.to_host_f32(q[u]))
-                            for u in units]
+        q = lp.window_queries()
+        snap["data"] = [(par.to_host_f32(lp.K[u]), par.to_host_f32(lp.V[u]), par.to_host_f32(q[u]))
+                        for u in units]
 
     loop.on_event = on_event
     done = 0
     for t in range(steps):
         k, v, q = stream.rows(t)
         ev = loop.events
-        if loop.append(k, v, q) and ev in checked:
+        if loop.append(k, v, q):
             torch.cuda.synchronize()
-            kept = loop.last_kept
+            kept = loop.last_kept.cpu().numpy()
             for (K, V, Q), u in zip(snap.pop("data"), units):
-                par.check_head(K, V, Q, B, w, lam, kept[u].cpu().numpy(), par.to_host_f32(loop.K[u]),
+                par.check_head(K, V, Q, B, w, lam, kept[u], par.to_host_f32(loop.K[u]),
                                par.to_host_f32(loop.V[u]), what=f"event {ev} unit {u}")
             done += 1
-    assert loop.events == 120 and done == len(checked)
+    assert loop.events == 120 and done == 120
