@@ -31,8 +31,9 @@
 //  * at the end of the unit the importance of every key is formed again from
 //    the held fragments (queries as MFMA rows, so a key's weights lie in one
 //    lane column and reduce in-lane and over two lane exchanges), then Z,
-//    the selection on Z in LDS, and the kept K rows stored from registers
-//    (the last tile's from LDS); the kept V rows move during the next unit's
+//    the selection on Z in LDS, and the kept K rows stored from registers,
+//    turned into whole rows per store through the wave's part of the V stage
+//    (the last tile's from its slot); the kept V rows move during the next unit's
 //    tile steps, a slice per step through an LDS stage;
 //  * a step's memory instructions are spread over its column loop (one V
 //    chunk per column block, the next tile's loads after the first block):
@@ -462,34 +463,46 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
       __syncthreads();
       int32_t* kept = kept_all + p.kept_off(u);
       for (int r = tid_u; r < B; r += kThreads) kept[r] = ks[r];
-      // kept K rows held in registers: lane quarter q writes chunks q + 4*ks,
-      // so the four quarters of a row fill 64 contiguous bytes per store;
-      // rows that are dropped store past the end of the buffer
+      // kept K rows held in registers. A fragment gives a row only four
+      // lanes (lane quarter q has chunks q + 4*ks), so a store straight from
+      // it writes 64-byte pieces of 16 rows; each 16-row half-block goes
+      // through this wave's 4 KiB of the V stage instead (chunk c of row r
+      // at r*256 + ((c ^ r) & 15)*16: no bank conflicts either way) and
+      // leaves as four stores of four whole rows. The stage is the wave's
+      // own and LDS operations of a wave run in order: no barrier. Rows
+      // that are dropped store past the end of the buffer.
       const __amdgpu_buffer_rsrc_t ko = __builtin_amdgcn_make_buffer_rsrc(
           K_out + (int64_t)u * out_stride, 0, B * kRowBytes, kBufferWord3);
       const int past = B * kRowBytes;
+      char* const tst = vstage + wave * 4096;
+      const int fr = lane_u & 15, fq = lane_u >> 4;
 #pragma unroll
       for (int s = 0; s < kHeld; ++s) {
         const int gb = 8 * s + wave;
         if (gb >= 4 * nh) continue;
 #pragma unroll
         for (int rs = 0; rs < 2; ++rs) {
-          const int o = pos[gb * 32 + rs * 16 + (lane_u & 15)];
-          const int ofs = o >= 0 ? o * kRowBytes + (lane_u >> 4) * 16 : past;
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            __builtin_amdgcn_raw_buffer_store_b128(A[s][rs][k], ko, ofs, k * 64, kOutPolicy);
+          for (int k = 0; k < 4; ++k) st16(tst + fr * 256 + (((fq + 4 * k) ^ fr) & 15) * 16, A[s][rs][k]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int rr = fq + 4 * k;   // row of the half-block; chunk fr
+            const int o = pos[gb * 32 + rs * 16 + rr];
+            __builtin_amdgcn_raw_buffer_store_b128(ld16(tst + rr * 256 + ((fr ^ rr) & 15) * 16), ko,
+                                                   o >= 0 ? o * kRowBytes + fr * 16 : past, 0,
+                                                   kOutPolicy);
+          }
         }
         vm += 8;
       }
-      // kept rows of the last tile, from its slot: four threads per row
+      // kept rows of the last tile, from its slot: sixteen threads per row,
+      // four whole rows per store
       {
-        const int x = tid_u >> 2, qq = tid_u & 3;
-        const int i = tl * 128 + x;
-        const int o = i < N ? pos[i] : -1;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int ch = qq * 4 + k;
+          const int x = k * 32 + (tid_u >> 4), ch = tid_u & 15;
+          const int i = tl * 128 + x;
+          const int o = i < N ? pos[i] : -1;
           __builtin_amdgcn_raw_buffer_store_b128(ld16(lslot + frag_offset<bf16_bits>(x, ch)), ko,
                                                  o >= 0 ? o * kRowBytes + ch * 16 : past, 0,
                                                  kOutPolicy);
