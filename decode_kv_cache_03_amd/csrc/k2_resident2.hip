@@ -26,7 +26,8 @@
 //    tile stays in its slot for its own pairs, as in the one-pass kernel.
 //  * the end of the unit is the one-pass kernel's: importance and Z of the
 //    rows held now and of the last tile, the selection, and K' rows stored
-//    from registers (rows of pass 1) and from LDS (the last tile). The kept
+//    from registers (rows of pass 1, turned into whole rows per store through
+//    the wave's part of the stage) and from LDS (the last tile). The kept
 //    rows of pass 0 are no longer in registers: they move, with the kept V
 //    rows, during the next unit's tile steps (a slice per step through an
 //    LDS stage); the last unit's move after the loop.
@@ -469,32 +470,43 @@ __global__ __launch_bounds__(kThreads, 1) void k2r2_kernel(
         if (kr < kPR && (r + 1 == B || ks[r + 1] >= kPR)) *nlow_lds = r + 1;
       }
       if (tid_u == 0 && ks[0] >= kPR) *nlow_lds = 0;
-      // kept K rows of pass 1 from registers (dropped rows store past the end)
+      // kept K rows of pass 1 from registers: each 16-row half-block turns
+      // into whole rows through this wave's 4 KiB of the stage (chunk c of
+      // row r at r*256 + ((c ^ r) & 15)*16; the wave's own, its LDS
+      // operations in order: no barrier) and leaves as four stores of four
+      // rows; dropped rows store past the end
       const __amdgpu_buffer_rsrc_t ko = __builtin_amdgcn_make_buffer_rsrc(
           K_out + (int64_t)u * out_stride, 0, B * kRowBytes, kBufferWord3);
       const int past = B * kRowBytes;
+      char* const tst = vstage + wave * 4096;
+      const int fr = lane_u & 15, fq = lane_u >> 4;
 #pragma unroll
       for (int s = 0; s < kHeld; ++s) {
         const int lb = 8 * s + wave;
         if (lb >= 4 * nh1) continue;
 #pragma unroll
         for (int rs = 0; rs < 2; ++rs) {
-          const int o = pos[kPR + lb * 32 + rs * 16 + (lane_u & 15)];
-          const int ofs = o >= 0 ? o * kRowBytes + (lane_u >> 4) * 16 : past;
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            __builtin_amdgcn_raw_buffer_store_b128(A[s][rs][k], ko, ofs, k * 64, kOutPolicy);
+          for (int k = 0; k < 4; ++k) st16(tst + fr * 256 + (((fq + 4 * k) ^ fr) & 15) * 16, A[s][rs][k]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int rr = fq + 4 * k;   // row of the half-block; chunk fr
+            const int o = pos[kPR + lb * 32 + rs * 16 + rr];
+            __builtin_amdgcn_raw_buffer_store_b128(ld16(tst + rr * 256 + ((fr ^ rr) & 15) * 16), ko,
+                                                   o >= 0 ? o * kRowBytes + fr * 16 : past, 0,
+                                                   kOutPolicy);
+          }
         }
         vm += 8;
       }
-      // kept rows of the last tile, from its slot: four threads per row
+      // kept rows of the last tile, from its slot: sixteen threads per row,
+      // four whole rows per store
       {
-        const int x = tid_u >> 2, qq = tid_u & 3;
-        const int i = tl * 128 + x;
-        const int o = i < N ? pos[i] : -1;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int ch = qq * 4 + k;
+          const int x = k * 32 + (tid_u >> 4), ch = tid_u & 15;
+          const int i = tl * 128 + x;
+          const int o = i < N ? pos[i] : -1;
           __builtin_amdgcn_raw_buffer_store_b128(ld16(lslot + frag_offset<bf16_bits>(x, ch)), ko,
                                                  o >= 0 ? o * kRowBytes + ch * 16 : past, 0,
                                                  kOutPolicy);
