@@ -249,6 +249,18 @@ __global__ __launch_bounds__(kThreads, 1) void k2r2_kernel(
           }
         }
 
+        // tiles that pass 0 does not hold: the statistics of 16 keys per wave
+        // from the slot, before the pair loop in waves 0..3 and after it in
+        // waves 4..7, so that on a SIMD (waves w and w + 4) one wave's
+        // exponentials run under the other's matrix work
+        auto slot_stats = [&]() {
+          u32x4_t kf[1][4];
+          load_frag(slot, wave * 16, lane_u, kf[0]);
+          stats_update_groups<1, NQG>(kf, qlds, t * 128 + wave * 16, N, W, G, rpg_shift, causal,
+                                      lane_u, mrun, srun);
+        };
+        if (pass == 0 && tl >= nhp && wave < 4) slot_stats();
+
         // columns: the tile's keys against every held row before them, then
         // the wave's own block of the tile under the diagonal mask
         const int nfull = min(kHeld, max(0, (4 * min(tl, nhp) - wave + 7) >> 3));
@@ -293,13 +305,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r2_kernel(
                                           mrun, srun);
             }
           }
-          // tiles that pass 0 does not hold: 16 keys per wave from the slot
-          if (tl >= nhp) {
-            u32x4_t kf[1][4];
-            load_frag(slot, wave * 16, lane_u, kf[0]);
-            stats_update_groups<1, NQG>(kf, qlds, t * 128 + wave * 16, N, W, G, rpg_shift, causal,
-                                        lane_u, mrun, srun);
-          }
+          if (tl >= nhp && wave >= 4) slot_stats();
         }
         if (nv > 0) {
           __builtin_amdgcn_s_waitcnt(vm_imm(0));   // the wave's chunks have landed
