@@ -141,6 +141,21 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Inclusive sum over lanes 0..lane of one 64-lane wave, in data-parallel
+// primitive (DPP) moves instead of cross-lane permutes through the LDS unit:
+// within each row of 16 lanes, the value 1, 2, 4 and 8 lanes down is added
+// (lanes with no source in the row add 0); then lane 15 of rows 0 and 2 is
+// added to every lane of rows 1 and 3, and lane 31 to rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return v;
+}
+
 // Inclusive scan of one uint32 per thread over a block of NT threads
 // (a multiple of 64, at most 1024). `scratch` must hold NT/64 uint32 and be
 // shared. Also returns the block total. All threads must call it.
@@ -149,11 +164,7 @@ __device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t* s
                                                          uint32_t* total) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
+  v = wave_inclusive_scan(v);
   if (lane == 63) scratch[wave] = v;
   __syncthreads();
   uint32_t before = 0, tot = 0;

@@ -110,16 +110,6 @@ __device__ __forceinline__ void select_block(const float* __restrict__ z, int N,
   }
 }
 
-// Inclusive sum over the lanes 0..lane of one wave.
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
-  return v;
-}
-
 // Shared scratch of select_block_lean: three rotating histograms and the
 // per-wave totals of the ordered pass's scan.
 struct SelectLeanScratch {
@@ -187,7 +177,7 @@ __device__ __forceinline__ void select_block_lean(const float* __restrict__ z, i
     const u32x4_t h = *reinterpret_cast<const u32x4_t*>(hc + 252 - 4 * lane);
     const uint32_t c[4] = {h.w, h.z, h.y, h.x};
     const uint32_t sum = c[0] + c[1] + c[2] + c[3];
-    const uint32_t incl = wave_inclusive_scan(sum, lane);
+    const uint32_t incl = wave_inclusive_scan(sum);
     uint32_t cum = incl - sum, dsel = 0u, abv = 0u;
     bool found = false;
 #pragma unroll
@@ -219,7 +209,7 @@ __device__ __forceinline__ void select_block_lean(const float* __restrict__ z, i
     eq += key == T;
   }
   const uint32_t packed = (gt << 16) | eq;
-  const uint32_t incl = wave_inclusive_scan(packed, lane);
+  const uint32_t incl = wave_inclusive_scan(packed);
   if (lane == 63) sh.wsum[wave] = incl;
   lds_barrier();
   uint32_t before = 0;
