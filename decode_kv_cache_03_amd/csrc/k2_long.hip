@@ -610,12 +610,22 @@ __global__ __launch_bounds__(kThreads, 1) void k2lr_kernel(P p, const float* __r
       for (int v = 0; v < 4; ++v) mx[s][rs][v] = vmax(mx[s][rs][v], vmax(acc[0][v] * rc0, acc[1][v] * rc1));
     };
 
+    // Tiles are taken two per barrier: after it, each wave works through
+    // both without waiting for the others (an owner copies only its own rows,
+    // and what it writes to LDS is read after the item's last barrier); the
+    // two slots are given back at the next barrier.
     const int len = g.len();
-    for (int k = 0; k < len; ++k) {
-      ensure_issued(c);
-      wait_tiles<kPer>(issued - (c + 1));
+    for (int k0 = 0; k0 < len; k0 += 2) {
+      const int two = k0 + 1 < len ? 2 : 1;
+      if (issued < c + two) {   // the pair not issued yet (start of an item)
+        lds_barrier();
+        refill(c);
+      }
+      wait_tiles<kPer>(issued - (c + two));
       lds_barrier();
       refill(c);
+#pragma unroll 1
+      for (int k = k0; k < k0 + two; ++k) {
       const char* slot = lds + cons_slot * kTileBytes;
       const float* rns = reinterpret_cast<const float*>(lds + L.rn + cons_slot * 512);
       const bool own = k < g.nt;
@@ -710,6 +720,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2lr_kernel(P p, const float* __r
       }
       ++c;
       cons_slot = cons_slot + 1 == S ? 0 : cons_slot + 1;
+      }
     }
 
     // row maxima over the 16 column lanes of each quarter, then R, I, Z

@@ -212,7 +212,7 @@ struct LongPlanR {
 
 __host__ __device__ inline LongPlanR long_plan_r(int gw) {
   LongPlanR L;
-  L.slots = 3;
+  L.slots = 4;   // two tiles in use, two in flight
   L.rn = L.slots * 128 * 256;
   L.q = L.rn + L.slots * 128 * 4;
   L.qbytes = (gw * 256 + 1023) / 1024 * 1024;
