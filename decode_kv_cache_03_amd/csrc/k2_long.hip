@@ -26,7 +26,9 @@
 //    up to 4 LDS slots by direct global->LDS loads; a step waits only for its
 //    own tile (the wait counts the loads issued after it), and the stream
 //    runs on across items; each item's window queries and softmax normalisers
-//    come with its first tile, into one of two parity buffers;
+//    come with its first tile, into one of two parity buffers; the 1024-row
+//    form takes two tiles per workgroup barrier (4 slots: two in use, two in
+//    flight);
 //  * an item streams its own tiles in descending order (each wave takes its
 //    rows as A fragments, its row norms and its keys' importance when its own
 //    tile arrives; tiles of lower rows come later, so every wave that needs a
