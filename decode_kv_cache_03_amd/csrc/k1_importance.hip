@@ -92,15 +92,18 @@ __global__ __launch_bounds__(256) void k1_stats_kernel(P p, float* __restrict__ 
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's rows are in
     // paged units scored by the long-unit kernel: their keys to contiguous
-    // rows, a whole row per 16 lanes
+    // rows, a whole row per 16 lanes, as streaming stores (the copy is far
+    // larger than the caches; the long-unit kernel reads it back later)
     if (p.copy_dst(u, 0) != nullptr) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int rr = 4 * i + (lane >> 4);
         const int key = rbase + rr;
         if (key < N)
-          st16(reinterpret_cast<char*>(p.copy_dst(u, key)) + (((lane & 15) ^ (rr & 15)) << 4),
-               ld16(ws + i * 1024 + lane * 16));
+          __builtin_nontemporal_store(
+              ld16(ws + i * 1024 + lane * 16),
+              reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(p.copy_dst(u, key)) +
+                                         (((lane & 15) ^ (rr & 15)) << 4)));
       }
     }
   }
