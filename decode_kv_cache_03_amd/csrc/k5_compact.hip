@@ -10,6 +10,9 @@
 // Dense: out of place, K_out[r] = K[kept[r]] and V_out[r] = V[kept[r]], as
 // bit copies in 16-byte chunks; each workgroup moves 64 rows of K and V.
 //
+// Every row moved is read once and written once: loads and stores are
+// streaming (non-temporal) in the paged compaction.
+//
 // Paged: in place, one workgroup per (sequence, head). Kept indices ascend,
 // so kept[r] >= r: slot r's source never lies before slot r. Slots are
 // processed in chunks of 128 in ascending order, each in two phases: every
@@ -101,8 +104,8 @@ __global__ __launch_bounds__(256) void k5_paged_kernel(PagedProblem<T> p, T* Kp,
       const int r = c0 + q / RC, c = q % RC;
       src[i] = (r < B) ? clamp_row(kept[r], N) : r;
       if (src[i] != r) {
-        kv[i] = ld16(reinterpret_cast<const char*>(p.krow(u, src[i])) + 16 * c);
-        vv[i] = ld16(reinterpret_cast<const char*>(p.vrow(u, src[i])) + 16 * c);
+        kv[i] = ld16_stream(reinterpret_cast<const char*>(p.krow(u, src[i])) + 16 * c);
+        vv[i] = ld16_stream(reinterpret_cast<const char*>(p.vrow(u, src[i])) + 16 * c);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);        // this chunk's loads have landed
@@ -112,8 +115,8 @@ __global__ __launch_bounds__(256) void k5_paged_kernel(PagedProblem<T> p, T* Kp,
       const int q = i * 256 + tid;
       const int r = c0 + q / RC, c = q % RC;
       if (src[i] != r) {
-        st16(wrow(p, Kp, u, r) + 16 * c, kv[i]);
-        st16(wrow(p, Vp, u, r) + 16 * c, vv[i]);
+        __builtin_nontemporal_store(kv[i], reinterpret_cast<u32x4_t*>(wrow(p, Kp, u, r) + 16 * c));
+        __builtin_nontemporal_store(vv[i], reinterpret_cast<u32x4_t*>(wrow(p, Vp, u, r) + 16 * c));
       }
     }
   }
