@@ -11,7 +11,7 @@
 // bit copies in 16-byte chunks; each workgroup moves 64 rows of K and V.
 //
 // Every row moved is read once and written once: loads and stores are
-// streaming (non-temporal) in the paged compaction.
+// streaming (non-temporal) in both.
 //
 // Paged: in place, one workgroup per (sequence, head). Kept indices ascend,
 // so kept[r] >= r: slot r's source never lies before slot r. Slots are
@@ -47,8 +47,8 @@ __global__ __launch_bounds__(256) void k5_gather_kernel(DenseProblem<T> p,
     const int r = r0 + q / RC, c = q % RC;
     if (r < nkeep) {
       const int src = clamp_row(kept[r], p.N);
-      kv[i] = ld16(reinterpret_cast<const char*>(p.krow(u, src)) + 16 * c);
-      vv[i] = ld16(reinterpret_cast<const char*>(p.vrow(u, src)) + 16 * c);
+      kv[i] = ld16_stream(reinterpret_cast<const char*>(p.krow(u, src)) + 16 * c);
+      vv[i] = ld16_stream(reinterpret_cast<const char*>(p.vrow(u, src)) + 16 * c);
     }
   }
 #pragma unroll
@@ -57,8 +57,8 @@ __global__ __launch_bounds__(256) void k5_gather_kernel(DenseProblem<T> p,
     const int r = r0 + q / RC, c = q % RC;
     if (r < nkeep) {
       const int64_t off = (int64_t)u * out_stride + (int64_t)r * kD;
-      st16(reinterpret_cast<char*>(K_out + off) + 16 * c, kv[i]);
-      st16(reinterpret_cast<char*>(V_out + off) + 16 * c, vv[i]);
+      __builtin_nontemporal_store(kv[i], reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(K_out + off) + 16 * c));
+      __builtin_nontemporal_store(vv[i], reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(V_out + off) + 16 * c));
     }
   }
 }
