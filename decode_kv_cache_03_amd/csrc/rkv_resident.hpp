@@ -25,9 +25,10 @@ using stream::vm_imm;
 constexpr int kThreads = 512;
 constexpr int kRowBytes = 256;                  // bf16 row of 128
 constexpr int kTileBytes = 128 * kRowBytes;
-// Cache policy of the K'/V' stores: the default (write-back through L2)
-// measured faster here than streaming stores.
-constexpr int kOutPolicy = 0;
+// Cache policy of the K'/V' stores: streaming (non-temporal). K' and V' are
+// written once and read by no later step of this call; with whole rows per
+// store this measured faster than the default write-back through L2.
+constexpr int kOutPolicy = kCachePolicyStream;
 
 // Wait until at most n vector-memory instructions of this wave are in
 // flight (n rounded down to a multiple of 4: never a shorter wait).
