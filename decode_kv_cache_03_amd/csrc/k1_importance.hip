@@ -36,6 +36,13 @@
 
 namespace rkv {
 
+// 16 bytes from global memory into LDS with the streaming (non-temporal)
+// cache policy: the statistics pass reads each key row once.
+__device__ __forceinline__ void load16_to_lds_stream(const void* src, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_dst), 16, 0,
+                                   kCachePolicyStream);
+}
+
 // Load the lane's half (64 elements) of a 128-element row, or zeros.
 template <typename T>
 __device__ __forceinline__ void load_half_row(u32x4_t (&f)[Elem<T>::kHalfChunks], const T* row,
@@ -87,7 +94,7 @@ __global__ __launch_bounds__(256) void k1_stats_kernel(P p, float* __restrict__ 
     for (int i = 0; i < 16; ++i) {
       const int rr = 4 * i + (lane >> 4);
       const int key = min(rbase + rr, N - 1);   // rows past N repeat row N-1
-      load16_to_lds(reinterpret_cast<const char*>(p.krow(u, key)) + (((lane & 15) ^ (rr & 15)) << 4),
+      load16_to_lds_stream(reinterpret_cast<const char*>(p.krow(u, key)) + (((lane & 15) ^ (rr & 15)) << 4),
                     ws + i * 1024);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's rows are in
