@@ -132,6 +132,10 @@ TIE_CASES = [
     ("one-row-lam", 1152, 1024, 8, 0.1),
     ("three-rows", 1100, 700, 8, 0.0),
     ("two-rows-small", 300, 150, 8, 0.0),
+    # the two-pass kernel (1152 < N <= 2176): its selection over 2168 and
+    # 1992 candidates, rows below 1024 moved a unit later
+    ("one-row-2pass", 2176, 2048, 8, 0.0),
+    ("three-rows-2pass", 2000, 1504, 8, 0.1),
 ]
 
 
@@ -148,7 +152,7 @@ def test_resident_selection_ties(rkv, case_):
         base = case.K[h, :rows].copy()
         case.K[h] = base[pick]
     res, labels = _run(rkv, case)
-    assert list(labels) == ["rkv_k2_resident"]
+    assert list(labels) == ["rkv_k2_resident" if n <= 1152 else "rkv_k2_resident2"]
     kept = res.kept_idx.cpu().numpy()
     Z = res.Z.cpu().numpy()
     Ko = par.to_host_f32(res.K_out)
