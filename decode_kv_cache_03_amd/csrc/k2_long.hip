@@ -36,8 +36,11 @@
 //    symmetric variant adds the tiles right of the block and, at the end, the
 //    own tiles above each wave's rows again;
 //  * the 1/||k|| of a tile's rows (from the statistics pass) travel with the
-//    tile into the ring, one 4-byte direct load per lane of 16 lanes per
-//    wave, so each wave issues 5 loads per tile and the waits count 5;
+//    tile into the ring, one 4-byte direct load per lane: in the 512-row
+//    form each wave loads 16 rows of keys and norms (5 loads per tile, the
+//    waits count 5); in the 1024-row form only waves 0-3 load, 32 rows each
+//    (9 loads), so that waves 4-7, which lose the matrix-pipe arbitration to
+//    them, never stall in the address unit;
 //  * work items go to workgroups in order of decreasing cost, alternating
 //    direction each round (a greedy longest-first schedule): item k of round
 //    r is k = r*G + b for workgroup b on even rounds, r*G + G-1-b on odd ones.
@@ -426,7 +429,12 @@ using stream::wait_tiles;
 constexpr int kThreads = 512;
 constexpr int kRowBytes = 256;
 constexpr int kTileBytes = 128 * kRowBytes;
-constexpr int kPer = kLoadsPerTile + 1;   // loads per wave per tile: 4 of keys, 1 of norms
+// Only waves 0-3 load tiles: 8 loads of keys and 1 of norms each per tile.
+// A wave stalls while the address unit takes its loads; waves 4-7, which
+// share each SIMD's matrix pipe with them and lose the issue arbitration to
+// the older waves, never do.
+constexpr int kLoaders = 4;
+constexpr int kPer = 2 * kLoadsPerTile + 1;
 
 // Tile order of an item of up to 8 own tiles: own tiles descending, then
 // tiles 0..t0-1.
@@ -504,24 +512,26 @@ __global__ __launch_bounds__(kThreads, 1) void k2lr_kernel(P p, const float* __r
     const int t = ld_g.tile(ld_k);
     char* slot = lds + issue_slot * kTileBytes;
     const bf16_bits* urows = rows + ld_it.row_base;
-    // 1/||k|| of tile rows 16w.. (rows past n repeat row n-1), 16 lanes x 4 bytes
-    if (lane_v < 16) {
-      const int rr = min(t * 128 + wave * 16 + lane_v, ld_it.n - 1);
-      __builtin_amdgcn_global_load_lds(rinv + ld_it.score_off + rr,
-                                       (__attribute__((address_space(3))) void*)(lds + L.rn + issue_slot * 512 + wave * 64),
-                                       4, 0, 0);
-    }
-    // Tile load q (0..3) of wave w fills KiB 4w + q of a slot: tile row
-    // 16w + 4q + lane/16 at chunk position lane % 16, fetching chunk
-    // (lane % 16) ^ (row & 15) of that row.
-    const int row0 = t * 128 + wave * 16;
+    if (wave < kLoaders) {
+      // 1/||k|| of tile rows 32w.. (rows past n repeat row n-1), 32 lanes x 4 bytes
+      if (lane_v < 32) {
+        const int rr = min(t * 128 + wave * 32 + lane_v, ld_it.n - 1);
+        __builtin_amdgcn_global_load_lds(rinv + ld_it.score_off + rr,
+                                         (__attribute__((address_space(3))) void*)(lds + L.rn + issue_slot * 512 + wave * 128),
+                                         4, 0, 0);
+      }
+      // Tile load q (0..7) of wave w fills KiB 8w + q of a slot: tile row
+      // 32w + 4q + lane/16 at chunk position lane % 16, fetching chunk
+      // (lane % 16) ^ (row & 15) of that row.
+      const int row0 = t * 128 + wave * 32;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int rt = row0 + 4 * q + lane_v / 16;
-      const int r = min(rt, ld_it.n - 1);   // rows past n repeat row n-1
-      const int c = (lane_v % 16) ^ (rt & 15);
-      load16_to_lds(reinterpret_cast<const char*>(urows + (int64_t)r * kD) + c * 16,
-                    slot + wave * 4096 + q * 1024);
+      for (int q = 0; q < 8; ++q) {
+        const int rt = row0 + 4 * q + lane_v / 16;
+        const int r = min(rt, ld_it.n - 1);   // rows past n repeat row n-1
+        const int c = (lane_v % 16) ^ (rt & 15);
+        load16_to_lds(reinterpret_cast<const char*>(urows + (int64_t)r * kD) + c * 16,
+                      slot + wave * 8192 + q * 1024);
+      }
     }
     ++issued;
     issue_slot = issue_slot + 1 == S ? 0 : issue_slot + 1;
@@ -623,7 +633,9 @@ __global__ __launch_bounds__(kThreads, 1) void k2lr_kernel(P p, const float* __r
         lds_barrier();
         refill(c);
       }
-      wait_tiles<kPer>(issued - (c + two));
+      // waves 4-7 issue only an item's window queries (and their Z stores):
+      // they wait for all of theirs
+      wait_tiles<kPer>(wave < kLoaders ? issued - (c + two) : 0);
       lds_barrier();
       refill(c);
 #pragma unroll 1
