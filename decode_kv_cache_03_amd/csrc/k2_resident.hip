@@ -38,7 +38,9 @@
 //  * a step's memory instructions are spread over its column loop (one V
 //    chunk per column block, the next tile's loads after the first block):
 //    issued together right after the step barrier, the eight waves' loads
-//    queue at the CU's vector-memory path and hold back the matrix work.
+//    queue at the CU's vector-memory path and hold back the matrix work;
+//    and only waves 0-3 load key tiles (8 KiB each): waves 4-7 share each
+//    SIMD with one of them and lose the issue arbitration to it.
 // Variants: without the causal window the statistics and weights mask only
 // padding keys; mean pooling sums the heads' window means and divides by G.
 // The symmetric R needs later keys as well and is served by k2_wide.hip.
@@ -53,6 +55,8 @@ namespace rkv {
 namespace resident {
 
 using namespace frag16;
+
+constexpr int kLoaders = 4;   // waves that load key tiles, 8 KiB each
 using stream::vm_imm;
 
 template <int kHeld>
@@ -105,9 +109,11 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
     if (ld_u >= p.num_units || ld_u >= ld_limit) return false;
     int lane_v = lane;   // per call: keeps lane-derived values out of the callers' loops
     asm volatile("" : "+v"(lane_v));
-    // Tile load q (0..3) of wave w fills KiB 4w + q of a slot: tile row
-    // 16w + 4q + lane/16 at chunk position lane % 16, fetching chunk
-    // (lane % 16) ^ (row & 15) of that row.
+    // Only waves 0-3 load tiles (waves 4-7 share each SIMD with them and
+    // lose the issue arbitration to the older waves). Tile load q (0..7) of
+    // wave w fills KiB 8w + q of a slot: tile row 32w + 4q + lane/16 at
+    // chunk position lane % 16, fetching chunk (lane % 16) ^ (row & 15) of
+    // that row (the lane offsets repeat every four loads).
     int lofs[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -127,21 +133,23 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
     }
     const int t = ld_k;
     char* slot = lds + issue_slot * kTileBytes;
-    const int row0 = t * 128 + wave * 16;   // first tile row this wave loads
-    if ((t + 1) * 128 <= N) {
-      const char* src = reinterpret_cast<const char*>(p.krow(ld_u, row0));
+    if (wave < kLoaders) {
+      const int row0 = t * 128 + wave * 32;   // first tile row this wave loads
+      if ((t + 1) * 128 <= N) {
+        const char* src = reinterpret_cast<const char*>(p.krow(ld_u, row0));
 #pragma unroll
-      for (int q = 0; q < 4; ++q) load16_to_lds(src + q * 1024 + lofs[q], slot + wave * 4096 + q * 1024);
-    } else {   // last tile of the unit: rows past N repeat row N-1
+        for (int q = 0; q < 8; ++q) load16_to_lds(src + q * 1024 + lofs[q & 3], slot + wave * 8192 + q * 1024);
+      } else {   // last tile of the unit: rows past N repeat row N-1
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = min(row0 + 4 * q + lane_v / 16, N - 1);
-        const int chunk_ofs = lofs[q] - (lane_v / 16) * kRowBytes;
-        load16_to_lds(reinterpret_cast<const char*>(p.krow(ld_u, r)) + chunk_ofs,
-                      slot + wave * 4096 + q * 1024);
+        for (int q = 0; q < 8; ++q) {
+          const int r = min(row0 + 4 * q + lane_v / 16, N - 1);
+          const int chunk_ofs = lofs[q & 3] - (lane_v / 16) * kRowBytes;
+          load16_to_lds(reinterpret_cast<const char*>(p.krow(ld_u, r)) + chunk_ofs,
+                        slot + wave * 8192 + q * 1024);
+        }
       }
+      vm += 8;
     }
-    vm += 4;
     if (issue_slot == 0)
       mark0 = vm;
     else
