@@ -19,8 +19,9 @@
 //    leave a partial column max (rows 0..1023 only, before the 1/||k_j||
 //    factor) in the score array. Pass 0 also takes every key's softmax
 //    statistics: held blocks from registers one step after their copy, later
-//    tiles from LDS, 16 keys per wave. At its end the statistics are merged
-//    and the importance and Z of rows 0..1023 are formed from the fragments.
+//    tiles from LDS, 32 keys per wave of waves 0-3. At its end the
+//    statistics are merged and the importance and Z of rows 0..1023 are
+//    formed from the fragments.
 //  * pass 1 holds tiles 8..nb-2 and streams tiles 8..nb-1: the pairs of those
 //    rows with every later key, merged with pass 0's partial maxima. The last
 //    tile stays in its slot for its own pairs, as in the one-pass kernel.
@@ -249,17 +250,21 @@ __global__ __launch_bounds__(kThreads, 1) void k2r2_kernel(
           }
         }
 
-        // tiles that pass 0 does not hold: the statistics of 16 keys per wave
-        // from the slot, before the pair loop in waves 0..3 and after it in
-        // waves 4..7, so that on a SIMD (waves w and w + 4) one wave's
-        // exponentials run under the other's matrix work
-        auto slot_stats = [&]() {
+        // tiles that pass 0 does not hold: the statistics of their keys from
+        // the slot, 32 keys per wave of waves 0..3, before their pair loop.
+        // Waves w and w + 4 share a SIMD and the older wave w wins its matrix
+        // pipe, so waves 4..7 finish their pair loops last: they start them
+        // at once, alone on the pipe while waves 0..3 take the exponentials.
+        auto slot_stats = [&](int r0) {
           u32x4_t kf[1][4];
-          load_frag(slot, wave * 16, lane_u, kf[0]);
-          stats_update_groups<1, NQG>(kf, qlds, t * 128 + wave * 16, N, W, G, rpg_shift, causal,
+          load_frag(slot, r0, lane_u, kf[0]);
+          stats_update_groups<1, NQG>(kf, qlds, t * 128 + r0, N, W, G, rpg_shift, causal,
                                       lane_u, mrun, srun);
         };
-        if (pass == 0 && tl >= nhp && wave < 4) slot_stats();
+        if (pass == 0 && tl >= nhp && wave < 4) {
+          slot_stats(wave * 32);
+          slot_stats(wave * 32 + 16);
+        }
 
         // columns: the tile's keys against every held row before them, then
         // the wave's own block of the tile under the diagonal mask
@@ -305,7 +310,6 @@ __global__ __launch_bounds__(kThreads, 1) void k2r2_kernel(
                                           mrun, srun);
             }
           }
-          if (tl >= nhp && wave >= 4) slot_stats();
         }
         if (nv > 0) {
           __builtin_amdgcn_s_waitcnt(vm_imm(0));   // the wave's chunks have landed
