@@ -55,9 +55,9 @@ namespace rkv {
 namespace resident {
 
 using namespace frag16;
-using stream::vm_imm;
 
 constexpr int kLoaders = 4;   // waves that load key tiles, 8 KiB each
+using stream::vm_imm;
 
 template <int kHeld>
 __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
