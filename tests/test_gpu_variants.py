@@ -90,7 +90,9 @@ def test_symmetric_scores_both_copies(rkv):
     assert np.all(R_sym >= R_def - 1e-6)
 
 
-@pytest.mark.parametrize("variant", ["symmetric", "all"])
+# symmetric (and all) run the 512-row long-unit form on the pages; no-causal
+# and mean pooling the 1024-row form
+@pytest.mark.parametrize("variant", ["symmetric", "no-causal", "pool-mean", "all"])
 def test_paged_variants(rkv, variant):
     import torch
     var = VARIANTS[variant]
