@@ -62,6 +62,9 @@ Variants of those readings, selected by keyword arguments (defaults = R1-R8):
   eviction-score all-reduce [P1 "What the redundancy scoring actually does
   at decode time"], select on the SUM of their Z (an all-reduce's default
   reduction); the window and the top B-w of that sum are kept by every head.
+  On pages (compress_paged(shared_heads=True)) the group is a sequence's H
+  heads: one token set per sequence, the layout vLLM's token-major pages
+  need.
 """
 from __future__ import annotations
 
@@ -261,7 +264,8 @@ def return_pages(page_table, seq_len, budget, free_list, page_size: int):
 
 
 def compress_paged(K_pages, V_pages, page_table, seq_len, budget, Q, free_list,
-                   window: int, lam: float, page_size: int, **variant) -> dict:
+                   window: int, lam: float, page_size: int, shared_heads: bool = False,
+                   **variant) -> dict:
     """Paged compression with page return (reading R8).
 
     K_pages, V_pages [P, H, page_size, d]; page_table [S, maxp]; seq_len,
@@ -269,6 +273,9 @@ def compress_paged(K_pages, V_pages, page_table, seq_len, budget, Q, free_list,
     call. Returns dict(K_pages, V_pages, page_table, free_list, kept) where
     kept[s][h] are the kept logical indices and the pages are new arrays.
     The keyword arguments select the reading variants, as in compress_head.
+    shared_heads: the H heads of each sequence select together, as in
+    compress_shared (one token set per sequence, chosen on the sum of the
+    heads' Z); the pages and the page return are handled as before.
     """
     Kp = np.array(K_pages, copy=True)
     Vp = np.array(V_pages, copy=True)
@@ -279,18 +286,21 @@ def compress_paged(K_pages, V_pages, page_table, seq_len, budget, Q, free_list,
         b = int(budget[s])
         if b % page_size != 0:
             raise ValueError("paged budget must be a multiple of the page size")
-        kept_s = []
-        for h in range(heads):
-            Kl = logical_rows(K_pages, page_table[s], n, h, page_size)
-            Vl = logical_rows(V_pages, page_table[s], n, h, page_size)
-            res = compress_head(Kl, Vl, np.asarray(Q)[s, h], b, window, lam, **variant)
-            kept = res["kept"]
-            kept_s.append(kept)
-            if n <= b:
-                continue
-            r = np.arange(len(kept))
-            Kp[page_table[s][r // page_size], h, r % page_size] = Kl[kept]
-            Vp[page_table[s][r // page_size], h, r % page_size] = Vl[kept]
+        Kl = [logical_rows(K_pages, page_table[s], n, h, page_size) for h in range(heads)]
+        Vl = [logical_rows(V_pages, page_table[s], n, h, page_size) for h in range(heads)]
+        if shared_heads:
+            res = compress_shared(np.stack(Kl), np.stack(Vl), np.asarray(Q)[s], b, window, lam,
+                                  **variant)
+            kept_s = [res["kept"]] * heads
+        else:
+            kept_s = [compress_head(Kl[h], Vl[h], np.asarray(Q)[s, h], b, window, lam,
+                                    **variant)["kept"] for h in range(heads)]
+        if n > b:
+            for h in range(heads):
+                kept = kept_s[h]
+                r = np.arange(len(kept))
+                Kp[page_table[s][r // page_size], h, r % page_size] = Kl[h][kept]
+                Vp[page_table[s][r // page_size], h, r % page_size] = Vl[h][kept]
         kept_all.append(kept_s)
     table, freed = return_pages(page_table, seq_len, budget, free_list, page_size)
     return dict(K_pages=Kp, V_pages=Vp, page_table=table, free_list=freed, kept=kept_all)

@@ -505,9 +505,67 @@ def check_shared(seed):
         assert list(o["kept"]) == list(orc.compress_head(K0, V0, Q0, b, w, lam)["kept"])
 
 
+def check_paged_shared(seed):
+    """Head-shared selection on pages: the page table and free list as for
+    per-head selection (page return does not depend on which tokens are
+    kept); every head of a compressed sequence keeps one set, the one the
+    brute-force shared selection picks on the sequence's logical rows; the
+    kept rows are moved exactly and nothing else changes. A pool whose heads
+    are copies of one another selects what per-head selection selects."""
+    from synth import paged_case_host
+    ps = 4   # tiny sequences: the brute force enumerates every kept set
+    lens, fracs = [10, 12, 7, 11], [0.6, 0.5, 0.9, 0.7]
+    case = paged_case_host(seed, lens, fracs, kv_heads=3, gqa=2, window=2, lam=0.1,
+                           dtype="f32", page_size=ps, spare_pages=3, d=4)
+    var = VARIANTS[seed % len(VARIANTS)] if seed % 2 else dict()
+    out = orc.compress_paged(case.K_pages, case.V_pages, case.page_table, case.seq_len,
+                             case.budget, case.Q, case.free_list, case.window, case.lam, ps,
+                             shared_heads=True, **var)
+    check_page_return(case.page_table, case.free_list, out["page_table"], out["free_list"],
+                      case.seq_len, case.budget, ps, case.meta["pool"])
+    H = case.kv_heads
+    live = np.zeros(case.K_pages.shape[:1] + case.K_pages.shape[1:3], dtype=bool)
+    for s, n in enumerate(case.seq_len):
+        n, b = int(n), int(case.budget[s])
+        kept = [list(map(int, out["kept"][s][h])) for h in range(H)]
+        assert all(k == kept[0] for k in kept), f"seq {s}: heads keep different sets"
+        if n > b:
+            Kl = [orc.logical_rows(case.K_pages, case.page_table[s], n, h, ps).tolist() for h in range(H)]
+            Vl = [orc.logical_rows(case.V_pages, case.page_table[s], n, h, ps).tolist() for h in range(H)]
+            r = bf.compress_shared_bf(Kl, Vl, np.asarray(case.Q)[s].tolist(), b, case.window,
+                                      case.lam, **var)
+            assert kept[0] == r["kept"], (s, kept[0], r["kept"])
+        else:
+            assert kept[0] == list(range(n))
+        for h in range(H):
+            for r_, src in enumerate(kept[h]):
+                pg_src = case.page_table[s, src // ps]
+                pg_dst = case.page_table[s, r_ // ps]
+                assert np.array_equal(out["K_pages"][pg_dst, h, r_ % ps],
+                                      case.K_pages[pg_src, h, src % ps])
+                assert np.array_equal(out["V_pages"][pg_dst, h, r_ % ps],
+                                      case.V_pages[pg_src, h, src % ps])
+                live[pg_dst, h, r_ % ps] = True
+    assert np.array_equal(out["K_pages"][~live], case.K_pages[~live])
+    assert np.array_equal(out["V_pages"][~live], case.V_pages[~live])
+    # heads that are copies of head 0 (2 or 4 of them: the sums are exact)
+    for copies in (2, 4):
+        Kc = np.repeat(case.K_pages[:, :1], copies, axis=1)
+        Vc = np.repeat(case.V_pages[:, :1], copies, axis=1)
+        Qc = np.repeat(np.asarray(case.Q)[:, :1], copies, axis=1)
+        a = orc.compress_paged(Kc, Vc, case.page_table, case.seq_len, case.budget, Qc,
+                               case.free_list, case.window, case.lam, ps, shared_heads=True)
+        p = orc.compress_paged(Kc, Vc, case.page_table, case.seq_len, case.budget, Qc,
+                               case.free_list, case.window, case.lam, ps)
+        for s in range(len(lens)):
+            for h in range(copies):
+                assert list(a["kept"][s][h]) == list(p["kept"][s][h])
+        assert np.array_equal(a["K_pages"], p["K_pages"]) and np.array_equal(a["V_pages"], p["V_pages"])
+
+
 ALL_CHECKS = [check_bruteforce, check_select_ties, check_lambda_one, check_lambda_zero,
               check_duplicates, check_orthogonal, check_scale_invariance, check_zero_queries,
               check_softmax_rows, check_identical_heads, check_logit_scale, check_hand_example, check_structure,
               check_paged, check_bruteforce_variants, check_symmetric_closed_forms,
               check_unmasked_closed_forms, check_pooling_closed_forms, check_shared,
-              check_redundancy_rows]
+              check_redundancy_rows, check_paged_shared]

@@ -18,6 +18,31 @@ _orig_red = orc.redundancy
 _orig_imp = orc.importance
 _orig_select = orc.select
 _orig_rows = orc.redundancy_rows
+_orig_paged = orc.compress_paged
+
+
+def _paged_shared_variant(K_pages, V_pages, page_table, seq_len, budget, Q, free_list, window,
+                          lam, page_size, shared_heads=False, mode="ignored", **variant):
+    """Paged compression with one mistake in its head-shared mode."""
+    if not shared_heads:
+        return _orig_paged(K_pages, V_pages, page_table, seq_len, budget, Q, free_list, window,
+                           lam, page_size, **variant)
+    if mode == "ignored":                    # every head selects alone
+        return _orig_paged(K_pages, V_pages, page_table, seq_len, budget, Q, free_list, window,
+                           lam, page_size, **variant)
+    # the right selection, but every head's slots receive head 0's rows
+    out = _orig_paged(K_pages, V_pages, page_table, seq_len, budget, Q, free_list, window, lam,
+                      page_size, shared_heads=True, **variant)
+    for s, n in enumerate(seq_len):
+        n = int(n)
+        if n <= int(budget[s]):
+            continue
+        kept = out["kept"][s][0]
+        K0 = orc.logical_rows(K_pages, page_table[s], n, 0, page_size)
+        r = np.arange(len(kept))
+        for h in range(1, np.shape(K_pages)[1]):
+            out["K_pages"][page_table[s][r // page_size], h, r % page_size] = K0[kept]
+    return out
 
 
 def _pages_variant(page_table, seq_len, budget, free_list, page_size, mode):
@@ -172,6 +197,9 @@ MUTANTS = {
     "pages_page_major_order": ("return_pages", lambda *a: _pages_variant(*a, mode="page_major")),
     "pages_freed_per_head": ("return_pages", lambda *a: _pages_variant(*a, mode="freed_per_head")),
     "pages_entries_kept": ("return_pages", lambda *a: _pages_variant(*a, mode="entries_kept")),
+    # head-shared selection on pages
+    "paged_shared_ignored": ("compress_paged", lambda *a, **kw: _paged_shared_variant(*a, mode="ignored", **kw)),
+    "paged_shared_head0_rows": ("compress_paged", lambda *a, **kw: _paged_shared_variant(*a, mode="head0_rows", **kw)),
     # redundancy of listed rows
     "rows_include_self": ("redundancy_rows", lambda K, rows, symmetric=False:
                           _rows_variant(K, rows, symmetric, "self")),

@@ -71,6 +71,11 @@ def test_shared_selection(seed):
     pins.check_shared(seed)
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_paged_shared_selection(seed):
+    pins.check_paged_shared(seed)
+
+
 def test_budget_not_above_window_is_invalid():
     import numpy as np
     from oracle import rkv_oracle as orc
