@@ -133,6 +133,7 @@ KERNEL_SOURCES = {
     "rkv_k1_combine": ["k1_importance.hip"] + _HEADERS,
     "rkv_k4_select": ["k4_select.hip", "rkv_select.hpp"] + _HEADERS,
     "rkv_k4_group_select": ["k4_select.hip", "rkv_select.hpp"] + _HEADERS,
+    "rkv_k4_paged_shared": ["k4_shared.hip", "rkv_select.hpp"] + _HEADERS,
     "rkv_k5_gather": ["k5_compact.hip"] + _HEADERS,
     "rkv_k5_paged_compact": ["k5_compact.hip"] + _HEADERS,
     "rkv_free_pages": ["k5_compact.hip"] + _HEADERS,
@@ -410,24 +411,29 @@ def run_paged(args, wl, c, rkv, variant):
     cpu = None
     if not args.no_cpu_baseline:
         # (sequence, head) units of the shorter sequences, read through the
-        # page table: the oracle's N^2 loop makes a 32K-token unit minutes long
+        # page table: the oracle's N^2 loop makes a 32K-token unit minutes long;
+        # under head-shared selection, whole sequences (all heads)
+        shared = bool(variant.get("shared_heads"))
+        ovar = {k: v for k, v in variant.items() if k != "shared_heads"}
         rng = np.random.default_rng(0)
         short = [int(s_) for s_ in rng.permutation(case.num_seqs) if case.seq_len[s_] <= 4096]
         sample, budgets = [], []
-        for s_ in short[:64]:
+        for s_ in short[:(8 if shared else 64)]:
             n = int(case.seq_len[s_])
             t = torch.arange(n, device="cuda")
             pg = table0[s_][t // ps].long()
-            h = int(rng.integers(0, H))
-            sample.append((K0[pg, h, t % ps].float().cpu().numpy()[None],
-                           V0[pg, h, t % ps].float().cpu().numpy()[None],
-                           case.Q[s_, h].float().cpu().numpy()[None]))
+            hs = list(range(H)) if shared else [int(rng.integers(0, H))]
+            sample.append((np.stack([K0[pg, h, t % ps].float().cpu().numpy() for h in hs]),
+                           np.stack([V0[pg, h, t % ps].float().cpu().numpy() for h in hs]),
+                           np.stack([case.Q[s_, h].float().cpu().numpy() for h in hs])))
             budgets.append(int(case.budget[s_]))
         if sample:
-            rate, workers, done, m = run_oracle_pool(sample, budgets, w, case.lam, variant,
-                                                     args.cpu_seconds)
+            rate, workers, done, m = run_oracle_pool(sample, budgets, w, case.lam, ovar,
+                                                     args.cpu_seconds, shared=shared)
+            what = (f"{m} whole sequences ({H} heads each, head-shared selection)" if shared
+                    else f"{m} (sequence, head) units")
             cpu = {"value": rate, "unit": "KV-heads/s", "cores": workers, "kind": "oracle",
-                   "sample": f"{m} (sequence, head) units of the sequences with N_s <= 4096, "
+                   "sample": f"{what} of the sequences with N_s <= 4096, "
                              f"one process per core with one BLAS thread each, cycling for "
                              f"{args.cpu_seconds:.0f} s ({done} units done); the rate "
                              f"overstates the oracle on the whole workload, whose units reach "
@@ -546,8 +552,12 @@ def main():
         return
     if args.workload == "paged":
         if group > 1:
-            print("head-shared selection is dense only", file=sys.stderr)
-            sys.exit(2)
+            # on pages the group is a sequence's KV heads (they share its pages)
+            if group != c["kv_heads"]:
+                print(f"on pages, head-shared selection groups the {c['kv_heads']} KV heads of a "
+                      f"sequence (--select-group {c['kv_heads']})", file=sys.stderr)
+                sys.exit(2)
+            variant = dict(variant, shared_heads=True)
         run_paged(args, wl, c, rkv, variant)
         return
     lam = args.lam if args.lam is not None else c.get("lam", 0.1)

@@ -225,7 +225,7 @@ def _host_i32(x):
 def compress_paged(K_pages, V_pages, page_table, seq_len, budget, Q_win, free_list, free_count: int,
                    window_size: int = 8, mix_lambda: float = 0.1, *, kept_idx=None,
                    debug: bool = False, workspace=None, stream=None, symmetric: bool = False,
-                   causal: bool = True, pool: str = "max") -> PagedResult:
+                   causal: bool = True, pool: str = "max", shared_heads: bool = False) -> PagedResult:
     """Compress a paged cache in place and return freed pages to ``free_list``.
 
     K_pages, V_pages: [P, H, page_size, 128] device tensors (any page/head/slot
@@ -233,7 +233,9 @@ def compress_paged(K_pages, V_pages, page_table, seq_len, budget, Q_win, free_li
     device, updated in place; seq_len, budget: host sequences of S ints;
     Q_win: [S, H, G, w, 128]; free_list: int32 device tensor of capacity
     free_list.numel() holding ``free_count`` ids. Returns the ragged kept
-    indices and the new free count.
+    indices and the new free count. ``shared_heads``: the H heads of each
+    sequence keep one token set, chosen on the sum of their scores
+    (RKV_VARIANT_SHARED_HEADS).
     """
     import torch
     _require_cuda(K_pages, V_pages, page_table, Q_win, free_list, kept_idx)
@@ -257,7 +259,8 @@ def compress_paged(K_pages, V_pages, page_table, seq_len, budget, Q_win, free_li
         raise ValueError("seq_len and budget need one entry per sequence")
     d = paged_desc(S, H, g, window_size, ps, int(page_table.shape[1]), P, mix_lambda,
                    _dtype_code(K_pages), K_pages.stride(0), K_pages.stride(1), K_pages.stride(2),
-                   variant_bits(symmetric, causal, pool))
+                   variant_bits(symmetric, causal, pool)
+                   | (_lib.RKV_VARIANT_SHARED_HEADS if shared_heads else 0))
     lib = _lib.load()
     need = lib.rkv_paged_workspace_size(ctypes.byref(d), sl_p, bu_p)
     if need == 0:

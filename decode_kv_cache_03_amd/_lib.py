@@ -18,6 +18,7 @@ RKV_BF16 = 1
 RKV_VARIANT_SYMMETRIC = 1
 RKV_VARIANT_NO_CAUSAL = 2
 RKV_VARIANT_POOL_MEAN = 4
+RKV_VARIANT_SHARED_HEADS = 8
 
 STATUS_NAMES = {RKV_OK: "RKV_OK", RKV_EINVAL: "RKV_EINVAL", RKV_EWORKSPACE: "RKV_EWORKSPACE",
                 RKV_EFREELIST: "RKV_EFREELIST", RKV_EUNSUPPORTED: "RKV_EUNSUPPORTED",

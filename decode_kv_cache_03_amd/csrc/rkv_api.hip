@@ -172,6 +172,8 @@ int check_dense_desc(const rkv_dense_desc* d) {
     return fail(RKV_EINVAL, "num_heads * n_cand too large");
   if ((int64_t)(d->num_heads + 7) / 8 * 8 * ((d->n_cand + rkv::kK2Rows - 1) / rkv::kK2Rows) > INT32_MAX)
     return fail(RKV_EINVAL, "num_heads * ceil(n_cand / 128) must stay below 2^31");
+  if (d->variant & RKV_VARIANT_SHARED_HEADS)
+    return fail(RKV_EINVAL, "RKV_VARIANT_SHARED_HEADS is for paged calls; dense calls take select_group");
   if (d->variant & ~rkv::kVariantMask)
     return fail(RKV_EINVAL, "unknown variant bits 0x%x", (unsigned)(d->variant & ~rkv::kVariantMask));
   if (d->select_group < 0) return fail(RKV_EINVAL, "select_group must be >= 0 (got %d)", d->select_group);
@@ -416,6 +418,13 @@ extern "C" int rkv_compress_static(const rkv_dense_desc* desc, const void* K, co
 }
 
 // ---- paged --------------------------------------------------------------------
+namespace rkv {
+// head-shared selection on pages (k4_shared.hip)
+template <typename T>
+hipError_t run_k4_paged_shared(const PagedProblem<T>& p, int num_seqs, const float* Z, float* zsum,
+                               int32_t* kept, hipStream_t st);
+}  // namespace rkv
+
 namespace {
 
 struct PagedPlan {
@@ -428,6 +437,7 @@ struct PagedPlan {
   int64_t kc_elems = 0;   // contiguous key copy of the scored units (bf16, long-unit kernel)
   int32_t freed = 0;
   int nqb = 1;
+  bool shared = false;   // head-shared selection: a sequence's heads keep one set
 };
 
 int check_paged(const rkv_paged_desc* d, const int32_t* seq_len, const int32_t* budget) {
@@ -441,8 +451,9 @@ int check_paged(const rkv_paged_desc* d, const int32_t* seq_len, const int32_t* 
   if (d->max_pages_per_seq < 1) return fail(RKV_EINVAL, "max_pages_per_seq must be >= 1");
   if (d->num_pages < 1) return fail(RKV_EINVAL, "num_pages must be >= 1");
   if ((int64_t)d->num_seqs * d->num_kv_heads > (1 << 30)) return fail(RKV_EINVAL, "too many units");
-  if (d->variant & ~rkv::kVariantMask)
-    return fail(RKV_EINVAL, "unknown variant bits 0x%x", (unsigned)(d->variant & ~rkv::kVariantMask));
+  if (d->variant & ~(rkv::kVariantMask | RKV_VARIANT_SHARED_HEADS))
+    return fail(RKV_EINVAL, "unknown variant bits 0x%x",
+                (unsigned)(d->variant & ~(rkv::kVariantMask | RKV_VARIANT_SHARED_HEADS)));
   const int64_t slot = d->slot_stride ? d->slot_stride : 128;
   const int64_t head = d->head_stride ? d->head_stride : (int64_t)d->page_size * 128;
   const int64_t page = d->page_stride ? d->page_stride : (int64_t)d->num_kv_heads * d->page_size * 128;
@@ -464,6 +475,7 @@ int check_paged(const rkv_paged_desc* d, const int32_t* seq_len, const int32_t* 
 void paged_plan(const rkv_paged_desc* d, const int32_t* seq_len, const int32_t* budget, PagedPlan& P) {
   const int S = d->num_seqs, H = d->num_kv_heads, ps = d->page_size;
   P.nqb = nqb_of(d->gqa_group, d->window);
+  P.shared = (d->variant & RKV_VARIANT_SHARED_HEADS) != 0;
   P.seq_len.assign(seq_len, seq_len + S);
   P.bud.assign(budget, budget + S);
   P.free_off.resize(S);
@@ -556,6 +568,7 @@ struct PagedLayout {
   float* z;
   float* part;
   float* fin;
+  float* zsum;         // head-shared selection: per-sequence sums of Z (else null)
   size_t meta_bytes;   // the uploaded prefix
   size_t bytes;
 };
@@ -581,6 +594,7 @@ PagedLayout paged_layout(const rkv_paged_desc* d, const PagedPlan& P, char* base
   L.z = c.take<float>(P.total_scores);
   L.part = c.take<float>((size_t)P.total_chunks * P.nqb * 32 * 2);
   L.fin = c.take<float>(U * P.nqb * 32 * 2);
+  L.zsum = P.shared ? c.take<float>((size_t)(P.total_scores / std::max(1, d->num_kv_heads))) : nullptr;
   L.bytes = std::max<size_t>(c.used, kAlign);
   return L;
 }
@@ -634,7 +648,7 @@ int paged_run(const rkv_paged_desc* d, void* Kp, void* Vp, int32_t* page_table, 
   p.unit_list = L.unit_list;
   p.unit_count = (int)P.unit_list.size();
   p.all_units = d->num_seqs * d->num_kv_heads;
-  p.variant = d->variant;
+  p.variant = d->variant & rkv::kVariantMask;   // the scoring readings
   float* z = dbg_Z ? dbg_Z : L.z;
   hipError_t e;
   if (p.unit_count > 0) {
@@ -656,7 +670,10 @@ int paged_run(const rkv_paged_desc* d, void* Kp, void* Vp, int32_t* page_table, 
                          rpg_shift, nullptr, nullptr, nullptr, nullptr, 0, 0, st);
     if (e != hipSuccess) return hip_fail(e, "redundancy launch");
   }
-  e = rkv::run_k4(p, p.all_units, z, kept, 0, st);
+  if (P.shared)
+    e = rkv::run_k4_paged_shared<T>(p, d->num_seqs, z, L.zsum, kept, st);
+  else
+    e = rkv::run_k4(p, p.all_units, z, kept, 0, st);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   if (p.unit_count > 0) {
     e = rkv::run_k5_paged<T>(p, static_cast<T*>(Kp), static_cast<T*>(Vp), kept, st);

@@ -81,10 +81,21 @@ extern "C" {
  *   RKV_VARIANT_POOL_MEAN  I_j = mean over the G query heads instead of the
  *                          max (the pooling ablation of P3 "Measured effects
  *                          reported in the paper", last row).
+ *   RKV_VARIANT_SHARED_HEADS  paged calls only: head-shared selection [P1
+ *                          "What the redundancy scoring actually does at
+ *                          decode time": tensor-parallel ranks all-reduce
+ *                          their eviction scores so that all evict the same
+ *                          tokens]. The H heads of a sequence keep one token
+ *                          set: the window and the B_s - w best candidates
+ *                          by the sum of their Z. Each head's Z is its own;
+ *                          kept_idx holds the same list for every head. The
+ *                          dense call takes select_group instead and rejects
+ *                          this bit.
  * Other bits are RKV_EINVAL. */
 #define RKV_VARIANT_SYMMETRIC 1u
 #define RKV_VARIANT_NO_CAUSAL 2u
 #define RKV_VARIANT_POOL_MEAN 4u
+#define RKV_VARIANT_SHARED_HEADS 8u
 
 /* Dense layout: unit h has K[h], V[h] = N rows of 128 contiguous elements,
  * consecutive rows 128 elements apart, consecutive units kv_head_stride

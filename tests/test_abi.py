@@ -203,6 +203,24 @@ def test_paged_desc_errors(lib, field, value):
     assert rc in (_lib.RKV_EINVAL, _lib.RKV_EUNSUPPORTED)
 
 
+def test_paged_shared_heads_accepted(lib):
+    """RKV_VARIANT_SHARED_HEADS is a paged variant (alone or with the reading
+    variants); its workspace adds the per-sequence sums of Z (one float per
+    candidate of every sequence). The dense call refuses the bit and names
+    its own way of sharing."""
+    lens, buds = [100, 50, 70], [64, 32, 48]
+    _, lp = arr(lens)
+    _, bp = arr(buds)
+    plain = lib.rkv_paged_workspace_size(ctypes.byref(paged()), lp, bp)
+    for v in range(8):
+        d = paged(variant=v | _lib.RKV_VARIANT_SHARED_HEADS)
+        need = lib.rkv_paged_workspace_size(ctypes.byref(d), lp, bp)
+        assert need >= plain + 4 * sum(lens), (v, need, plain)
+    d = dense(variant=_lib.RKV_VARIANT_SHARED_HEADS)
+    assert lib.rkv_workspace_size(ctypes.byref(d)) == 0
+    assert b"select_group" in lib.rkv_last_error()
+
+
 def test_paged_workspace_too_small(lib):
     lens, buds = [100, 50, 70], [64, 32, 48]
     _, lp = arr(lens)

@@ -260,6 +260,138 @@ def test_paged_ragged_full_size(rkv):
     assert np.array_equal(kept, orc.select(z.astype(np.float64), n, b, case.window))
 
 
+def _device_sum(Zh, zoff_s, n, H):
+    """A sequence's Z summed over its heads as the device sums it: fp32, in
+    head order, -0 folded onto +0."""
+    acc = np.zeros(n, dtype=np.float32)
+    for h in range(H):
+        acc = acc + Zh[zoff_s + h * n: zoff_s + (h + 1) * n].astype(np.float32)
+    return (acc + np.float32(0.0)).astype(np.float64)
+
+
+@pytest.mark.parametrize("variant", ["default", "all"])
+def test_shared_heads_small(rkv, variant):
+    """Head-shared selection on pages: every head of a compressed sequence
+    keeps one set; page return as for per-head selection; per-head Z against
+    the oracle; the set tau-valid for the oracle's summed scores and exactly
+    the selection on the device's own sum; rows moved bit-exactly."""
+    import torch
+    var = {} if variant == "default" else dict(symmetric=True, causal=False, pool="mean")
+    case = paged_case_host(61, LENS, FRACS, kv_heads=4, gqa=2, window=8, lam=0.1)
+    H, ps = case.kv_heads, case.page_size
+    Kp = par.to_device(case.K_pages, case.dtype)
+    Vp = par.to_device(case.V_pages, case.dtype)
+    table = torch.from_numpy(case.page_table).cuda()
+    ref = orc.compress_paged(case.K_pages, case.V_pages, case.page_table, case.seq_len,
+                             case.budget, case.Q, case.free_list, case.window, case.lam, ps,
+                             shared_heads=True, **var)
+    cap = len(ref["free_list"])
+    fl = torch.full((cap,), -5, dtype=torch.int32, device="cuda")
+    fl[:len(case.free_list)] = torch.from_numpy(case.free_list.astype(np.int32)).cuda()
+    res = rkv.compress_paged(Kp, Vp, table, case.seq_len, case.budget,
+                             par.to_device(case.Q, case.dtype), fl, len(case.free_list),
+                             case.window, case.lam, debug=True, shared_heads=True, **var)
+    torch.cuda.synchronize()
+    assert np.array_equal(table.cpu().numpy(), ref["page_table"])
+    assert np.array_equal(fl.cpu().numpy(), ref["free_list"].astype(np.int32))
+    kept_all = res.kept_idx.cpu().numpy()
+    Zh = res.Z.cpu().numpy()
+    off, zoff = _kept_offsets(case.seq_len, case.budget, H)
+    Kn, Vn = par.to_host_f32(Kp), par.to_host_f32(Vp)
+    live = np.zeros(Kn.shape[:3], dtype=bool)
+    for s, (n, b) in enumerate(zip(case.seq_len, case.budget)):
+        n, b = int(n), int(b)
+        nk = min(n, b)
+        kept = kept_all[off[s]: off[s] + H * nk].reshape(H, nk).astype(np.int64)
+        what = f"{variant} seq {s} (N={n}, B={b})"
+        assert all(np.array_equal(kept[h], kept[0]) for h in range(H)), what + ": heads differ"
+        if n <= b:
+            assert np.array_equal(kept[0], np.arange(n)), what
+            continue
+        Kl = np.stack([orc.logical_rows(case.K_pages, case.page_table[s], n, h, ps) for h in range(H)])
+        Vl = np.stack([orc.logical_rows(case.V_pages, case.page_table[s], n, h, ps) for h in range(H)])
+        rr = orc.compress_shared(Kl, Vl, case.Q[s], b, case.window, case.lam, **var)
+        for h in range(H):
+            par.assert_close(Zh[zoff[s] + h * n: zoff[s] + (h + 1) * n], rr["Z"][h], par.TOL_RZ,
+                             f"{what} head {h} Z")
+        par.assert_tau_valid(kept[0], rr["Z_sum"], n, b, case.window, what)
+        assert np.array_equal(kept[0], orc.select(_device_sum(Zh, zoff[s], n, H), n, b,
+                                                  case.window)), what + ": not the device sum's set"
+        r = np.arange(nk)
+        for h in range(H):
+            dst = (case.page_table[s][r // ps], h, r % ps)
+            assert np.array_equal(Kn[dst], Kl[h][kept[h]]), what + " K slots"
+            assert np.array_equal(Vn[dst], Vl[h][kept[h]]), what + " V slots"
+            live[dst] = True
+    assert np.array_equal(Kn[~live], case.K_pages[~live])
+    assert np.array_equal(Vn[~live], case.V_pages[~live])
+
+
+def test_shared_heads_full_size(rkv):
+    """The paged ragged workload (128 sequences of 2K..32K tokens, 8 KV heads)
+    with head-shared selection: the page return; for every sequence one kept
+    set, exactly the selection on the device's summed scores; every live slot
+    a bit-exact copy; the oracle's scores and set on the two shortest
+    sequences."""
+    import torch
+    c = CONFIGS[4]
+    case = paged_case_device(4, c["seqs"], c["kv_heads"], c["gqa"], c["n_min"], c["n_max"],
+                             c["frac_min"], c["frac_max"], c["window"], c["lam"], c["dtype"],
+                             c["coverage"], c["sigma"], c["page_size"], c["spare_pages"])
+    H, ps = case.kv_heads, case.page_size
+    K0, V0 = case.K_pages.clone(), case.V_pages.clone()
+    table = torch.from_numpy(case.page_table).cuda()
+    t_ref, f_ref = orc.return_pages(case.page_table, case.seq_len, case.budget, case.free_list, ps)
+    fl = torch.full((len(f_ref),), -5, dtype=torch.int32, device="cuda")
+    fl[:len(case.free_list)] = torch.from_numpy(case.free_list).cuda()
+    res = rkv.compress_paged(case.K_pages, case.V_pages, table, case.seq_len, case.budget, case.Q,
+                             fl, len(case.free_list), case.window, case.lam, debug=True,
+                             shared_heads=True)
+    torch.cuda.synchronize()
+    assert res.free_count == len(f_ref)
+    assert np.array_equal(table.cpu().numpy(), t_ref)
+    assert np.array_equal(fl.cpu().numpy(), f_ref.astype(np.int32))
+    off, zoff = _kept_offsets(case.seq_len, case.budget, H)
+    kh, Zh = res.kept_idx.cpu().numpy(), res.Z.cpu().numpy()
+    bad = []
+    for s, (n, b) in enumerate(zip(case.seq_len, case.budget)):
+        n, b = int(n), int(b)
+        if n <= b:
+            continue
+        k = kh[off[s]: off[s] + H * b].reshape(H, b)
+        if not all(np.array_equal(k[h], k[0]) for h in range(H)) or \
+                not np.array_equal(k[0], orc.select(_device_sum(Zh, zoff[s], n, H), n, b, case.window)):
+            bad.append(s)
+    assert not bad, f"{len(bad)} sequences: heads differ or not the device sum's set: {bad[:5]}"
+    ptab = torch.from_numpy(case.page_table.astype(np.int64)).cuda()
+    live = torch.zeros(case.K_pages.shape[:3], dtype=torch.bool, device="cuda")
+    kept_all = res.kept_idx
+    for s, (n, b) in enumerate(zip(case.seq_len, case.budget)):
+        n, b = int(n), int(b)
+        nk = min(n, b)
+        kept = kept_all[off[s]: off[s] + H * nk].view(H, nk).long()
+        hh = torch.arange(H, device="cuda")[:, None].expand(H, nk)
+        r = torch.arange(nk, device="cuda")[None, :].expand(H, nk)
+        src = (ptab[s][kept // ps], hh, kept % ps)
+        dst = (ptab[s][r // ps], hh, r % ps)
+        assert par.bits_equal(case.K_pages[dst], K0[src]), f"seq {s} K"
+        assert par.bits_equal(case.V_pages[dst], V0[src]), f"seq {s} V"
+        live[dst] = True
+    assert par.bits_equal(case.K_pages[~live], K0[~live])
+    assert par.bits_equal(case.V_pages[~live], V0[~live])
+    order = np.argsort(case.seq_len)
+    for s in [int(order[0]), int(order[1])]:
+        n, b = int(case.seq_len[s]), int(case.budget[s])
+        t = torch.arange(n, device="cuda")
+        Kl = np.stack([par.to_host_f32(K0[ptab[s][t // ps], h, t % ps]) for h in range(H)])
+        Vl = np.stack([par.to_host_f32(V0[ptab[s][t // ps], h, t % ps]) for h in range(H)])
+        rr = orc.compress_shared(Kl, Vl, par.to_host_f32(case.Q[s]), b, case.window, case.lam)
+        for h in range(H):
+            par.assert_close(Zh[zoff[s] + h * n: zoff[s] + (h + 1) * n], rr["Z"][h], par.TOL_RZ,
+                             f"seq {s} head {h} Z")
+        par.assert_tau_valid(kh[off[s]: off[s] + b], rr["Z_sum"], n, b, case.window, f"seq {s}")
+
+
 def test_two_runs_are_bit_identical(rkv):
     """Same inputs twice: kept indices, scores, pages, page table and free
     list (including its order) are bit-identical."""
