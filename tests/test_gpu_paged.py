@@ -269,15 +269,15 @@ def _device_sum(Zh, zoff_s, n, H):
     return (acc + np.float32(0.0)).astype(np.float64)
 
 
-@pytest.mark.parametrize("variant", ["default", "all"])
-def test_shared_heads_small(rkv, variant):
+@pytest.mark.parametrize("variant,dtype", [("default", "bf16"), ("all", "bf16"), ("default", "f32")])
+def test_shared_heads_small(rkv, variant, dtype):
     """Head-shared selection on pages: every head of a compressed sequence
     keeps one set; page return as for per-head selection; per-head Z against
     the oracle; the set tau-valid for the oracle's summed scores and exactly
     the selection on the device's own sum; rows moved bit-exactly."""
     import torch
     var = {} if variant == "default" else dict(symmetric=True, causal=False, pool="mean")
-    case = paged_case_host(61, LENS, FRACS, kv_heads=4, gqa=2, window=8, lam=0.1)
+    case = paged_case_host(61, LENS, FRACS, kv_heads=4, gqa=2, window=8, lam=0.1, dtype=dtype)
     H, ps = case.kv_heads, case.page_size
     Kp = par.to_device(case.K_pages, case.dtype)
     Vp = par.to_device(case.V_pages, case.dtype)
@@ -303,7 +303,7 @@ def test_shared_heads_small(rkv, variant):
         n, b = int(n), int(b)
         nk = min(n, b)
         kept = kept_all[off[s]: off[s] + H * nk].reshape(H, nk).astype(np.int64)
-        what = f"{variant} seq {s} (N={n}, B={b})"
+        what = f"{variant} {dtype} seq {s} (N={n}, B={b})"
         assert all(np.array_equal(kept[h], kept[0]) for h in range(H)), what + ": heads differ"
         if n <= b:
             assert np.array_equal(kept[0], np.arange(n)), what
