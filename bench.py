@@ -202,8 +202,8 @@ def cpu_model() -> str:
 
 
 def pool_workers() -> int:
-    """One worker per core this process may run on, at most 16 (a GPU machine's
-    CPU share per GPU)."""
+    """One worker per core this process may run on, at most 16 (the host cores
+    that one GPU of a shared node gets)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
