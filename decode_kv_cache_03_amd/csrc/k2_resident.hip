@@ -183,9 +183,9 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
       const float* pp = part + (tt & 1) * 1024 + tid_f;
       float m = pp[0];
 #pragma unroll
-      for (int w = 1; w < 8; ++w) m = fmaxf(m, pp[w * 128]);
+      for (int w = 1; w < 8; ++w) m = vmax(m, pp[w * 128]);
       if (with_diag)
-        for (int r = 0; r <= (tid_f >> 5); ++r) m = fmaxf(m, dpart[r * 128 + tid_f]);
+        for (int r = 0; r <= (tid_f >> 5); ++r) m = vmax(m, dpart[r * 128 + tid_f]);
       zs[j] = j == 0 ? 0.f : m * rn[j];
     }
   };
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
     ld_limit = u + 2 * gridDim.x;
     const int64_t so = p.score_off(u);
     const char* qlds = lds + L.q + par * L.qbytes;
-    float mrun[2] = {-INFINITY, -INFINITY}, srun[2] = {0.f, 0.f};
+    float mrun[2] = {kNoLogit, kNoLogit}, srun[2] = {0.f, 0.f};
     // the kept V rows of this workgroup's previous unit move during this
     // unit's tile steps, kps 16-byte chunks per thread per step
     const int pu = u - (int)gridDim.x;
@@ -387,7 +387,9 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
           if (em != -INFINITY) st += es * fast_exp2(em - mm);
         }
       }
-      const bool seen = mm != -INFINITY && st > 0.f;
+      // padding query rows (head g >= G or row r >= W) are unseen
+      const bool qok = (m >> rpg_shift) < G && (m & ((1 << rpg_shift) - 1)) < W;
+      const bool seen = qok && mm != -INFINITY && st > 0.f;
       stats[m] = u32x2_t{__float_as_uint(seen ? mm : 0.f), __float_as_uint(seen ? 1.0f / st : 0.f)};
     }
     lds_barrier();

@@ -168,10 +168,10 @@ __global__ __launch_bounds__(kThreads, 1) void k2r2_kernel(
       const float* pp = part + (tt & 1) * 1024 + tid_f;
       float m = pp[0];
 #pragma unroll
-      for (int w = 1; w < 8; ++w) m = fmaxf(m, pp[w * 128]);
+      for (int w = 1; w < 8; ++w) m = vmax(m, pp[w * 128]);
       if (with_diag)
-        for (int r = 0; r <= (tid_f >> 5); ++r) m = fmaxf(m, dpart[r * 128 + tid_f]);
-      if (mode == 2) m = fmaxf(m, zs[j]);
+        for (int r = 0; r <= (tid_f >> 5); ++r) m = vmax(m, dpart[r * 128 + tid_f]);
+      if (mode == 2) m = vmax(m, zs[j]);
       zs[j] = mode == 1 ? m : (j == 0 ? 0.f : m * rn[j]);
     }
   };
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r2_kernel(
     float mrun[NQG], srun[NQG];
 #pragma unroll
     for (int qs = 0; qs < NQG; ++qs) {
-      mrun[qs] = -INFINITY;
+      mrun[qs] = kNoLogit;
       srun[qs] = 0.f;
     }
     // the previous unit's kept V rows, then its kept K rows below row 1024,
@@ -374,7 +374,9 @@ __global__ __launch_bounds__(kThreads, 1) void k2r2_kernel(
               if (em != -INFINITY) sum += es * fast_exp2(em - mm);
             }
           }
-          const bool seen = mm != -INFINITY && sum > 0.f;
+          // padding query rows (head g >= G or row r >= W) are unseen
+          const bool qok = (m >> rpg_shift) < G && (m & ((1 << rpg_shift) - 1)) < W;
+          const bool seen = qok && mm != -INFINITY && sum > 0.f;
           stats[m] = u32x2_t{__float_as_uint(seen ? mm : 0.f), __float_as_uint(seen ? 1.0f / sum : 0.f)};
         }
         lds_barrier();

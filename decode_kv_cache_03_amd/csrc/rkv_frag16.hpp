@@ -43,17 +43,20 @@ __device__ __forceinline__ float sum_quarters(float x) {   // over lanes l, l^16
   const LanePair b = pair32(a.lo + a.hi);
   return b.lo + b.hi;
 }
-__device__ __forceinline__ float max_quarters(float x) {
-  const LanePair a = pair16(x);
-  const LanePair b = pair32(fmaxf(a.lo, a.hi));
-  return fmaxf(b.lo, b.hi);
-}
 
 // max(a, b) that propagates NaN (IEEE 754-2019 maximum; -0 < +0). Unlike
 // fmaxf it needs no quieting of its inputs, so a running max over products
-// compiles to one v_maximum3_f32 per one or two new values. The scores here
-// hold no NaN, where the two agree up to the sign of a zero.
+// compiles to one v_maximum3_f32 per one or two new values, and a max of
+// values that came through a lane swap or from LDS is one instruction, not
+// three. The scores here hold no NaN, where the two agree up to the sign of
+// a zero.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+__device__ __forceinline__ float max_quarters(float x) {
+  const LanePair a = pair16(x);
+  const LanePair b = pair32(vmax(a.lo, a.hi));
+  return vmax(b.lo, b.hi);
+}
 
 // Scheduling hint for one pipeline stage of 8 MFMA and 12 VALU instructions
 // (products of one row half-block, maxima of the previous one): two MFMA,
@@ -124,7 +127,7 @@ __device__ __forceinline__ float key_importance16(const u32x4_t (&kf)[4], const 
   // bit b of the query index m = 16 qs + 4 q + v: summed within a head
   // (b < rpg_shift) or under mean pooling, else max over heads
   auto comb = [&](float a, float b, int bit) {
-    return (mean || bit < rpg_shift) ? a + b : fmaxf(a, b);
+    return (mean || bit < rpg_shift) ? a + b : vmax(a, b);
   };
   // probabilities; keys before the window are seen by every window query
   // (a block-uniform test), so only later keys take the causal mask
@@ -156,9 +159,9 @@ __device__ __forceinline__ float key_importance16(const u32x4_t (&kf)[4], const 
       const LanePair a = pair16(x[qs]);
       x[qs] = a.lo + a.hi;
       const LanePair b = pair32(x[qs]);
-      x[qs] = fmaxf(b.lo, b.hi);
+      x[qs] = vmax(b.lo, b.hi);
     }
-    return fmaxf(x[0], x[1]) * inv_pool;
+    return vmax(x[0], x[1]) * inv_pool;
   }
   float x[2];
 #pragma unroll

@@ -70,6 +70,26 @@ __device__ __forceinline__ void row_norms(const u32x4_t (&f)[NK][4], int key0, i
 
 // Online softmax statistics of the window queries over 16*NK keys: lane l
 // owns query columns l % 16 and 16 + l % 16 (mrun/srun [qs]).
+// The running softmax statistics of one query column start at (kNoLogit, 0)
+// and take a block of logits lg[] (masked ones -inf) whose max is mt: the
+// max moves to max(m, mt), the sum is rescaled to it and the block's
+// exponentials added. kNoLogit is finite and below every logit, so the first
+// block rescales a zero sum by exp2 of a very negative number (0) and
+// masked logits add exp2(-inf) = 0: the same sum as starting from -inf with
+// that case branched around, without a test per update. Padding query
+// columns (g >= G or r >= W) accumulate zero logits here; the merge at the
+// end of the unit marks them unseen.
+constexpr float kNoLogit = -3.40282347e38f;   // -FLT_MAX
+template <int NV>
+__device__ __forceinline__ void stats_accumulate(const float (&lg)[NV], float mt, float& m, float& s) {
+  const float mn = vmax(m, mt);
+  float sum = s * fast_exp2(m - mn);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) sum += fast_exp2(lg[i] - mn);
+  s = sum;
+  m = mn;
+}
+
 template <int NK>
 __device__ __forceinline__ void stats_update(const u32x4_t (&kf)[NK][4], const u32x4_t (&qf)[2][4],
                                              int key0, int N, int W, int G, int rpg_shift,
@@ -88,13 +108,12 @@ __device__ __forceinline__ void stats_update(const u32x4_t (&kf)[NK][4], const u
     for (int ksb = 0; ksb < NK; ++ksb)
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) mma16(acc[ksb][qs], kf[ksb][ks], qf[qs][ks]);   // C[key][query]
-  // the block holds padding or keys that some window query cannot see
+  // the block holds padding or keys that some window query cannot see (a
+  // block-uniform test: every other block is seen whole by every query)
   const bool edge = key0 + 16 * NK > (causal ? N - W : N);
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
-    const int m = qs * 16 + (lane & 15);
-    const int g = m >> rpg_shift, r = m & rpg_mask;
-    const bool qok = g < G && r < W;
+    const int r = (qs * 16 + (lane & 15)) & rpg_mask;
     const int last = causal ? N - W + r : N - 1;   // last key visible to window query r
     float lg[4 * NK];
     float mt = -INFINITY;
@@ -104,18 +123,11 @@ __device__ __forceinline__ void stats_update(const u32x4_t (&kf)[NK][4], const u
       for (int v = 0; v < 4; ++v) {
         const int key = key0 + ksb * 16 + 4 * (lane >> 4) + v;
         float x = acc[ksb][qs][v] * kLogitScaleLog2;
-        if (edge || !qok) x = (qok && key <= last) ? x : -INFINITY;
+        if (edge) x = key <= last ? x : -INFINITY;
         lg[ksb * 4 + v] = x;
-        mt = fmaxf(mt, x);
+        mt = vmax(mt, x);
       }
-    const float mn = fmaxf(mrun[qs], mt);
-    if (mn != -INFINITY) {
-      float s = (mrun[qs] != -INFINITY) ? srun[qs] * fast_exp2(mrun[qs] - mn) : 0.f;
-#pragma unroll
-      for (int i = 0; i < 4 * NK; ++i) s += fast_exp2(lg[i] - mn);
-      srun[qs] = s;
-      mrun[qs] = mn;
-    }
+    stats_accumulate<4 * NK>(lg, mt, mrun[qs], srun[qs]);
   }
 }
 
@@ -158,7 +170,7 @@ __device__ __forceinline__ void pair_max(const u32x4_t (&af)[2][4], const float*
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const bool before = rs < cs || row0 + v < col;
-          if (before) cm[cs] = fmaxf(cm[cs], acc[rs][cs][v] * rr[rs][v]);
+          if (before) cm[cs] = vmax(cm[cs], acc[rs][cs][v] * rr[rs][v]);
         }
       }
   }
@@ -184,7 +196,7 @@ __device__ __forceinline__ void pair_max16(const u32x4_t (&af)[2][4], const floa
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const bool before = !diag || rs < cs || row0 + v < col;
-      if (before) cm = fmaxf(cm, acc[rs][v] * rr[v]);
+      if (before) cm = vmax(cm, acc[rs][v] * rr[v]);
     }
   }
 }
@@ -229,7 +241,7 @@ __device__ __forceinline__ void stats_update_groups(const u32x4_t (&kf)[NK][4], 
                                                     float (&srun)[NQG]) {
   asm volatile("" : "+v"(lane));   // per call: keeps lane-derived masks out of loop preheaders
   const int rpg_mask = (1 << rpg_shift) - 1;
-  const bool edge = key0 + 16 * NK > (causal ? N - W : N);
+  const bool edge = key0 + 16 * NK > (causal ? N - W : N);   // as in stats_update
 #pragma unroll
   for (int qs = 0; qs < NQG; ++qs) {
     u32x4_t qf[4];
@@ -241,9 +253,7 @@ __device__ __forceinline__ void stats_update_groups(const u32x4_t (&kf)[NK][4], 
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int a = 0; a < NK; ++a) mma16(acc[a], kf[a][ks], qf[ks]);   // C[key][query]
-    const int m = qs * 16 + (lane & 15);
-    const int g = m >> rpg_shift, r = m & rpg_mask;
-    const bool qok = g < G && r < W;
+    const int r = (qs * 16 + (lane & 15)) & rpg_mask;
     const int last = causal ? N - W + r : N - 1;   // last key visible to window query r
     float lg[4 * NK];
     float mt = -INFINITY;
@@ -253,18 +263,11 @@ __device__ __forceinline__ void stats_update_groups(const u32x4_t (&kf)[NK][4], 
       for (int v = 0; v < 4; ++v) {
         const int key = key0 + a * 16 + 4 * (lane >> 4) + v;
         float x = acc[a][v] * kLogitScaleLog2;
-        if (edge || !qok) x = (qok && key <= last) ? x : -INFINITY;
+        if (edge) x = key <= last ? x : -INFINITY;
         lg[a * 4 + v] = x;
-        mt = fmaxf(mt, x);
+        mt = vmax(mt, x);
       }
-    const float mn = fmaxf(mrun[qs], mt);
-    if (mn != -INFINITY) {
-      float sum = (mrun[qs] != -INFINITY) ? srun[qs] * fast_exp2(mrun[qs] - mn) : 0.f;
-#pragma unroll
-      for (int i = 0; i < 4 * NK; ++i) sum += fast_exp2(lg[i] - mn);
-      srun[qs] = sum;
-      mrun[qs] = mn;
-    }
+    stats_accumulate<4 * NK>(lg, mt, mrun[qs], srun[qs]);
   }
 }
 
@@ -284,7 +287,7 @@ __device__ __forceinline__ float key_importance16_groups(const u32x4_t (&kf)[4],
   const int rpg_mask = (1 << rpg_shift) - 1;
   const int key = key0 + (lane & 15);
   const int q = lane >> 4;
-  auto comb = [&](float a, float b, int bit) { return (mean || bit < rpg_shift) ? a + b : fmaxf(a, b); };
+  auto comb = [&](float a, float b, int bit) { return (mean || bit < rpg_shift) ? a + b : vmax(a, b); };
   const bool all_seen = !causal || key0 + 15 <= N - W;
   float res = 0.f;
 #pragma unroll
