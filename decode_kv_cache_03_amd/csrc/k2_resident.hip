@@ -252,6 +252,11 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
       // with the diagonal mask.
       const int nfull = min(kHeld, max(0, (4 * t - wave + 7) >> 3));
       const bool has_diag = t < nh && (wave >> 2) == (t & 1);
+      // per column block and half: the max over the lane's accumulator rows,
+      // reduced over the lane quarters and stored once after the loop
+      float cmx[4][2];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) cmx[cb][0] = cmx[cb][1] = -INFINITY;
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         // the next tile's loads, after one column block of matrix work (the
@@ -262,7 +267,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
         u32x4_t bf[2][4];
         load_frag(slot, cb * 32, lane_u, bf[0]);
         load_frag(slot, cb * 32 + 16, lane_u, bf[1]);
-        float cm[2] = {-INFINITY, -INFINITY};
+        float(&cm)[2] = cmx[cb];
         auto full = [&](auto sc) {
           constexpr int s = decltype(sc)::value;
           pair_max(A[s], rn + (8 * s + wave) * 32, bf, false, lane_u, cm);
@@ -283,8 +288,8 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
             pair_max(A[s], rn + (8 * s + wave) * 32, bf, (wave & 3) == cb, lane_u, cm);
           }
         }
-        publish_cols(cm, part + (t & 1) * 1024 + wave * 128 + cb * 32, lane_u);
       }
+      publish_step(cmx, part + (t & 1) * 1024 + wave * 128, lane_u);
       // statistics of the block this wave copied at step t-1
       if (t >= 1 && t - 1 < nh && (wave >> 2) == ((t - 1) & 1)) {
         const int key0 = (t - 1) * 128 + (wave & 3) * 32;

@@ -269,6 +269,11 @@ __global__ __launch_bounds__(kThreads, 1) void k2r2_kernel(
         // columns: the tile's keys against every held row before them, then
         // the wave's own block of the tile under the diagonal mask
         const int nfull = min(kHeld, max(0, (4 * min(tl, nhp) - wave + 7) >> 3));
+        // per column block and half: the max over the lane's accumulator
+        // rows, reduced over the lane quarters and stored once after the loop
+        float cmx[4][2];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) cmx[cb][0] = cmx[cb][1] = -INFINITY;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
           if (cb == 1) refill(c);
@@ -276,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r2_kernel(
           u32x4_t bf[2][4];
           load_frag(slot, cb * 32, lane_u, bf[0]);
           load_frag(slot, cb * 32 + 16, lane_u, bf[1]);
-          float cm[2] = {-INFINITY, -INFINITY};
+          float(&cm)[2] = cmx[cb];
           auto full = [&](auto sc) {
             constexpr int s = decltype(sc)::value;
             pair_max(A[s], rn + hb * 128 + (8 * s + wave) * 32, bf, false, lane_u, cm);
@@ -297,8 +302,8 @@ __global__ __launch_bounds__(kThreads, 1) void k2r2_kernel(
               pair_max(A[s], rn + hb * 128 + (8 * s + wave) * 32, bf, (wave & 3) == cb, lane_u, cm);
             }
           }
-          publish_cols(cm, part + (t & 1) * 1024 + wave * 128 + cb * 32, lane_u);
         }
+        publish_step(cmx, part + (t & 1) * 1024 + wave * 128, lane_u);
         if (pass == 0) {
           // statistics of the block this wave copied at the previous step
           if (tl >= 1 && tl - 1 < nhp && (wave >> 2) == ((tl - 1) & 1)) {

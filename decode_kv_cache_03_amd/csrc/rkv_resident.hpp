@@ -54,17 +54,24 @@ __device__ __forceinline__ void wait_vm(int n) {
 }
 
 // 1/||k|| of the 16*NK rows of NK fragments, written to rn[key0 + row]
-// (each row's four quarters add their partial sums; rows past N are padding).
+// (rows past N are padding). ||k||^2 of a fragment's 16 rows is the
+// diagonal of the fragment's product with itself (A and B fragments of the
+// same rows are the same registers), four MFMA instead of a sum of squares
+// per lane: lane l holds C[4q + v][l % 16] (q = l / 16), so the lanes with
+// (l % 16) / 4 == q hold diagonal element l % 16 in acc[l % 4].
 template <int NK>
 __device__ __forceinline__ void row_norms(const u32x4_t (&f)[NK][4], int key0, int lane, float* rn) {
+  asm volatile("" : "+v"(lane));   // per call: keeps lane-derived masks out of loop preheaders
+  const int c = lane & 15;
+  const bool on_diag = (c >> 2) == (lane >> 4);
 #pragma unroll
   for (int rs = 0; rs < NK; ++rs) {
-    float ss = 0.f;
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) ss += sumsq_chunk<bf16_bits>(f[rs][ks]);
-    ss = sum_quarters(ss);
-    const int key = key0 + rs * 16 + (lane & 15);
-    if (lane < 16) rn[key] = ss > 0.f ? __frsqrt_rn(ss) : 0.f;
+    for (int ks = 0; ks < 4; ++ks) mma16(acc, f[rs][ks], f[rs][ks]);
+    const float lo = (c & 1) ? acc[1] : acc[0], hi = (c & 1) ? acc[3] : acc[2];
+    const float ss = (c & 2) ? hi : lo;
+    if (on_diag) rn[key0 + rs * 16 + c] = ss > 0.f ? __frsqrt_rn(ss) : 0.f;
   }
 }
 
@@ -201,13 +208,33 @@ __device__ __forceinline__ void pair_max16(const u32x4_t (&af)[2][4], const floa
   }
 }
 
-// Max over the four lane quarters: lanes 0..15 end with the column maxima.
-__device__ __forceinline__ void publish_cols(float (&cm)[2], float* dst, int lane) {
+// The column maxima of a whole step stored at once: cm[cb][cs] holds, per
+// lane, the max over its four accumulator rows of column cb*32 + cs*16 +
+// l%16. A transposing butterfly reduces the eight values over the four lane
+// quarters with six lane swaps: a swap of two different registers leaves
+// the lower lane of each pair with both copies of the first value and the
+// upper lane with both copies of the second, so each swap and max finishes
+// two values and the results spread over the lanes. After the 16-lane stage
+// (values 2i, 2i+1) and the 32-lane stage, lane l of quarter q holds values
+// q and q + 4, the maxima of columns l and 64 + l, stored by every lane.
+__device__ __forceinline__ void publish_step(const float (&cm)[4][2], float* dst, int lane) {
+  float r[4];
 #pragma unroll
-  for (int cs = 0; cs < 2; ++cs) {
-    const float x = max_quarters(cm[cs]);
-    if (lane < 16) dst[cs * 16 + lane] = x;
+  for (int i = 0; i < 4; ++i) {
+    // values 2i and 2i + 1: the two column halves of column block i
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(cm[i][0]), __float_as_uint(cm[i][1]),
+                                                    false, false);
+    r[i] = vmax(__uint_as_float(s[0]), __uint_as_float(s[1]));
   }
+  float o[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(r[2 * i]), __float_as_uint(r[2 * i + 1]),
+                                                    false, false);
+    o[i] = vmax(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  }
+  dst[lane] = o[0];
+  dst[64 + lane] = o[1];
 }
 
 // ---- query groups one at a time (windows of up to 48 query rows) ----------
