@@ -207,6 +207,9 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
     // unit's tile steps, kps 16-byte chunks per thread per step
     const int pu = u - (int)gridDim.x;
     const bool vg = !score_only && pu >= (int)blockIdx.x;
+    // the previous unit's N value rows as a buffer (bounded reads)
+    const __amdgpu_buffer_rsrc_t v_prev = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_bits*>(p.vrow(vg ? pu : 0, 0)), 0, N * kRowBytes, kBufferWord3);
     // (declared per unit: nothing held lives on into the next unit)
     u32x4_t A[kHeld][2][4];   // held row blocks: slot s = row block 8s + wave
 
@@ -224,8 +227,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
       auto v_chunk = [&](int j) {
         const int q = (t * kps + j) * kThreads + tid_u;
         const int r = min(q >> 4, B - 1);   // chunks past the end re-read a kept row
-        load16_to_lds(reinterpret_cast<const char*>(p.vrow(pu, clamp_row(ks[r], N))) + (q & 15) * 16,
-                      vstage + (wave * 4 + j) * 1024);
+        load16_to_lds(v_prev, clamp_row(ks[r], N) * kRowBytes + (q & 15) * 16, vstage + (wave * 4 + j) * 1024);
       };
       vm += nv;
       if (t > 0 && tid_u < 128) finalize(t - 1, false, tid_u);
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
         for (int s = 0; s < kHeld; ++s) {
           if (s != ((t - 1) >> 1)) continue;
           u32x4_t qf[2][4];
-          load_queries(qlds, lane_u, W, G, rpg_shift, qf);
+          load_queries<false>(qlds, lane_u, W, G, rpg_shift, qf);
           stats_update(A[s], qf, key0, N, W, G, rpg_shift, causal, lane_u, mrun, srun);
         }
       }
@@ -333,7 +335,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
       load_frag(lslot, wave * 16, lane_p, kf[0]);
       row_norms(kf, tl * 128 + wave * 16, lane_p, rn);
       u32x4_t qf[2][4];
-      load_queries(qlds, lane_p, W, G, rpg_shift, qf);
+      load_queries<false>(qlds, lane_p, W, G, rpg_shift, qf);
       stats_update(kf, qf, tl * 128 + wave * 16, N, W, G, rpg_shift, causal, lane_p, mrun, srun);
     }
     lds_barrier();

@@ -203,6 +203,11 @@ __global__ __launch_bounds__(kThreads, 1) void k2r2_kernel(
         V_out + (int64_t)(vg ? pu : 0) * out_stride, 0, B * kRowBytes, kBufferWord3);
     const __amdgpu_buffer_rsrc_t ko_prev = __builtin_amdgcn_make_buffer_rsrc(
         K_out + (int64_t)(vg ? pu : 0) * out_stride, 0, nlow_prev * kRowBytes, kBufferWord3);
+    // the previous unit's N value and key rows as buffers (bounded reads)
+    const __amdgpu_buffer_rsrc_t v_prev = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_bits*>(p.vrow(vg ? pu : 0, 0)), 0, N * kRowBytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t k_prev = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_bits*>(p.krow(vg ? pu : 0, 0)), 0, N * kRowBytes, kBufferWord3);
     u32x4_t A[kHeld][2][4];   // held row blocks: slot s = local row block 8s + wave
     int st = 0;               // tile step of the unit
 
@@ -225,13 +230,10 @@ __global__ __launch_bounds__(kThreads, 1) void k2r2_kernel(
         auto v_chunk = [&](int j) {
           const int q = (st * kps + j) * kThreads + tid_u;
           const int r = q >> 4;
-          const char* src;
-          if ((st * kps + j) * kThreads < 16 * B)
-            src = reinterpret_cast<const char*>(p.vrow(pu, clamp_row(ks[r], N)));
-          else
-            src = reinterpret_cast<const char*>(
-                p.krow(pu, clamp_row(ks[min(r - B, max(nlow_prev - 1, 0))], N)));
-          load16_to_lds(src + (q & 15) * 16, vstage + (wave * 4 + j) * 1024);
+          const bool is_v = (st * kps + j) * kThreads < 16 * B;   // uniform
+          const int row = is_v ? ks[r] : ks[min(r - B, max(nlow_prev - 1, 0))];
+          load16_to_lds(is_v ? v_prev : k_prev, clamp_row(row, N) * kRowBytes + (q & 15) * 16,
+                        vstage + (wave * 4 + j) * 1024);
         };
         vm += nv;
         if (t > hb && tid_u < 128) finalize(t - 1, pass == 1 ? 2 : (t - 1 < kPT ? 0 : 1), false, tid_u);

@@ -88,7 +88,10 @@ __device__ __forceinline__ void load_frag(const char* base, int r0, int lane, u3
 }
 
 // Query fragments of the window: MFMA row m = 16*qs + l%16 is query row r of
-// head g with m = g * 2^rpg_shift + r; padding rows are zero.
+// head g with m = g * 2^rpg_shift + r; padding rows are zero (kZeroPad), or
+// a copy of row 0 where the caller discards them anyway (the softmax
+// statistics: padding columns are marked unseen when they are merged).
+template <bool kZeroPad = true>
 __device__ __forceinline__ void load_queries(const char* qlds, int lane, int W, int G, int rpg_shift,
                                              u32x4_t (&qf)[2][4]) {
   const int rpg_mask = (1 << rpg_shift) - 1;
@@ -100,8 +103,10 @@ __device__ __forceinline__ void load_queries(const char* qlds, int lane, int W, 
     const bool ok = g < G && r < W;
     const int n = ok ? g * W + r : 0;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qf[qs][ks] = ok ? ld16(qlds + frag_offset<bf16_bits>(n, q + 4 * ks)) : zero16();
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4_t x = ld16(qlds + frag_offset<bf16_bits>(n, q + 4 * ks));
+      qf[qs][ks] = (!kZeroPad || ok) ? x : zero16();
+    }
   }
 }
 
