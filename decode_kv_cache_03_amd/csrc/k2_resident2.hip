@@ -121,17 +121,20 @@ __global__ __launch_bounds__(kThreads, 1) void k2r2_kernel(
     const int t = ld_k < nb ? ld_k : ld_k - nb + kPT;
     char* slot = lds + issue_slot * kTileBytes;
     const int row0 = t * 128 + wave * 16;   // first tile row this wave loads
+    // the unit's N key rows as a buffer: the tile's row base is a scalar
+    // offset, the lane's part a fixed vector offset
+    const __amdgpu_buffer_rsrc_t ksrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_bits*>(p.krow(ld_u, 0)), 0, N * kRowBytes, kBufferWord3);
     if ((t + 1) * 128 <= N) {
-      const char* src = reinterpret_cast<const char*>(p.krow(ld_u, row0));
 #pragma unroll
-      for (int q = 0; q < 4; ++q) load16_to_lds(src + q * 1024 + lofs[q], slot + wave * 4096 + q * 1024);
+      for (int q = 0; q < 4; ++q)
+        load16_to_lds(ksrc, lofs[q], slot + wave * 4096 + q * 1024, row0 * kRowBytes + q * 1024);
     } else {   // last tile of the unit: rows past N repeat row N-1
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = min(row0 + 4 * q + lane_v / 16, N - 1);
         const int chunk_ofs = lofs[q] - (lane_v / 16) * kRowBytes;
-        load16_to_lds(reinterpret_cast<const char*>(p.krow(ld_u, r)) + chunk_ofs,
-                      slot + wave * 4096 + q * 1024);
+        load16_to_lds(ksrc, r * kRowBytes + chunk_ofs, slot + wave * 4096 + q * 1024);
       }
     }
     vm += 4;

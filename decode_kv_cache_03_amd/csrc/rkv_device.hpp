@@ -80,12 +80,14 @@ __device__ __forceinline__ void load16_to_lds(const void* src, char* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_dst), 16, 0, 0);
 }
 
-// The same from a raw buffer resource at a per-lane byte offset: the base
-// stays in scalar registers (no 64-bit address arithmetic per lane), and an
-// offset past the resource's size reads zeros instead of touching memory.
-__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t rsrc, int voffset, char* lds_dst) {
+// The same from a raw buffer resource at byte offset voffset (per lane) +
+// soffset (uniform): the base stays in scalar registers (no 64-bit address
+// arithmetic per lane), and an offset past the resource's size reads zeros
+// instead of touching memory.
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t rsrc, int voffset, char* lds_dst,
+                                              int soffset = 0) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(lds_dst), 16,
-                                           voffset, 0, 0, 0);
+                                           voffset, soffset, 0, 0);
 }
 
 // acc += A_chunk * B_chunk over the k-values of one 16-byte chunk per lane.
