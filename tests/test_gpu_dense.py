@@ -236,7 +236,8 @@ def test_llama_decode_event_full_size(rkv):
                              c["budget"], c["window"], c["lam"], c["dtype"], c["coverage"],
                              c["sigma"])
     rng = np.random.default_rng(2)
-    sample = [0, 255, 16383] + rng.choice(case.num_heads, 3, replace=False).tolist()
+    # the oracle on 48 units (first, last, a layer boundary and 45 drawn)
+    sample = [0, 255, 16383] + rng.choice(np.arange(1, 16383), 45, replace=False).tolist()
     _device_case_checks(rkv, case, sample, "llama-event")
 
 
@@ -248,7 +249,7 @@ def test_qwen_full_size_lambda_sweep(rkv):
     rng = np.random.default_rng(3)
     for lam in c["lams"]:
         case.lam = lam
-        sample = [int(x) for x in rng.choice(case.num_heads, 2, replace=False)]
+        sample = [int(x) for x in rng.choice(case.num_heads, 12, replace=False)]   # the oracle on 12 units per lambda
         _device_case_checks(rkv, case, sample, f"qwen lam={lam}")
 
 
