@@ -260,15 +260,12 @@ __global__ __launch_bounds__(kThreads, 1) void k2r2_kernel(
         // Waves w and w + 4 share a SIMD and the older wave w wins its matrix
         // pipe, so waves 4..7 finish their pair loops last: they start them
         // at once, alone on the pipe while waves 0..3 take the exponentials.
-        auto slot_stats = [&](int r0) {
-          u32x4_t kf[1][4];
-          load_frag(slot, r0, lane_u, kf[0]);
-          stats_update_groups<1, NQG>(kf, qlds, t * 128 + r0, N, W, G, rpg_shift, causal,
-                                      lane_u, mrun, srun);
-        };
         if (pass == 0 && tl >= nhp && wave < 4) {
-          slot_stats(wave * 32);
-          slot_stats(wave * 32 + 16);
+          u32x4_t kf[2][4];
+          load_frag(slot, wave * 32, lane_u, kf[0]);
+          load_frag(slot, wave * 32 + 16, lane_u, kf[1]);
+          stats_update_groups<2, NQG>(kf, qlds, t * 128 + wave * 32, N, W, G, rpg_shift, causal,
+                                      lane_u, mrun, srun);
         }
 
         // columns: the tile's keys against every held row before them, then
