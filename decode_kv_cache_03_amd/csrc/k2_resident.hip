@@ -479,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void k2r_kernel(
       __syncthreads();
       // the kept list and every candidate's output row (-1: dropped), in the
       // norms' place
-      select_block_lean<kThreads>(zs, N, B, W, ks, pos, ssh);
+      select_block_lean<kThreads, 3>(zs, N, B, W, ks, pos, ssh);   // N <= 1152
       __syncthreads();
       int32_t* kept = kept_all + p.kept_off(u);
       for (int r = tid_u; r < B; r += kThreads) kept[r] = ks[r];

@@ -119,24 +119,28 @@ struct SelectLeanScratch {
 
 // The selection of select_block (same keys, same threshold and tie rule,
 // same output) with one workgroup barrier per digit pass instead of six,
-// for units whose candidates fit 16-bit counts (N - W < 65536):
+// for units whose candidates fit 16-bit counts (N - W < 65536) and at most
+// KMAX per thread (N - W <= KMAX * NT):
+//  * each thread reads its strided candidates i = wave0 + lane + j*NT once
+//    and keeps their order keys in registers for the digit passes;
 //  * pass p adds its keys into histogram p % 3 (the lanes of a wave that
 //    share the first active lane's digit add with one atomic) and clears
 //    histogram (p + 1) % 3 for the next pass, which no wave has read since
 //    pass p - 2, before the barrier p; after it, EVERY wave reads the 256
 //    counts (lane l: digits 255-4l .. 252-4l), scans them over its lanes and
 //    finds the same digit and count above it, so nothing is broadcast;
-//  * the ordered pass gives thread t the candidates [t*per, t*per + per):
-//    one block scan of (keys above T) << 16 | (keys equal to T) yields both
-//    the thread's output position (above-T keys before it, plus the equal
-//    keys taken before it: the first take_eq in index order) and how many
-//    of its own equal keys it takes.
+//  * the ordered pass gives thread t the candidates [t*per, t*per + per),
+//    their keys read once for its two sweeps: one block scan of
+//    (keys above T) << 16 | (keys equal to T) yields both the thread's output
+//    position (above-T keys before it, plus the equal keys taken before it:
+//    the first take_eq in index order) and how many of its own equal keys it
+//    takes.
 // Writes ks[0..B) and pos[i] (output row of candidate i, or -1) for every
 // i < N, both in LDS; every index written is bounded ([0, B), [0, N)). The
 // caller's barrier after the call publishes them. All NT threads call it
 // with the same arguments; sh.hist[0] and [1] are cleared here (one barrier).
 // Requires N > B > W.
-template <int NT>
+template <int NT, int KMAX>
 __device__ __forceinline__ void select_block_lean(const float* __restrict__ z, int N, int B, int W,
                                                   int32_t* __restrict__ ks, int32_t* __restrict__ pos,
                                                   SelectLeanScratch& sh) {
@@ -147,6 +151,12 @@ __device__ __forceinline__ void select_block_lean(const float* __restrict__ z, i
   const int wave0 = tid - lane;
   const int cand = N - W;
   const int k = B - W;
+  uint32_t key[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int i = wave0 + j * NT + lane;
+    key[j] = i < cand ? order_key(z[i]) : 0u;
+  }
   if (tid < 256) {
     sh.hist[0][tid] = 0u;
     sh.hist[1][tid] = 0u;
@@ -157,11 +167,12 @@ __device__ __forceinline__ void select_block_lean(const float* __restrict__ z, i
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     uint32_t* const hc = sh.hist[pass % 3];
-    for (int i0 = wave0; i0 < cand; i0 += NT) {   // bounds uniform across the wave
-      const int i = i0 + lane;
-      const uint32_t key = i < cand ? order_key(z[i]) : 0u;
-      const bool in = i < cand && (key & mask) == prefix;
-      const uint32_t dig = (key >> shift) & 255u;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (wave0 + j * NT >= cand) continue;   // uniform across the wave
+      const int i = wave0 + j * NT + lane;
+      const bool in = i < cand && (key[j] & mask) == prefix;
+      const uint32_t dig = (key[j] >> shift) & 255u;
       const uint64_t act = __ballot(in);
       if (act != 0) {
         const int lead = __builtin_amdgcn_readfirstlane(__ffsll((long long)act) - 1);
@@ -200,20 +211,26 @@ __device__ __forceinline__ void select_block_lean(const float* __restrict__ z, i
   }
   const uint32_t T = prefix;
   const uint32_t take_eq = remaining;   // keys equal to T to keep, smallest indices first
-  const int per = (cand + NT - 1) / NT;
+  const int per = (cand + NT - 1) / NT;   // at most KMAX
   const int lo = min(cand, tid * per), hi = min(cand, lo + per);
+  uint32_t ckey[KMAX];
   uint32_t gt = 0, eq = 0;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t key = order_key(z[i]);
-    gt += key > T;
-    eq += key == T;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int i = lo + j;
+    ckey[j] = i < hi ? order_key(z[i]) : 0u;
+    gt += i < hi && ckey[j] > T;
+    eq += i < hi && ckey[j] == T;
   }
   const uint32_t packed = (gt << 16) | eq;
   const uint32_t incl = wave_inclusive_scan(packed);
   if (lane == 63) sh.wsum[wave] = incl;
   lds_barrier();
+  // the totals of the waves before this one (every wave's entry is read, the
+  // later ones masked, so the reads do not wait on each other)
   uint32_t before = 0;
-  for (int w = 0; w < wave; ++w) before += sh.wsum[w];
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) before += w < wave ? sh.wsum[w] : 0u;
   const uint32_t excl = before + incl - packed;
   // equal keys taken by the threads before this one (the first take_eq in
   // index order), then this thread's share; take_eq - taken_before cannot
@@ -224,10 +241,12 @@ __device__ __forceinline__ void select_block_lean(const float* __restrict__ z, i
   uint32_t p = (excl >> 16) + taken_before;
   const uint32_t take = min(eq, take_eq - taken_before);
   uint32_t taken = 0;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t key = order_key(z[i]);
-    bool keep = key > T;
-    if (key == T && taken < take) {
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int i = lo + j;
+    if (i >= hi) continue;
+    bool keep = ckey[j] > T;
+    if (ckey[j] == T && taken < take) {
       keep = true;
       ++taken;
     }

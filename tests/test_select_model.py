@@ -12,8 +12,9 @@ conflict fails the test, whatever order the waves would run in. The result
 (kept list and output row of every candidate) is compared with the oracle's
 selection step, and the waves run in a random order per epoch, so a result
 that depended on the order would show too. The index logic is modelled lane
-by lane: the histogram with the first-lane aggregation, each wave's own scan
-of the counts, the packed block scan of the ordered pass.
+by lane: the strided keys read once before the digit passes, the histogram
+with the first-lane aggregation, each wave's own scan of the counts, the
+packed block scan of the ordered pass.
 """
 import numpy as np
 import pytest
@@ -67,6 +68,16 @@ def wave_program(wave, N, B, W, lds, shared, clear_late=False):
     lane = np.arange(LANES)
     tid = wave * LANES + lane
     cand, k = N - W, B - W
+    # each thread's strided candidates wave*64 + lane + j*NT, read once: their
+    # keys stay in registers for the digit passes
+    kmax = (cand + NT - 1) // NT
+    regkey = np.zeros((kmax, LANES), np.uint64)
+    for j in range(kmax):
+        for l in range(LANES):
+            i = wave * LANES + j * NT + l
+            if i < cand:
+                lds.read(wave, "z", i)
+                regkey[j, l] = shared["keys"][i]
     for t in tid[tid < 256]:
         lds.write(wave, "hist0", t, 0)
         lds.write(wave, "hist1", t, 0)
@@ -75,14 +86,10 @@ def wave_program(wave, N, B, W, lds, shared, clear_late=False):
     for pas in range(4):
         shift = 24 - 8 * pas
         hc = f"hist{pas % 3}"
-        for i0 in range(wave * LANES, cand, NT):
+        for j, i0 in enumerate(range(wave * LANES, cand, NT)):
             i = i0 + lane
             valid = i < cand
-            key = np.zeros(LANES, np.uint64)
-            for l in range(LANES):
-                if valid[l]:
-                    lds.read(wave, "z", i[l])
-                    key[l] = shared["keys"][i[l]]
+            key = np.where(valid, regkey[j], 0).astype(np.uint64)
             inn = valid & ((key & mask) == prefix)
             dig = (key >> shift) & 255
             if inn.any():
@@ -135,7 +142,7 @@ def wave_program(wave, N, B, W, lds, shared, clear_late=False):
     incl = np.cumsum(packed)
     lds.write(wave, "wsum", wave, int(incl[-1]))
     yield
-    before = sum(lds.read(wave, "wsum", w) for w in range(wave))
+    before = sum(v for w, v in ((w, lds.read(wave, "wsum", w)) for w in range(WAVES)) if w < wave)
     excl = before + incl - packed
     eq_before = excl & 0xFFFF
     for l in range(LANES):
