@@ -11,7 +11,8 @@ the even rows (lower half) of b, so a lane gets (lower lane's value, upper
 lane's value) when a and b are the same register. The test checks that the
 helpers' meaning holds in the model and that every stored column is the
 max over the four quarters, on random values with ties, infinities and
-signed zeros.
+signed zeros. A last test checks the lanes that hold a fragment's diagonal
+in the row-norm MFMA layout.
 """
 import numpy as np
 
@@ -86,3 +87,19 @@ def test_a_single_quarter_decides():
         dst = publish_step(cm)
         for c in range(128):
             assert dst[c] == vals[c % 16, c // 32, (c % 32) // 16]
+
+
+def test_row_norm_diagonal_lanes():
+    """Row norms from a fragment's product with itself (row_norms): lane l
+    holds C[4q + v][l % 16] (q = l / 16), so the lanes with (l % 16) / 4 == q
+    hold diagonal element l % 16 in accumulator v = l % 4. Each of the 16
+    rows is written by exactly one lane, from the right accumulator entry."""
+    writers = {}
+    for l in range(LANES):
+        c, q = l % 16, l // 16
+        if (c >> 2) == q:
+            v = c & 3
+            assert 4 * q + v == c            # the entry is C[c][c]
+            writers.setdefault(c, []).append(l)
+    assert sorted(writers) == list(range(16))
+    assert all(len(w) == 1 for w in writers.values())
